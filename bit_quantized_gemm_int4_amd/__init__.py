@@ -1,0 +1,223 @@
+"""Python binding of libwq (argument marshalling only).
+
+Every computation runs in the HIP kernels of ``libwq.so``; this module only
+turns tensors into device pointers and sizes, calls the C ABI declared in
+``include/wq.h`` through ctypes on torch's current stream, and raises
+:class:`WqError` on a non-zero status. PyTorch provides device memory and
+streams. Importing works without the library; the first call raises
+``ImportError`` if ``libwq.so`` has not been built, and nothing falls back
+to another implementation.
+
+The C names are exported unchanged (``wq_pack_int4``, ``wq_dynamic_quant``,
+``wq_matmul_add_rmsnorm``, ``mx_quant_matmul_inplace_add`` and the size
+queries); the lower-case helpers without the prefix allocate outputs with
+torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+# wq_status
+WQ_OK, WQ_ERR_NULLPTR, WQ_ERR_SHAPE, WQ_ERR_DTYPE, WQ_ERR_GROUP = 0, 1, 2, 3, 4
+WQ_ERR_WORKSPACE, WQ_ERR_UNSUPPORTED, WQ_ERR_LAUNCH, WQ_ERR_ALIAS = 5, 6, 7, 8
+# wq_dtype
+WQ_F16, WQ_BF16, WQ_F32, WQ_INT8, WQ_INT4 = 1, 2, 3, 4, 5
+WQ_INT32, WQ_FP8_E4M3, WQ_FP4_E2M1, WQ_E8M0 = 6, 7, 8, 9
+# wq_layout
+WQ_LAYOUT_ND, WQ_LAYOUT_GFX950_B = 0, 1
+
+MX_GROUP_SIZE = 32 | (1 << 16) | (1 << 32)
+
+EXPORTS = (
+    "wq_status_string", "wq_abi_version",
+    "wq_pack_int4_bytes", "wq_pack_int4",
+    "wq_dynamic_quant",
+    "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
+    "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
+)
+
+_lib = None
+
+
+class WqError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {lib().wq_status_string(status).decode()}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libwq (declares argument types on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                              "or python -m bit_quantized_gemm_int4_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, D, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+        sig = {
+            "wq_status_string": (ctypes.c_char_p, [I]),
+            "wq_abi_version": (I, []),
+            "wq_pack_int4_bytes": (S, [I64, I64, I]),
+            "wq_pack_int4": (I, [P, I64, I64, I, I, P, P]),
+            "wq_dynamic_quant": (I, [P, I, I64, I64, P, I, I64, I, P, P, P]),
+            "wq_matmul_add_rmsnorm_workspace_size": (S, [I64, I64, I64]),
+            "wq_matmul_add_rmsnorm": (I, [P, I64, I64, I, P, I64, I, I, I, P, I64, I64, P, I64,
+                                          P, P, P, D, P, P, P, S, P]),
+            "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
+            "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, fn: str, check: bool) -> int:
+    if check and status != WQ_OK:
+        raise WqError(status, fn)
+    return status
+
+
+def act_code(dtype: torch.dtype) -> int:
+    return {torch.float16: WQ_F16, torch.bfloat16: WQ_BF16}[dtype]
+
+
+# ---- the C entry points, one to one ------------------------------------------
+
+def wq_pack_int4_bytes(k: int, n: int, layout: int) -> int:
+    return lib().wq_pack_int4_bytes(k, n, layout)
+
+
+def wq_pack_int4(weight, k, n, transpose, layout, out, stream=None, check=True) -> int:
+    st = lib().wq_pack_int4(_ptr(weight), k, n, int(transpose), layout, _ptr(out), _stream(stream))
+    return _check(st, "wq_pack_int4", check)
+
+
+def wq_dynamic_quant(x, x_dtype, rows, cols, smooth, y_dtype, block_k, transpose_y, y, scale,
+                     stream=None, check=True) -> int:
+    st = lib().wq_dynamic_quant(_ptr(x), x_dtype, rows, cols, _ptr(smooth), y_dtype, block_k,
+                                int(transpose_y), _ptr(y), _ptr(scale), _stream(stream))
+    return _check(st, "wq_dynamic_quant", check)
+
+
+def wq_matmul_add_rmsnorm_workspace_size(m: int, k: int, n: int) -> int:
+    return lib().wq_matmul_add_rmsnorm_workspace_size(m, k, n)
+
+
+def wq_matmul_add_rmsnorm(x1, m, k, act_dtype, x2, n, w_dtype, x2_layout, transpose_x2,
+                          scale, scale_rows, scale_cols, offset, group_size, bias, residual,
+                          gamma, epsilon, y, norm_out, workspace, workspace_size,
+                          stream=None, check=True) -> int:
+    st = lib().wq_matmul_add_rmsnorm(
+        _ptr(x1), m, k, act_dtype, _ptr(x2), n, w_dtype, x2_layout, int(transpose_x2),
+        _ptr(scale), scale_rows, scale_cols, _ptr(offset), group_size, _ptr(bias),
+        _ptr(residual), _ptr(gamma), float(epsilon), _ptr(y), _ptr(norm_out),
+        _ptr(workspace), workspace_size, _stream(stream))
+    return _check(st, "wq_matmul_add_rmsnorm", check)
+
+
+def mx_quant_matmul_inplace_add_workspace_size(m: int, k: int, n: int) -> int:
+    return lib().mx_quant_matmul_inplace_add_workspace_size(m, k, n)
+
+
+def mx_quant_matmul_inplace_add(x1, x2, x2_layout, x1_scale, x2_scale, m, k, n, transpose_x1,
+                                transpose_x2, group_size, y, workspace=None, workspace_size=0,
+                                stream=None, check=True) -> int:
+    st = lib().mx_quant_matmul_inplace_add(
+        _ptr(x1), _ptr(x2), x2_layout, _ptr(x1_scale), _ptr(x2_scale), m, k, n,
+        int(transpose_x1), int(transpose_x2), group_size, _ptr(y), _ptr(workspace),
+        workspace_size, _stream(stream))
+    return _check(st, "mx_quant_matmul_inplace_add", check)
+
+
+# ---- allocating helpers (torch for memory only) -------------------------------
+
+def pack_int4(weight: torch.Tensor, layout: int = WQ_LAYOUT_GFX950_B, transpose: bool = False,
+              stream=None) -> torch.Tensor:
+    """Pack a device int32 weight (k, n) (or (n, k) with ``transpose``)."""
+    k, n = (weight.shape[1], weight.shape[0]) if transpose else tuple(weight.shape)
+    out = torch.empty(wq_pack_int4_bytes(k, n, layout), dtype=torch.uint8, device=weight.device)
+    wq_pack_int4(weight, k, n, transpose, layout, out, stream)
+    return out
+
+
+def dynamic_quant(x: torch.Tensor, smooth: Optional[torch.Tensor] = None, y_dtype: int = WQ_INT8,
+                  block_k: int = 0, transpose_y: bool = False, stream=None):
+    """Returns (y, scale) of the dynamic quantization of ``x`` (rows = all but
+    the last dimension)."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    dev = x.device
+    if block_k == 0:
+        shape = {WQ_INT8: (rows, cols), WQ_INT4: (rows, cols // 2), WQ_INT32: (rows, cols // 8)}[y_dtype]
+        dt = {WQ_INT8: torch.int8, WQ_INT4: torch.uint8, WQ_INT32: torch.int32}[y_dtype]
+        y = torch.empty(shape, dtype=dt, device=dev)
+        scale = torch.empty(rows, dtype=torch.float32, device=dev)
+    else:
+        if y_dtype == WQ_FP8_E4M3:
+            shape = (cols, rows) if transpose_y else (rows, cols)
+        else:
+            shape = (rows, cols // 2)
+        y = torch.empty(shape, dtype=torch.uint8, device=dev)
+        scale = torch.empty((rows, (cols + 31) // 32), dtype=torch.uint8, device=dev)
+    wq_dynamic_quant(x, act_code(x.dtype), rows, cols, smooth, y_dtype, block_k, transpose_y,
+                     y, scale, stream)
+    return y, scale
+
+
+def matmul_add_rmsnorm(x1: torch.Tensor, x2: torch.Tensor, k: int, n: int, w_dtype: int,
+                       scale: torch.Tensor, offset: Optional[torch.Tensor], group_size: int,
+                       bias: Optional[torch.Tensor], residual: torch.Tensor, gamma: torch.Tensor,
+                       eps: float, layout: int = WQ_LAYOUT_GFX950_B, transpose_x2: bool = False,
+                       inplace: bool = False, workspace: Optional[torch.Tensor] = None,
+                       norm_out: Optional[torch.Tensor] = None, stream=None):
+    """Returns (y, norm_out); ``inplace`` writes y into ``residual``."""
+    m = x1.numel() // k
+    if scale.dim() == 2:
+        s_rows, s_cols = scale.shape
+    else:
+        s_rows, s_cols = 1, scale.numel()
+    y = residual if inplace else torch.empty_like(residual)
+    if norm_out is None:
+        norm_out = torch.empty_like(residual)
+    ws = wq_matmul_add_rmsnorm_workspace_size(m, k, n)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=x1.device)
+    wq_matmul_add_rmsnorm(x1, m, k, act_code(x1.dtype), x2, n, w_dtype, layout, transpose_x2,
+                          scale, s_rows, s_cols, offset, group_size, bias, residual, gamma, eps,
+                          y, norm_out, workspace, workspace.numel(), stream)
+    return y, norm_out
+
+
+def mx_matmul_inplace_add(x1_t: torch.Tensor, x2_packed: torch.Tensor, x1_scale: torch.Tensor,
+                          x2_scale: torch.Tensor, y: torch.Tensor, m: int, k: int, n: int,
+                          group_size: int = MX_GROUP_SIZE, stream=None) -> torch.Tensor:
+    """y += the MX block-32 product; x1_t is (k, m) E4M3, x2 GFX950_B E2M1."""
+    mx_quant_matmul_inplace_add(x1_t, x2_packed, WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n,
+                                1, 0, group_size, y, None, 0, stream)
+    return y

@@ -1,0 +1,243 @@
+// C ABI of libwq: argument validation (host only, before any launch) and
+// dispatch to the kernel launchers. Every rule cited here comes from the
+// operator pages named in wq.h; the status codes are this library's own.
+#include <cmath>
+#include <cstdint>
+
+#include "wq_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int64_t kMaxKN = 65535;            // k, n range (AddRmsNorm page, Constraints)
+constexpr int64_t kMaxRows = 2147483647LL;   // b*s range (same)
+
+bool is_act(wq_dtype d) { return d == WQ_F16 || d == WQ_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (both non-empty).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+wq_status from_hip(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* wq_status_string(wq_status status) {
+  switch (status) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_ERR_NULLPTR: return "WQ_ERR_NULLPTR: a required pointer is null";
+    case WQ_ERR_SHAPE: return "WQ_ERR_SHAPE: size out of range, shapes disagree or pointer misaligned";
+    case WQ_ERR_DTYPE: return "WQ_ERR_DTYPE: unsupported dtype";
+    case WQ_ERR_GROUP: return "WQ_ERR_GROUP: group size / scale shape rule broken";
+    case WQ_ERR_WORKSPACE: return "WQ_ERR_WORKSPACE: workspace missing or too small";
+    case WQ_ERR_UNSUPPORTED: return "WQ_ERR_UNSUPPORTED: option not offered by this library";
+    case WQ_ERR_LAUNCH: return "WQ_ERR_LAUNCH: the HIP runtime refused a launch";
+    case WQ_ERR_ALIAS: return "WQ_ERR_ALIAS: an output overlaps an input it may not alias";
+  }
+  return "unknown wq_status";
+}
+
+int wq_abi_version(void) { return kAbiVersion; }
+
+// ---------------------------------------------------------------------------
+size_t wq_pack_int4_bytes(int64_t k, int64_t n, wq_layout layout) {
+  if (k < 0 || n < 0) return 0;
+  if (layout == WQ_LAYOUT_ND) return (n % 2) ? 0 : (size_t)(k * (n / 2));
+  if (layout == WQ_LAYOUT_GFX950_B) {
+    const int64_t kp = 128 * ((k + 127) / 128), np = 16 * ((n + 15) / 16);
+    return (size_t)(kp * np / 2);
+  }
+  return 0;
+}
+
+wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n, int transpose,
+                       wq_layout layout, void* out, hipStream_t stream) {
+  if (layout != WQ_LAYOUT_ND && layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
+  if (k < 0 || n < 0) return WQ_ERR_SHAPE;
+  if (layout == WQ_LAYOUT_ND && (n % 2)) return WQ_ERR_SHAPE;
+  if ((k + 127) / 128 > 65535 || (n + 63) / 64 > 2147483647LL) return WQ_ERR_SHAPE;
+  if (k == 0 || n == 0) return WQ_OK;
+  if (!weight || !out) return WQ_ERR_NULLPTR;
+  if (!aligned16(out)) return WQ_ERR_SHAPE;
+  if (overlap(weight, (size_t)(k * n) * 4, out, wq_pack_int4_bytes(k, n, layout))) return WQ_ERR_ALIAS;
+  return from_hip(wq::launch_pack_int4(weight, k, n, transpose != 0, layout,
+                                       static_cast<uint8_t*>(out), stream));
+}
+
+// ---------------------------------------------------------------------------
+wq_status wq_dynamic_quant(const void* x, wq_dtype x_dtype, int64_t rows, int64_t cols,
+                           const void* smooth, wq_dtype y_dtype, int64_t block_k,
+                           int transpose_y, void* y, void* scale, hipStream_t stream) {
+  if (!is_act(x_dtype)) return WQ_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || rows > kMaxRows) return WQ_ERR_SHAPE;
+  const bool bf16 = x_dtype == WQ_BF16;
+  if (block_k == 0) {
+    if (y_dtype != WQ_INT8 && y_dtype != WQ_INT4 && y_dtype != WQ_INT32) return WQ_ERR_DTYPE;
+    if (transpose_y) return WQ_ERR_UNSUPPORTED;
+    // Constraints: INT4 needs an even last dim, INT32 one divisible by 8.
+    if (y_dtype == WQ_INT4 && (cols % 2)) return WQ_ERR_SHAPE;
+    if (y_dtype == WQ_INT32 && (cols % 8)) return WQ_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return WQ_OK;
+    if (!x || !y || !scale) return WQ_ERR_NULLPTR;
+    if (!aligned16(x) || (smooth && !aligned16(smooth)) || !aligned16(y)) return WQ_ERR_SHAPE;
+    return from_hip(wq::launch_quant_per_token(x, bf16, rows, cols, smooth, y_dtype, y,
+                                               static_cast<float*>(scale), stream));
+  }
+  if (block_k != 32) return WQ_ERR_UNSUPPORTED;
+  if (y_dtype != WQ_FP8_E4M3 && y_dtype != WQ_FP4_E2M1) return WQ_ERR_DTYPE;
+  if (transpose_y && y_dtype != WQ_FP8_E4M3) return WQ_ERR_UNSUPPORTED;
+  if (y_dtype == WQ_FP4_E2M1 && (cols % 2)) return WQ_ERR_SHAPE;
+  if ((cols + 63) / 64 > 65535) return WQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return WQ_OK;
+  if (!x || !y || !scale) return WQ_ERR_NULLPTR;
+  if (!aligned16(x) || (smooth && !aligned16(smooth)) || !aligned16(y)) return WQ_ERR_SHAPE;
+  return from_hip(wq::launch_quant_mx(x, bf16, rows, cols, smooth, y_dtype, transpose_y != 0,
+                                      static_cast<uint8_t*>(y), static_cast<uint8_t*>(scale),
+                                      stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t wq_matmul_add_rmsnorm_workspace_size(int64_t m, int64_t k, int64_t n) {
+  if (m < 0 || k < 0 || n < 0) return 0;
+  return wq::wq_workspace_bytes(m, k, n);
+}
+
+wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
+                                const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
+                                int transpose_x2, const void* antiquant_scale, int64_t scale_rows,
+                                int64_t scale_cols, const void* antiquant_offset,
+                                int64_t antiquant_group_size, const void* bias,
+                                const void* residual, const void* gamma, double epsilon, void* y,
+                                void* norm_out, void* workspace, size_t workspace_size,
+                                hipStream_t stream) {
+  // dtypes: x2 int8 or int4; every other input shares one dtype (Constraints)
+  if (!is_act(act_dtype)) return WQ_ERR_DTYPE;
+  if (w_dtype != WQ_INT4 && w_dtype != WQ_INT8) return WQ_ERR_DTYPE;
+  if (x2_layout != WQ_LAYOUT_ND && x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
+  if (w_dtype == WQ_INT4 && transpose_x2) return WQ_ERR_UNSUPPORTED;   // pack the transpose
+  if (w_dtype == WQ_INT8 && x2_layout != WQ_LAYOUT_ND) return WQ_ERR_UNSUPPORTED;
+  // shapes: b*s in [0, 2^31-1] (0 = empty); k in [1, 65535]; n in [0, 65535]
+  if (m < 0 || m > kMaxRows) return WQ_ERR_SHAPE;
+  if (k < 1 || k > kMaxKN) return WQ_ERR_SHAPE;
+  if (n < 0 || n > kMaxKN) return WQ_ERR_SHAPE;
+  if (w_dtype == WQ_INT4 && x2_layout == WQ_LAYOUT_ND && (n % 2)) return WQ_ERR_SHAPE;
+  if (!std::isfinite(epsilon) || epsilon < 0) return WQ_ERR_SHAPE;
+  // quantization granularity (Constraints): per tensor (1), per channel
+  // (1, n) / (n), per group (ceil(k/G), n) with G in [32, k-1], G % 32 == 0.
+  const int64_t G = antiquant_group_size;
+  wq::WqProblem p{};
+  if (G != 0) {
+    if (G < 32 || G % 32 != 0 || G > k - 1) return WQ_ERR_GROUP;
+    if (scale_rows != (k + G - 1) / G || scale_cols != n) return WQ_ERR_GROUP;
+    p.group = G;
+    p.s_row = n;
+    p.s_col = 1;
+  } else if (scale_rows == 1 && scale_cols == 1) {
+    p.group = k;
+    p.s_row = 0;
+    p.s_col = 0;
+  } else if (scale_rows == 1 && scale_cols == n) {
+    p.group = k;
+    p.s_row = 0;
+    p.s_col = 1;
+  } else {
+    return WQ_ERR_GROUP;
+  }
+  if (m == 0 || n == 0) return WQ_OK;                  // empty tensors (Constraints)
+  if (!x1 || !x2 || !antiquant_scale || !residual || !gamma || !y || !norm_out)
+    return WQ_ERR_NULLPTR;
+  const size_t need = wq::wq_workspace_bytes(m, k, n);
+  if (!workspace || workspace_size < need) return WQ_ERR_WORKSPACE;
+  const void* ptrs[] = {x1, x2, antiquant_scale, antiquant_offset, bias, residual, gamma,
+                        y, norm_out, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return WQ_ERR_SHAPE;
+  // aliasing: y may be residual (inplace); norm_out may overlap nothing
+  const size_t mn2 = (size_t)(m * n) * 2;
+  const size_t wbytes = w_dtype == WQ_INT8 ? (size_t)(k * n)
+                                            : wq_pack_int4_bytes(k, n, x2_layout);
+  const size_t sbytes = (size_t)(scale_rows * scale_cols) * 2;
+  if (overlap(norm_out, mn2, x1, (size_t)(m * k) * 2) || overlap(norm_out, mn2, x2, wbytes) ||
+      overlap(norm_out, mn2, antiquant_scale, sbytes) ||
+      overlap(norm_out, mn2, antiquant_offset, sbytes) ||
+      overlap(norm_out, mn2, bias, (size_t)n * 2) || overlap(norm_out, mn2, residual, mn2) ||
+      overlap(norm_out, mn2, gamma, (size_t)n * 2) || overlap(norm_out, mn2, y, mn2) ||
+      overlap(norm_out, mn2, workspace, need))
+    return WQ_ERR_ALIAS;
+  if (y != residual && overlap(y, mn2, residual, mn2)) return WQ_ERR_ALIAS;
+  if (overlap(y, mn2, x1, (size_t)(m * k) * 2) || overlap(y, mn2, x2, wbytes) ||
+      overlap(y, mn2, workspace, need))
+    return WQ_ERR_ALIAS;
+
+  p.x1 = x1;
+  p.x2 = x2;
+  p.scale = antiquant_scale;
+  p.offset = antiquant_offset;
+  p.bias = bias;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.y = y;
+  p.norm_out = norm_out;
+  p.workspace = workspace;
+  p.workspace_size = workspace_size;
+  p.m = m;
+  p.k = k;
+  p.n = n;
+  p.bf16 = act_dtype == WQ_BF16;
+  p.w_bits = w_dtype == WQ_INT4 ? 4 : 8;
+  p.layout = x2_layout;
+  p.transpose_x2 = transpose_x2 != 0;
+  p.eps = (float)epsilon;
+  return from_hip(wq::launch_wq_matmul_add_rmsnorm(p, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t mx_quant_matmul_inplace_add_workspace_size(int64_t m, int64_t k, int64_t n) {
+  (void)m;
+  (void)k;
+  (void)n;
+  return 0;
+}
+
+wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout x2_layout,
+                                      const uint8_t* x1_scale, const uint8_t* x2_scale,
+                                      int64_t m, int64_t k, int64_t n, int transpose_x1,
+                                      int transpose_x2, int64_t group_size, float* y,
+                                      void* workspace, size_t workspace_size,
+                                      hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_size;
+  // Constraints: only transposeX1 = true, transposeX2 = false.
+  if (transpose_x1 != 1 || transpose_x2 != 0) return WQ_ERR_UNSUPPORTED;
+  if (x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
+  if (m < 0 || k < 0 || n < 0 || m > kMaxRows || k > kMaxRows || n > kMaxRows) return WQ_ERR_SHAPE;
+  if ((m + 63) / 64 > 65535) return WQ_ERR_SHAPE;
+  // groupSize = K | N << 16 | M << 32; zero fields inferred from the shapes:
+  // scale1 is (m, ceil(k/32)) and scale2 (ceil(k/32), n), so M and N infer to
+  // 1 by exact division and K to 32.
+  if (group_size < 0 || (group_size >> 48) != 0) return WQ_ERR_GROUP;
+  const int64_t gk = group_size & 0xFFFF, gn = (group_size >> 16) & 0xFFFF,
+                gm = (group_size >> 32) & 0xFFFF;
+  if ((gk != 0 && gk != 32) || (gn != 0 && gn != 1) || (gm != 0 && gm != 1)) return WQ_ERR_GROUP;
+  if (m == 0 || n == 0 || k == 0) return WQ_OK;
+  if (!x1 || !x2 || !x1_scale || !x2_scale || !y) return WQ_ERR_NULLPTR;
+  if (!aligned16(x2) || !aligned16(y)) return WQ_ERR_SHAPE;
+  const size_t ybytes = (size_t)(m * n) * 4;
+  const int64_t kb = (k + 31) / 32;
+  if (overlap(y, ybytes, x1, (size_t)(k * m)) ||
+      overlap(y, ybytes, x2, wq_pack_int4_bytes(k, n, WQ_LAYOUT_GFX950_B)) ||
+      overlap(y, ybytes, x1_scale, (size_t)(m * kb)) || overlap(y, ybytes, x2_scale, (size_t)(kb * n)))
+    return WQ_ERR_ALIAS;
+  wq::MxProblem p{static_cast<const uint8_t*>(x1), static_cast<const uint8_t*>(x2), x1_scale,
+                  x2_scale, y, m, k, n};
+  return from_hip(wq::launch_mx_matmul(p, stream));
+}
+
+}  // extern "C"

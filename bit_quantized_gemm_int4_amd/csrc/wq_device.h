@@ -1,0 +1,114 @@
+// Device helpers shared by the libwq kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef int i32x8 __attribute__((__vector_size__(32)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum Act { ACT_F16 = 0, ACT_BF16 = 1 };
+
+// ---- 16-bit float storage <-> float ------------------------------------
+template <int ACT>
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  if constexpr (ACT == ACT_BF16) {
+    return __uint_as_float((uint32_t)h << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+}
+
+// Round-to-nearest-even float -> 16-bit storage.
+template <int ACT>
+__device__ __forceinline__ uint16_t from_f32(float f) {
+  if constexpr (ACT == ACT_BF16) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+  } else {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)from_f32<ACT>(lo) | ((uint32_t)from_f32<ACT>(hi) << 16);
+}
+
+// Low / high 16-bit halves of a packed pair, as float.
+template <int ACT>
+__device__ __forceinline__ float lo_f32(uint32_t v) {
+  if constexpr (ACT == ACT_BF16) return __uint_as_float(v << 16);
+  else return to_f32<ACT>((uint16_t)(v & 0xFFFFu));
+}
+template <int ACT>
+__device__ __forceinline__ float hi_f32(uint32_t v) {
+  if constexpr (ACT == ACT_BF16) return __uint_as_float(v & 0xFFFF0000u);
+  else return to_f32<ACT>((uint16_t)(v >> 16));
+}
+
+// ---- DPP reductions over the 16 lanes of a row -------------------------
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
+// afterwards every lane of the row holds the row's result, combined in a
+// fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = quad_max(v);
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+
+// Whole-wavefront max (64 lanes) via cross-lane swizzles.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---- MFMA (16x16x32, 16-bit inputs, fp32 accumulate) --------------------
+// Operand layout for lane l: A row l%16, B column l%16, eight consecutive K
+// values starting at 8*(l/16); D column l%16, rows 4*(l/16)+i.
+template <int ACT>
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
+  if constexpr (ACT == ACT_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+}  // namespace wq

@@ -1,0 +1,293 @@
+// Weight-quantized matmul + residual add + RMSNorm
+// (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula):
+//   mm = x1 @ (x2 * antiquantScale + antiquantOffset) + bias
+//   y = mm + residual;  normOut = y / sqrt(mean(y^2) + eps) * gamma
+//
+// Two launches on the caller's stream:
+//   1. a GEMM kernel whose epilogue adds bias and residual, stores y and
+//      writes per-(32-column tile, row) partial sums of y^2 (float32 y) to
+//      the workspace;
+//   2. rmsnorm_finish: sums a row's partials in a fixed order, forms
+//      1/RMS and writes normOut = y * rstd * gamma.
+// GEMM kernels:
+//   - gemm_generic: any weight layout (INT4 ND / GFX950_B, INT8 ND /
+//     transposed), 64x64x32 tiles, both operands staged in LDS, the weight
+//     dequantized (q * s + o in float32, rounded to the activation dtype)
+//     while it is written to LDS.
+#include "wq_device.h"
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+enum WFmt { W_I4_ND = 0, W_I4_B = 1, W_I8_ND = 2, W_I8_T = 3 };
+
+struct GemmArgs {
+  const uint16_t* x1;
+  const uint8_t* x2;
+  const uint16_t* scale;
+  const uint16_t* offset;
+  const uint16_t* bias;
+  const uint16_t* residual;
+  uint16_t* y;
+  float* partial;        // [ceil(n/32)][m]
+  int64_t m, k, n, np;   // np: padded N of the GFX950_B layout
+  int64_t group, s_row, s_col;
+};
+
+// Dequantize one code q at (k, n) to float32: q * s + o.
+template <int ACT>
+__device__ __forceinline__ float dequant(const GemmArgs& a, int q, int64_t k, int64_t n) {
+  const int64_t si = (k / a.group) * a.s_row + n * a.s_col;
+  float w = (float)q * to_f32<ACT>(a.scale[si]);
+  if (a.offset) w += to_f32<ACT>(a.offset[si]);
+  return w;
+}
+
+// Epilogue for one 16x16 MFMA tile held by a wave: y = acc + bias + residual,
+// stored rounded; returns the float32 y values (0 outside the matrix).
+template <int ACT>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x4& acc, int64_t row0,
+                                              int64_t col, float yv[4]) {
+  const int lane = threadIdx.x & 63;
+  const bool cin = col < a.n;
+  const float b = (cin && a.bias) ? to_f32<ACT>(a.bias[col]) : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + 4 * (lane >> 4) + i;
+    float v = 0.f;
+    if (cin && row < a.m) {
+      const int64_t idx = row * a.n + col;
+      v = acc[i] + b + to_f32<ACT>(a.residual[idx]);
+      a.y[idx] = from_f32<ACT>(v);
+    }
+    yv[i] = v;
+  }
+}
+
+constexpr int GB_M = 64, GB_N = 64, GB_K = 32, G_LDS = GB_K + 8;
+
+template <int ACT, int WF>
+__global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[GB_M][G_LDS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[GB_N][G_LDS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * GB_M;
+  const int64_t n0 = (int64_t)blockIdx.y * GB_N;
+  const bool avec = (a.k & 7) == 0;
+  f32x4 acc[2][2] = {};
+
+  for (int64_t k0 = 0; k0 < a.k; k0 += GB_K) {
+    // ---- A tile: thread -> row t/4, 8 consecutive k ----
+    {
+      const int r = t >> 2, kc = (t & 3) * 8;
+      const int64_t row = m0 + r, kk = k0 + kc;
+      u32x4 v = {0, 0, 0, 0};
+      if (row < a.m) {
+        const uint16_t* src = a.x1 + row * a.k + kk;
+        if (avec && kk + 8 <= a.k) {
+          v = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          uint16_t e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = (kk + i < a.k) ? src[i] : (uint16_t)0;
+          v.x = e[0] | ((uint32_t)e[1] << 16);
+          v.y = e[2] | ((uint32_t)e[3] << 16);
+          v.z = e[4] | ((uint32_t)e[5] << 16);
+          v.w = e[6] | ((uint32_t)e[7] << 16);
+        }
+      }
+      *reinterpret_cast<u32x4*>(&As[r][kc]) = v;
+    }
+    // ---- B tile, dequantized, stored [n][k] ----
+    if constexpr (WF == W_I4_B || WF == W_I8_T) {
+      // thread -> column t/4, 8 consecutive k
+      const int c = t >> 2, kc = (t & 3) * 8;
+      const int64_t col = n0 + c, kk = k0 + kc;
+      int q[8];
+      if constexpr (WF == W_I4_B) {
+        uint32_t word = 0;
+        if (col < a.np)
+          word = *reinterpret_cast<const uint32_t*>(
+              a.x2 + ((kk / 128) * a.np + col) * 64 + ((kk / 32) % 4) * 16 + (kk % 32) / 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = ((int)(word << (28 - 4 * i))) >> 28;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          q[i] = (col < a.n && kk + i < a.k) ? (int)(int8_t)a.x2[col * a.k + kk + i] : 0;
+      }
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = (col < a.n && kk + i < a.k) ? dequant<ACT>(a, q[i], kk + i, col) : 0.f;
+      u32x4 v;
+      v.x = pack2<ACT>(w[0], w[1]);
+      v.y = pack2<ACT>(w[2], w[3]);
+      v.z = pack2<ACT>(w[4], w[5]);
+      v.w = pack2<ACT>(w[6], w[7]);
+      *reinterpret_cast<u32x4*>(&Bs[c][kc]) = v;
+    } else {
+      // row-major (k, n): thread -> k row t/8, 8 consecutive columns
+      const int r = t >> 3, nc = (t & 7) * 8;
+      const int64_t kk = k0 + r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t col = n0 + nc + i;
+        float w = 0.f;
+        if (kk < a.k && col < a.n) {
+          int q;
+          if constexpr (WF == W_I4_ND) {
+            const uint8_t b = a.x2[kk * (a.n / 2) + col / 2];
+            q = (col & 1) ? ((int)(int8_t)b >> 4) : (((int)(int8_t)(b << 4)) >> 4);
+          } else {
+            q = (int)(int8_t)a.x2[kk * a.n + col];
+          }
+          w = dequant<ACT>(a, q, kk, col);
+        }
+        Bs[nc + i][r] = from_f32<ACT>(w);
+      }
+    }
+    __syncthreads();
+    // ---- MFMA: each wave 32x32 = 2x2 tiles of 16x16 ----
+    const int kq = (lane >> 4) * 8;
+    u32x4 af[2], bf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      af[i] = *reinterpret_cast<const u32x4*>(&As[wr * 32 + i * 16 + (lane & 15)][kq]);
+      bf[i] = *reinterpret_cast<const u32x4*>(&Bs[wc * 32 + i * 16 + (lane & 15)][kq]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<ACT>(af[i], bf[j], acc[i][j]);
+    __syncthreads();
+  }
+
+  // ---- epilogue: y, and the wave's per-row sum of y^2 over its 32 columns ----
+  float ss[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float y0[4], y1[4];
+    const int64_t row0 = m0 + wr * 32 + i * 16;
+    epilogue_tile<ACT>(a, acc[i][0], row0, n0 + wc * 32 + (lane & 15), y0);
+    epilogue_tile<ACT>(a, acc[i][1], row0, n0 + wc * 32 + 16 + (lane & 15), y1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ss[i][r] = row16_sum(y0[r] * y0[r] + y1[r] * y1[r]);
+  }
+  const int64_t tile32 = (n0 + wc * 32) / 32;
+  if ((lane & 15) == 0 && n0 + wc * 32 < a.n) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wr * 32 + i * 16 + 4 * (lane >> 4) + r;
+        if (row < a.m) a.partial[tile32 * a.m + row] = ss[i][r];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm finish: grid (m rows, column chunks). Every workgroup of a row sums
+// the same partials in the same order, so all of them agree on rstd.
+// ---------------------------------------------------------------------------
+template <int ACT>
+__global__ __launch_bounds__(256) void rmsnorm_finish(const uint16_t* __restrict__ y,
+                                                      const float* __restrict__ partial,
+                                                      int64_t tiles, const uint16_t* __restrict__ gamma,
+                                                      uint16_t* __restrict__ out, int64_t m, int64_t n,
+                                                      float eps, int64_t chunk) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  float s = 0.f;
+  for (int64_t i = t; i < tiles; i += 256) s += partial[i * m + row];
+  s = wave_sum(s);
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  s = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rstd = 1.0f / sqrtf(s / (float)n + eps);
+  const int64_t c_begin = (int64_t)blockIdx.y * chunk;
+  const int64_t c_end = c_begin + chunk < n ? c_begin + chunk : n;
+  const uint16_t* yr = y + row * n;
+  uint16_t* orow = out + row * n;
+  if ((n & 7) == 0) {
+    for (int64_t c = c_begin + t * 8; c < c_end; c += 256 * 8) {
+      const u32x4 yv = *reinterpret_cast<const u32x4*>(yr + c);
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(gamma + c);
+      uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w}, ow[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ow[i] = pack2<ACT>(lo_f32<ACT>(yw[i]) * rstd * lo_f32<ACT>(gw[i]),
+                           hi_f32<ACT>(yw[i]) * rstd * hi_f32<ACT>(gw[i]));
+      u32x4 o;
+      o.x = ow[0];
+      o.y = ow[1];
+      o.z = ow[2];
+      o.w = ow[3];
+      *reinterpret_cast<u32x4*>(orow + c) = o;
+    }
+  } else {
+    for (int64_t c = c_begin + t; c < c_end; c += 256)
+      orow[c] = from_f32<ACT>(to_f32<ACT>(yr[c]) * rstd * to_f32<ACT>(gamma[c]));
+  }
+}
+
+template <int ACT>
+hipError_t launch_generic(const WqProblem& p, const GemmArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((p.m + GB_M - 1) / GB_M), (unsigned)((p.n + GB_N - 1) / GB_N));
+  if (p.w_bits == 4) {
+    if (p.layout == WQ_LAYOUT_GFX950_B) gemm_generic<ACT, W_I4_B><<<grid, 256, 0, s>>>(a);
+    else gemm_generic<ACT, W_I4_ND><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (p.transpose_x2) gemm_generic<ACT, W_I8_T><<<grid, 256, 0, s>>>(a);
+    else gemm_generic<ACT, W_I8_ND><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_finish(const WqProblem& p, const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = (p.n + 31) / 32;
+  int64_t chunk = 2048;
+  if (p.m < 256) chunk = 512;
+  if (chunk > p.n) chunk = p.n;
+  dim3 grid((unsigned)p.m, (unsigned)((p.n + chunk - 1) / chunk));
+  rmsnorm_finish<ACT><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(p.y), a.partial, tiles,
+                                           static_cast<const uint16_t*>(p.gamma),
+                                           static_cast<uint16_t*>(p.norm_out), p.m, p.n, p.eps, chunk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  (void)k;
+  const int64_t tiles = (n + 31) / 32;
+  return (size_t)(tiles * m * (int64_t)sizeof(float)) + 256;
+}
+
+hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
+  GemmArgs a;
+  a.x1 = static_cast<const uint16_t*>(p.x1);
+  a.x2 = static_cast<const uint8_t*>(p.x2);
+  a.scale = static_cast<const uint16_t*>(p.scale);
+  a.offset = static_cast<const uint16_t*>(p.offset);
+  a.bias = static_cast<const uint16_t*>(p.bias);
+  a.residual = static_cast<const uint16_t*>(p.residual);
+  a.y = static_cast<uint16_t*>(p.y);
+  a.partial = static_cast<float*>(p.workspace);
+  a.m = p.m;
+  a.k = p.k;
+  a.n = p.n;
+  a.np = 16 * ((p.n + 15) / 16);
+  a.group = p.group;
+  a.s_row = p.s_row;
+  a.s_col = p.s_col;
+  hipError_t e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
+  if (e != hipSuccess) return e;
+  return p.bf16 ? launch_finish<ACT_BF16>(p, a, s) : launch_finish<ACT_F16>(p, a, s);
+}
+
+}  // namespace wq

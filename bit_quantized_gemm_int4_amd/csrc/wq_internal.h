@@ -1,0 +1,63 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+// Arguments here are already validated; launchers only pick a kernel and a
+// grid and enqueue it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/wq.h"
+
+namespace wq {
+
+hipError_t launch_pack_int4(const int32_t* w, int64_t k, int64_t n, bool transpose,
+                            wq_layout layout, uint8_t* out, hipStream_t s);
+
+hipError_t launch_quant_per_token(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                  const void* smooth, wq_dtype y_dtype, void* y,
+                                  float* scale, hipStream_t s);
+
+hipError_t launch_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols,
+                           const void* smooth, wq_dtype y_dtype, bool transpose_y,
+                           uint8_t* y, uint8_t* scale, hipStream_t s);
+
+// Weight-quantized matmul + AddRmsNorm problem after validation.
+struct WqProblem {
+  const void* x1;
+  const void* x2;
+  const void* scale;
+  const void* offset;   // may be null
+  const void* bias;     // may be null
+  const void* residual;
+  const void* gamma;
+  void* y;
+  void* norm_out;
+  void* workspace;
+  size_t workspace_size;
+  int64_t m, k, n;
+  bool bf16;
+  int w_bits;           // 4 or 8
+  wq_layout layout;
+  bool transpose_x2;    // int8 only
+  // dequant indexing: scale index of (k, n) = (k / group) * s_row + n * s_col
+  int64_t group;        // k-group length (>= k for per-channel / per-tensor)
+  int64_t s_row;
+  int64_t s_col;
+  float eps;
+};
+
+size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n);
+hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s);
+
+struct MxProblem {
+  const uint8_t* x1;     // (k, m) e4m3
+  const uint8_t* x2;     // GFX950_B e2m1
+  const uint8_t* s1;     // (m, kb)
+  const uint8_t* s2;     // (kb, n)
+  float* y;
+  int64_t m, k, n;
+};
+
+hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s);
+
+}  // namespace wq

@@ -1,0 +1,223 @@
+/*
+ * wq.h - C ABI of libwq: weight-quantized matmul + AddRmsNorm and its
+ * companions, written for AMD Instinct MI355X (gfx950).
+ *
+ * Four operators, each following one operator page:
+ *   wq_pack_int4                  aclnnConvertWeightToINT4Pack
+ *   wq_dynamic_quant              aclnnDynamicQuant (plus an MX block-32 mode)
+ *   wq_matmul_add_rmsnorm         aclnnWeightQuantMatmulAllReduceAddRmsNorm
+ *                                 (single device: the AllReduce is the identity)
+ *   mx_quant_matmul_inplace_add   aclnnQuantBatchMatmulInplaceAdd (mx)
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major
+ *     ("ND") unless stated otherwise. Sizes are element counts.
+ *   - The library never allocates, frees or synchronizes. Work is enqueued on
+ *     `stream` (0 = the null stream) and the call returns at once; errors
+ *     raised by the kernels themselves surface at the caller's next sync.
+ *   - Arguments are validated on the host before anything is launched. On an
+ *     error the call returns a non-zero wq_status, launches nothing and
+ *     writes nothing.
+ *   - Two-phase pattern of the pages (GetWorkspaceSize, then execute) becomes
+ *     `*_workspace_size()` (pure host arithmetic) plus the execute call.
+ *   - Results are deterministic: every reduction has a fixed order.
+ *   - Calls that share a workspace must be ordered (same stream).
+ */
+#ifndef WQ_H_
+#define WQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wq_status {
+  WQ_OK = 0,
+  WQ_ERR_NULLPTR = 1,      /* a required pointer is null */
+  WQ_ERR_SHAPE = 2,        /* a size is out of range or shapes disagree */
+  WQ_ERR_DTYPE = 3,        /* unsupported dtype or dtype combination */
+  WQ_ERR_GROUP = 4,        /* group size / scale shape rule broken */
+  WQ_ERR_WORKSPACE = 5,    /* workspace missing or too small */
+  WQ_ERR_UNSUPPORTED = 6,  /* valid on the pages but not offered here */
+  WQ_ERR_LAUNCH = 7,       /* the HIP runtime refused a launch */
+  WQ_ERR_ALIAS = 8         /* an output overlaps an input it may not alias */
+} wq_status;
+
+typedef enum wq_dtype {
+  WQ_F16 = 1,
+  WQ_BF16 = 2,
+  WQ_F32 = 3,
+  WQ_INT8 = 4,
+  WQ_INT4 = 5,             /* two per byte, even index in the low nibble */
+  WQ_INT32 = 6,            /* as a quant output: eight INT4 per word, lowest nibble first */
+  WQ_FP8_E4M3 = 7,         /* OCP E4M3 (FN): bias 7, max 448, NaN = S.1111.111 */
+  WQ_FP4_E2M1 = 8,         /* OCP E2M1, two per byte like WQ_INT4 */
+  WQ_E8M0 = 9              /* one byte, value 2^(c-127) */
+} wq_dtype;
+
+typedef enum wq_layout {
+  /* (K, N) 4-bit codes packed along N: byte [k][n/2], even n in the low
+   * nibble. N must be even. */
+  WQ_LAYOUT_ND = 0,
+  /* gfx950 MFMA-operand order for a logical (K, N) matrix of 4-bit codes.
+   * Kp = 128*ceil(K/128), Np = 16*ceil(N/16), Kp*Np/2 bytes; the padding
+   * holds code 0. Code (k, n) sits in
+   *     byte   ((k/128)*Np + n)*64 + ((k/32)%4)*16 + (k%32)/2
+   *     nibble k%2  (0 = bits 0..3)
+   * so the 32 codes of one column in one 32-deep K block are 16 contiguous
+   * bytes (one dwordx4 per lane) and the 16 columns x 128 K read by one
+   * wavefront are 1 KiB contiguous. */
+  WQ_LAYOUT_GFX950_B = 1
+} wq_layout;
+
+/* Text of a status code (static storage). */
+const char* wq_status_string(wq_status status);
+
+/* Incremented when an entry point changes its arguments. */
+int wq_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * INT4 weight pack. aclnnConvertWeightToINT4Pack page, operator description:
+ * INT32 weights holding one 4-bit value each become tightly packed nibbles
+ * (the pages' FRACTAL_NZ output is replaced by WQ_LAYOUT_GFX950_B).
+ *
+ * weight     device int32, logical (k, n); stored (k, n) row-major, or
+ *            (n, k) row-major when transpose != 0.
+ * out        device, wq_pack_int4_bytes(k, n, layout) bytes.
+ * Stores v & 0xF for each value v (two's complement of an int4 in [-8, 7],
+ * or an FP4 E2M1 code 0..15). Values outside [-8, 15] are outside the
+ * contract: their low nibble is stored.
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE if k < 0, n < 0, or layout ND with n
+ * odd; WQ_ERR_UNSUPPORTED for an unknown layout. k == 0 or n == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+size_t wq_pack_int4_bytes(int64_t k, int64_t n, wq_layout layout);
+wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n,
+                       int transpose, wq_layout layout, void* out,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dynamic quantization. aclnnDynamicQuant page, Formula: with optional
+ * smooth scales, input = x * smooth; scale = row_max(|input|) / dtypeMax;
+ * y = round(input / scale). Constraints section: an INT4 output needs an even
+ * last dimension and an INT32 output one divisible by 8.
+ *
+ * x          device (rows, cols), x_dtype WQ_F16 or WQ_BF16 (leading
+ *            dimensions flattened into rows).
+ * smooth     device (cols) of x_dtype, or NULL.
+ * block_k == 0  per-token mode. y_dtype WQ_INT8 (y int8 (rows, cols)),
+ *            WQ_INT4 (y uint8 (rows, cols/2)) or WQ_INT32 (y int32
+ *            (rows, cols/8)); dtypeMax 127 for INT8 and 7 otherwise.
+ *            scale: device float32 (rows). The scale is the correctly rounded
+ *            float32 quotient row_max / dtypeMax, the code the float32
+ *            quotient input / scale rounded half to even, clamped to
+ *            [-dtypeMax, dtypeMax]; an all-zero row gives scale 0, codes 0.
+ * block_k == 32 MX mode (the 32-long K blocks of the
+ *            aclnnQuantBatchMatmulInplaceAdd page). y_dtype WQ_FP8_E4M3
+ *            (one byte per element) or WQ_FP4_E2M1 (two per byte).
+ *            scale: device uint8 E8M0 codes (rows, ceil(cols/32)), code
+ *            e + 127 with e the smallest integer such that
+ *            dtypeMax * 2^e >= block max (dtypeMax 448 / 6), clamped to
+ *            [-127, 127]; an all-zero block gets 127. Codes are
+ *            input * 2^-e rounded to nearest even, keeping the sign of zero.
+ *            transpose_y != 0 (WQ_FP8_E4M3 only) stores y as (cols, rows):
+ *            the transposeX1 layout of the MX matmul.
+ * Products x * smooth must be exact in float32 (always true for fp16).
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (negative sizes, odd cols for INT4 or
+ * FP4, cols % 8 for INT32); WQ_ERR_DTYPE; WQ_ERR_UNSUPPORTED (other block_k,
+ * transpose with a non-FP8 output). rows == 0 or cols == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+wq_status wq_dynamic_quant(const void* x, wq_dtype x_dtype, int64_t rows,
+                           int64_t cols, const void* smooth, wq_dtype y_dtype,
+                           int64_t block_k, int transpose_y, void* y,
+                           void* scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weight-quantized matmul + residual add + RMSNorm.
+ * aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula:
+ *     mm      = x1 @ (x2 * antiquantScale + antiquantOffset) + bias
+ *     y       = mm + residual
+ *     normOut = y / RMS(y) * gamma,  RMS(y) = sqrt(mean_n(y^2) + epsilon)
+ * (the page's AllReduce is the identity on one device). Constraints section:
+ * x1 (b, s, k) or (s, k), m = b*s in [0, 2^31-1]; x2 (k, n) with k in
+ * [1, 65535], n in [0, 65535]; bias (n); residual (b, s, n); gamma (n);
+ * per-tensor scale (1), per-channel (1, n) or (n), per-group (ceil(k/G), n)
+ * with G in [32, k-1] a multiple of 32; the offset has the scale's shape;
+ * m == 0 or n == 0 is an empty no-op, k == 0 an error; the inplace variant
+ * writes y into residual's memory.
+ *
+ * x1          device (m, k) of act_dtype (WQ_F16 or WQ_BF16), row-major.
+ * x2          device weight. w_dtype WQ_INT4: packed by wq_pack_int4 in
+ *             x2_layout (ND or GFX950_B), transpose_x2 must be 0 (pack the
+ *             transpose instead). w_dtype WQ_INT8: layout ND, (k, n)
+ *             row-major, or (n, k) row-major when transpose_x2 != 0.
+ * antiquant_scale   device act_dtype, (scale_rows, scale_cols):
+ *             (1, 1) per tensor, (1, n) per channel, (ceil(k/G), n) per group.
+ * antiquant_offset  device, same shape and dtype, or NULL (zero).
+ * antiquant_group_size  G for per-group scales, else 0.
+ * bias        device (n) act_dtype, or NULL (zero).
+ * residual    device (m, n) act_dtype.
+ * gamma       device (n) act_dtype.
+ * y           device (m, n) act_dtype; may equal residual (inplace).
+ * norm_out    device (m, n) act_dtype; may not overlap any other argument.
+ * workspace   device, >= wq_matmul_add_rmsnorm_workspace_size(m, k, n)
+ *             bytes, no initial contents needed.
+ * Numerics: each weight is dequantized in float32 (q * s + o), rounded to
+ * act_dtype and fed to the MFMA; or, when the group size is a multiple of
+ * 128 (and for per-channel/per-tensor scales), the integer codes go to the
+ * MFMA and the scale and offset are applied to the float32 partial sums of
+ * each group. Accumulation is float32; y is rounded to act_dtype once;
+ * RMS uses the float32 y.
+ * Errors: WQ_ERR_NULLPTR, WQ_ERR_SHAPE, WQ_ERR_DTYPE, WQ_ERR_GROUP,
+ * WQ_ERR_WORKSPACE, WQ_ERR_UNSUPPORTED, WQ_ERR_ALIAS (norm_out overlapping).
+ * ---------------------------------------------------------------------- */
+size_t wq_matmul_add_rmsnorm_workspace_size(int64_t m, int64_t k, int64_t n);
+wq_status wq_matmul_add_rmsnorm(
+    const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
+    const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
+    int transpose_x2,
+    const void* antiquant_scale, int64_t scale_rows, int64_t scale_cols,
+    const void* antiquant_offset, int64_t antiquant_group_size,
+    const void* bias, const void* residual, const void* gamma,
+    double epsilon, void* y, void* norm_out,
+    void* workspace, size_t workspace_size, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MX block-32 quantized matmul with in-place add.
+ * aclnnQuantBatchMatmulInplaceAdd page, Formula (mx quantization):
+ *     y[m,n] += sum_j (sum_{k in slice j} x1[m,k] * x2[k,n])
+ *                     * scale1[m,j] * scale2[j,n]
+ * with 32-long K slices, j < ceil(K/32), the last slice possibly shorter.
+ * Constraints section: only transposeX1 = true and transposeX2 = false;
+ * groupSize = groupSizeK | groupSizeN << 16 | groupSizeM << 32, a zero field
+ * inferred from the shapes.
+ *
+ * x1          device E4M3 codes stored (k, m) (transposeX1).
+ * x2          device E2M1 codes, logical (k, n), packed by wq_pack_int4 in
+ *             WQ_LAYOUT_GFX950_B (ND is rejected: WQ_ERR_UNSUPPORTED).
+ * x1_scale    device E8M0 (m, ceil(k/32)) = scale1[m][j].
+ * x2_scale    device E8M0 (ceil(k/32), n) = scale2[j][n].
+ * transpose_x1 must be 1, transpose_x2 must be 0 (else WQ_ERR_UNSUPPORTED).
+ * group_size  0 or 32 | 1 << 16 | 1 << 32 (= 4295032864); zero fields are
+ *             inferred (M and N by exact division, K as 32 when ceil(k/32)
+ *             slices match); anything else is WQ_ERR_GROUP.
+ * y           device float32 (m, n), read and written.
+ * workspace   may be NULL; wq's MX kernel needs none (size 0).
+ * Accumulation is float32; block sums are exact, the scaled sums are added
+ * in a fixed order. Empty m or n is a no-op; k == 0 leaves y unchanged.
+ * ---------------------------------------------------------------------- */
+size_t mx_quant_matmul_inplace_add_workspace_size(int64_t m, int64_t k, int64_t n);
+wq_status mx_quant_matmul_inplace_add(
+    const void* x1, const void* x2, wq_layout x2_layout,
+    const uint8_t* x1_scale, const uint8_t* x2_scale,
+    int64_t m, int64_t k, int64_t n, int transpose_x1, int transpose_x2,
+    int64_t group_size, float* y, void* workspace, size_t workspace_size,
+    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H_ */

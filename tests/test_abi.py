@@ -1,0 +1,177 @@
+"""The C ABI: the library loads, exports every entry point declared in
+include/wq.h, and its host-side validation rejects bad arguments before any
+launch. No test here launches a kernel: each call breaks a rule that is
+checked on the host, and the fake device addresses are never dereferenced."""
+import os
+import re
+
+import pytest
+
+import bit_quantized_gemm_int4_amd as wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(wq.LIB_PATH),
+                                reason="libwq.so not built (run __graft_entry__.build())")
+
+FAKE = 0x7F0000000000          # 16-byte aligned fake device address, never touched
+FAKE2 = 0x7F0000100000
+FAKE3 = 0x7F0000200000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:wq|mx)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 9, names
+    L = wq.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(wq.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert wq.lib().wq_abi_version() == 1
+    for code in range(9):
+        s = wq.lib().wq_status_string(code).decode()
+        assert s.startswith("WQ_")
+    assert wq.lib().wq_status_string(99).decode() == "unknown wq_status"
+
+
+def test_size_queries():
+    assert wq.wq_pack_int4_bytes(256, 128, wq.WQ_LAYOUT_ND) == 256 * 64
+    assert wq.wq_pack_int4_bytes(256, 128, wq.WQ_LAYOUT_GFX950_B) == 256 * 128 // 2
+    assert wq.wq_pack_int4_bytes(80, 20, wq.WQ_LAYOUT_GFX950_B) == 128 * 32 // 2
+    assert wq.wq_pack_int4_bytes(4, 3, wq.WQ_LAYOUT_ND) == 0
+    assert wq.wq_pack_int4_bytes(-1, 3, wq.WQ_LAYOUT_GFX950_B) == 0
+    ws = wq.wq_matmul_add_rmsnorm_workspace_size(4096, 8192, 8192)
+    assert ws >= 4096 * (8192 // 32) * 4
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(4096, 8192, 4096) == 0
+
+
+def _pack(**kw):
+    a = dict(weight=FAKE, k=64, n=64, transpose=0, layout=wq.WQ_LAYOUT_ND, out=FAKE2, stream=0)
+    a.update(kw)
+    return wq.lib().wq_pack_int4(a["weight"], a["k"], a["n"], a["transpose"], a["layout"],
+                                 a["out"], a["stream"])
+
+
+def test_pack_validation():
+    assert _pack(n=63) == wq.WQ_ERR_SHAPE
+    assert _pack(k=-1) == wq.WQ_ERR_SHAPE
+    assert _pack(layout=7) == wq.WQ_ERR_UNSUPPORTED
+    assert _pack(weight=None) == wq.WQ_ERR_NULLPTR
+    assert _pack(out=None, layout=wq.WQ_LAYOUT_GFX950_B) == wq.WQ_ERR_NULLPTR
+    assert _pack(out=FAKE2 + 4) == wq.WQ_ERR_SHAPE                 # misaligned output
+    assert _pack(out=FAKE + 64) == wq.WQ_ERR_ALIAS                 # overlaps the input
+    assert _pack(k=0) == wq.WQ_OK and _pack(n=0) == wq.WQ_OK       # empty: no-op
+
+
+def _quant(**kw):
+    a = dict(x=FAKE, x_dtype=wq.WQ_F16, rows=4, cols=64, smooth=None, y_dtype=wq.WQ_INT8,
+             block_k=0, transpose_y=0, y=FAKE2, scale=FAKE3, stream=0)
+    a.update(kw)
+    return wq.lib().wq_dynamic_quant(a["x"], a["x_dtype"], a["rows"], a["cols"], a["smooth"],
+                                     a["y_dtype"], a["block_k"], a["transpose_y"], a["y"],
+                                     a["scale"], a["stream"])
+
+
+def test_dynamic_quant_validation():
+    assert _quant(x_dtype=wq.WQ_F32) == wq.WQ_ERR_DTYPE
+    assert _quant(y_dtype=wq.WQ_FP8_E4M3) == wq.WQ_ERR_DTYPE        # per-token
+    assert _quant(y_dtype=wq.WQ_INT4, cols=63) == wq.WQ_ERR_SHAPE   # INT4: even cols
+    assert _quant(y_dtype=wq.WQ_INT32, cols=60) == wq.WQ_ERR_SHAPE  # INT32: cols % 8
+    assert _quant(transpose_y=1) == wq.WQ_ERR_UNSUPPORTED
+    assert _quant(block_k=16) == wq.WQ_ERR_UNSUPPORTED
+    assert _quant(block_k=32, y_dtype=wq.WQ_INT8) == wq.WQ_ERR_DTYPE
+    assert _quant(block_k=32, y_dtype=wq.WQ_FP4_E2M1, transpose_y=1) == wq.WQ_ERR_UNSUPPORTED
+    assert _quant(block_k=32, y_dtype=wq.WQ_FP4_E2M1, cols=63) == wq.WQ_ERR_SHAPE
+    assert _quant(rows=-1) == wq.WQ_ERR_SHAPE
+    assert _quant(scale=None) == wq.WQ_ERR_NULLPTR
+    assert _quant(x=FAKE + 2) == wq.WQ_ERR_SHAPE
+    assert _quant(rows=0) == wq.WQ_OK and _quant(cols=0) == wq.WQ_OK
+
+
+def _wqmm(**kw):
+    m, k, n = kw.pop("m", 16), kw.pop("k", 256), kw.pop("n", 128)
+    a = dict(x1=FAKE, act=wq.WQ_F16, x2=FAKE + 0x10000, w=wq.WQ_INT4,
+             layout=wq.WQ_LAYOUT_GFX950_B, tx2=0, scale=FAKE + 0x20000, srows=8, scols=n,
+             offset=None, group=32, bias=None, residual=FAKE + 0x30000, gamma=FAKE + 0x40000,
+             eps=1e-6, y=FAKE + 0x50000, norm=FAKE + 0x60000, ws=FAKE + 0x70000,
+             ws_size=1 << 20)
+    a.update(kw)
+    return wq.lib().wq_matmul_add_rmsnorm(
+        a["x1"], m, k, a["act"], a["x2"], n, a["w"], a["layout"], a["tx2"], a["scale"],
+        a["srows"], a["scols"], a["offset"], a["group"], a["bias"], a["residual"], a["gamma"],
+        a["eps"], a["y"], a["norm"], a["ws"], a["ws_size"], 0)
+
+
+def test_wq_matmul_validation_dtypes_and_layouts():
+    assert _wqmm(act=wq.WQ_F32) == wq.WQ_ERR_DTYPE
+    assert _wqmm(w=wq.WQ_FP8_E4M3) == wq.WQ_ERR_DTYPE
+    assert _wqmm(layout=5) == wq.WQ_ERR_UNSUPPORTED
+    assert _wqmm(tx2=1) == wq.WQ_ERR_UNSUPPORTED                    # int4: pack the transpose
+    assert _wqmm(w=wq.WQ_INT8) == wq.WQ_ERR_UNSUPPORTED             # int8 in GFX950_B
+
+
+def test_wq_matmul_validation_shapes():
+    assert _wqmm(k=0) == wq.WQ_ERR_SHAPE                             # k = 0 is not supported
+    assert _wqmm(k=65536, srows=2048) == wq.WQ_ERR_SHAPE
+    assert _wqmm(n=65536) == wq.WQ_ERR_SHAPE
+    assert _wqmm(m=-1) == wq.WQ_ERR_SHAPE
+    assert _wqmm(m=2 ** 31) == wq.WQ_ERR_SHAPE
+    assert _wqmm(n=127, layout=wq.WQ_LAYOUT_ND, scols=127) == wq.WQ_ERR_SHAPE
+    assert _wqmm(eps=-1.0) == wq.WQ_ERR_SHAPE
+    assert _wqmm(eps=float("nan")) == wq.WQ_ERR_SHAPE
+    assert _wqmm(x1=FAKE + 8) == wq.WQ_ERR_SHAPE                     # misaligned
+
+
+def test_wq_matmul_validation_groups():
+    assert _wqmm(group=16, srows=16) == wq.WQ_ERR_GROUP              # below 32
+    assert _wqmm(group=48, srows=6) == wq.WQ_ERR_GROUP               # not a multiple of 32
+    assert _wqmm(group=256, srows=1) == wq.WQ_ERR_GROUP              # G > k - 1
+    assert _wqmm(group=32, srows=7) == wq.WQ_ERR_GROUP               # rows != ceil(k/G)
+    assert _wqmm(group=32, scols=64) == wq.WQ_ERR_GROUP
+    assert _wqmm(group=0, srows=8) == wq.WQ_ERR_GROUP                # 2-D scale without G
+    assert _wqmm(group=0, srows=1, scols=7) == wq.WQ_ERR_GROUP
+
+
+def test_wq_matmul_validation_pointers_workspace_alias():
+    assert _wqmm(m=0) == wq.WQ_OK and _wqmm(n=0, scols=0) == wq.WQ_OK   # empty
+    assert _wqmm(gamma=None) == wq.WQ_ERR_NULLPTR
+    assert _wqmm(residual=None) == wq.WQ_ERR_NULLPTR
+    assert _wqmm(ws=None) == wq.WQ_ERR_WORKSPACE
+    assert _wqmm(ws_size=16) == wq.WQ_ERR_WORKSPACE
+    assert _wqmm(norm=FAKE + 0x30000) == wq.WQ_ERR_ALIAS             # norm_out == residual
+    assert _wqmm(norm=FAKE + 0x50000) == wq.WQ_ERR_ALIAS             # norm_out == y
+    assert _wqmm(y=FAKE + 0x30010) == wq.WQ_ERR_ALIAS                # y partially over residual
+    assert _wqmm(y=FAKE, m=16) == wq.WQ_ERR_ALIAS                    # y over x1
+
+
+def _mx(**kw):
+    a = dict(x1=FAKE, x2=FAKE2, layout=wq.WQ_LAYOUT_GFX950_B, s1=FAKE3, s2=FAKE3 + 0x10000,
+             m=64, k=256, n=64, t1=1, t2=0, group=wq.MX_GROUP_SIZE, y=FAKE3 + 0x100000)
+    a.update(kw)
+    return wq.lib().mx_quant_matmul_inplace_add(a["x1"], a["x2"], a["layout"], a["s1"], a["s2"],
+                                                a["m"], a["k"], a["n"], a["t1"], a["t2"],
+                                                a["group"], a["y"], None, 0, 0)
+
+
+def test_mx_matmul_validation():
+    assert wq.MX_GROUP_SIZE == 4295032864
+    assert _mx(t1=0) == wq.WQ_ERR_UNSUPPORTED                        # only transposeX1 = true
+    assert _mx(t2=1) == wq.WQ_ERR_UNSUPPORTED                        # only transposeX2 = false
+    assert _mx(layout=wq.WQ_LAYOUT_ND) == wq.WQ_ERR_UNSUPPORTED
+    assert _mx(group=64) == wq.WQ_ERR_GROUP
+    assert _mx(group=32 | (2 << 16)) == wq.WQ_ERR_GROUP
+    assert _mx(group=-1) == wq.WQ_ERR_GROUP
+    assert _mx(m=-3) == wq.WQ_ERR_SHAPE
+    assert _mx(y=None) == wq.WQ_ERR_NULLPTR
+    assert _mx(y=FAKE2 + 4) == wq.WQ_ERR_SHAPE
+    assert _mx(y=FAKE2 + 16) == wq.WQ_ERR_ALIAS                      # y over x2
+    assert _mx(m=0) == wq.WQ_OK and _mx(k=0) == wq.WQ_OK

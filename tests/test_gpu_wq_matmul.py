@@ -1,0 +1,152 @@
+"""GPU parity: wq_matmul_add_rmsnorm against the float64 oracle.
+
+Tolerance: max_i |gpu_i - oracle_i| / max(|oracle_i|, RMS(oracle)) <= 1e-2
+for the fp16/bf16 outputs y and normOut; bit-exact y for integer-valued
+inputs whose partial sums are all exactly representable."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_gemm_int4_amd as wq
+import oracle
+import workloads
+from oracle import as_f64
+from tests.gpu_util import DEV, check_wq, note, wq_on_gpu
+
+pytestmark = pytest.mark.gpu
+
+B, ND = wq.WQ_LAYOUT_GFX950_B, wq.WQ_LAYOUT_ND
+
+
+def test_tiny_workload():
+    c = workloads.tiny()
+    for layout in (B, ND):
+        note(f"wq tiny fp16 g32 layout={layout}")
+        y, n = wq_on_gpu(c, layout)
+        check_wq(c, y, n)
+
+
+def test_w8_workload():
+    c = workloads.w8()
+    for t in (False, True):
+        note(f"wq w8 per-channel transpose_x2={t}")
+        y, n = wq_on_gpu(c, transpose_x2=t)
+        check_wq(c, y, n)
+
+
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_decode_workload(m):
+    c = workloads.decode(m)
+    note(f"wq decode m={m}")
+    y, n = wq_on_gpu(c)
+    check_wq(c, y, n)
+
+
+def test_prefill_workload_sampled_rows():
+    c = workloads.prefill()
+    note("wq prefill 4096x8192x8192 (sampled rows)")
+    y, n = wq_on_gpu(c)
+    rows = np.array([0, 1, 255, 256, 1023, 2048, 3071, 4094, 4095])
+    check_wq(c, y, n, rows=rows)
+    # every row: finite, and normOut has RMS(normOut / gamma) close to 1
+    nn = as_f64(n) / as_f64(c.gamma)[None, :]
+    rms = np.sqrt(np.mean(nn * nn, axis=1))
+    assert np.all(np.abs(rms - 1) < 1e-2)
+
+
+SHAPES = [  # m, k, n, granularity, group, offset, bias, act
+    (17, 80, 20, "group", 32, (-0.5, 0.5), 0.1, torch.float16),
+    (1, 64, 2, "tensor", 0, (-0.5, 0.5), 0.1, torch.bfloat16),
+    (33, 100, 70, "channel", 0, "none", None, torch.bfloat16),
+    (65, 257, 48, "channel2d", 0, (-0.5, 0.5), 0.1, torch.float16),
+    (130, 512, 96, "group", 64, None, 0.1, torch.bfloat16),
+    (5, 384, 130, "group", 128, (-1.0, 1.0), None, torch.bfloat16),
+    (3, 32, 16, "tensor", 0, "none", 0.1, torch.float16),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}" for s in SHAPES])
+@pytest.mark.parametrize("layout", [B, ND])
+def test_edge_shapes_int4(shape, layout):
+    m, k, n, gran, g, off, bias, act = shape
+    if layout == ND and n % 2:
+        pytest.skip("ND packs pairs along n")
+    c = workloads.wq_case(f"edge{m}x{k}x{n}", m, k, n, act=act, w_bits=4, granularity=gran,
+                          group_size=g, offset_range=off, bias_std=bias, seed=m + k + n)
+    note(f"wq edge int4 {c.name} {gran} g={g} layout={layout}")
+    y, nrm = wq_on_gpu(c, layout)
+    check_wq(c, y, nrm)
+
+
+@pytest.mark.parametrize("shape", SHAPES[:4], ids=[f"{s[0]}x{s[1]}x{s[2]}" for s in SHAPES[:4]])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_edge_shapes_int8(shape, transpose):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"edge8_{m}x{k}x{n}", m, k, n, act=act, w_bits=8, granularity=gran,
+                          group_size=g, scale_range=(0.001, 0.01), offset_range=off,
+                          bias_std=bias, seed=m * k + n)
+    note(f"wq edge int8 {c.name} transpose={transpose}")
+    y, nrm = wq_on_gpu(c, transpose_x2=transpose)
+    check_wq(c, y, nrm)
+
+
+def test_inplace_matches_out_of_place():
+    c = workloads.tiny()
+    note("wq inplace tiny")
+    y0, n0 = wq_on_gpu(c)
+    y1, n1 = wq_on_gpu(c, inplace=True)
+    assert torch.equal(y0, y1) and torch.equal(n0, n1)
+
+
+def test_deterministic():
+    c = workloads.decode(16)
+    note("wq determinism decode m=16")
+    y0, n0 = wq_on_gpu(c)
+    y1, n1 = wq_on_gpu(c)
+    assert torch.equal(y0, y1) and torch.equal(n0, n1)
+
+
+@pytest.mark.parametrize("act", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("k,G", [(256, 32), (512, 128), (384, 0)])
+def test_integer_valued_y_is_bit_exact(act, k, G):
+    # Sparse x1 in {-1,0,1}, int4 weights, scale 1, offset 0, bias 0 and an
+    # integer residual: every partial sum is an integer far below 2^24 and
+    # |y| <= 256, so y is exact in fp16 and bf16 alike.
+    m, n = 20, 64
+    rng = np.random.default_rng(k + G)
+    xv = rng.integers(-1, 2, (m, k)) * (rng.random((m, k)) < 0.25)
+    x1 = torch.from_numpy(xv.astype(np.float32)).to(act)
+    w = torch.from_numpy(rng.integers(-8, 8, (k, n), dtype=np.int32))
+    srows = (k + G - 1) // G if G else 1
+    scale = torch.ones((srows, n) if G else (1,), dtype=act)
+    res = torch.from_numpy(rng.integers(-4, 5, (1, m, n)).astype(np.float32)).to(act)
+    c = workloads.WQCase("intexact", x1, w, 4, scale, torch.zeros_like(scale), G,
+                         torch.zeros(n, dtype=act), res, torch.ones(n, dtype=act), 1e-6)
+    _, oy, on = oracle.wq_matmul_add_rmsnorm(as_f64(x1), w.numpy(), as_f64(scale), None, G, None,
+                                             as_f64(res).reshape(m, n), np.ones(n), 1e-6)
+    assert np.max(np.abs(oy)) <= 256            # the case's own precondition
+    note(f"wq integer-exact {act} k={k} G={G}")
+    y, nrm = wq_on_gpu(c)
+    assert np.array_equal(as_f64(y).reshape(m, n), oy)
+    assert oracle.rel_err_floor(nrm, on) <= 1e-2
+
+
+def test_one_hot_rows_pin_group_indexing():
+    k, n, G = 256, 32, 32
+    m = 8
+    rows = [0, 31, 32, 100, 128, 200, 224, 255]
+    x1 = torch.zeros((m, k), dtype=torch.bfloat16)
+    for i, r in enumerate(rows):
+        x1[i, r] = 1.0
+    c = workloads.wq_case("onehot", m, k, n, act=torch.bfloat16, w_bits=4, granularity="group",
+                          group_size=G, offset_range=(-1, 1), bias_std=None, seed=5)
+    c.x1 = x1
+    c.residual = torch.zeros_like(c.residual)
+    note("wq one-hot rows")
+    y, nrm = wq_on_gpu(c)
+    _, oy, _ = oracle.wq_matmul_add_rmsnorm(as_f64(x1), c.w.numpy(), as_f64(c.scale),
+                                            as_f64(c.offset), G, None, np.zeros((m, n)),
+                                            np.ones(n), 1e-6)
+    # y is the dequantized weight row, rounded once to bf16 (plus a bf16
+    # rounding of the dequantized weight on the dequant-before-MFMA path)
+    assert oracle.rel_err_floor(y.reshape(m, n), oy) <= 8e-3
