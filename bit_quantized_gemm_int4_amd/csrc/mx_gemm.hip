@@ -7,8 +7,11 @@
 // gfx950's scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4 computes a 16x16
 // tile over 128 K with one E8M0 scale per (row, 32-block) of A and per
 // (column, 32-block) of B: exactly the page's block-scaled sum. Lane l
-// supplies row/column l%16 and the 32 K values of block l/16 (32 E4M3 bytes
-// for A, 32 E2M1 nibbles = 16 bytes for B) plus that block's scale byte.
+// supplies row/column l%16 and the scale byte of 32-block l/16. Operand
+// order, measured on the device with one-hot and random probes: the B lane
+// (E2M1) holds the 32 K values of block l/16 as 16 bytes, low nibble first;
+// the A lane (E4M3) holds K 16*(l/16) .. +16 in bytes 0..15 and
+// K 64 + 16*(l/16) .. +16 in bytes 16..31.
 // Since GFX950_B stores each column's 32-deep block as 16 contiguous bytes,
 // a B fragment is one dwordx4 load straight from global memory. A arrives
 // K-major, so the workgroup transposes its A tile into LDS ([m][k] bytes).
@@ -53,8 +56,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = wr * 32 + i * 16 + (lane & 15);
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(&As[r][kbl * 32]);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(&As[r][kbl * 32 + 16]);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(&As[r][kbl * 16]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(&As[r][64 + kbl * 16]);
       af[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       const int64_t row = m0 + r;

@@ -11,9 +11,9 @@
 //      1/RMS and writes normOut = y * rstd * gamma.
 // GEMM kernels:
 //   - gemm_generic: any weight layout (INT4 ND / GFX950_B, INT8 ND /
-//     transposed), 64x64x32 tiles, both operands staged in LDS, the weight
-//     dequantized (q * s + o in float32, rounded to the activation dtype)
-//     while it is written to LDS.
+//     transposed), any group size, 64x64x32 tiles with both operands staged
+//     in LDS; integer codes go to the MFMA and each group's scale and
+//     offset are applied to its float32 partial sums.
 #include "wq_device.h"
 #include "wq_internal.h"
 
@@ -34,15 +34,6 @@ struct GemmArgs {
   int64_t m, k, n, np;   // np: padded N of the GFX950_B layout
   int64_t group, s_row, s_col;
 };
-
-// Dequantize one code q at (k, n) to float32: q * s + o.
-template <int ACT>
-__device__ __forceinline__ float dequant(const GemmArgs& a, int q, int64_t k, int64_t n) {
-  const int64_t si = (k / a.group) * a.s_row + n * a.s_col;
-  float w = (float)q * to_f32<ACT>(a.scale[si]);
-  if (a.offset) w += to_f32<ACT>(a.offset[si]);
-  return w;
-}
 
 // Epilogue for one 16x16 MFMA tile held by a wave: y = acc + bias + residual,
 // stored rounded; returns the float32 y values (0 outside the matrix).
@@ -67,6 +58,12 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x4& ac
 
 constexpr int GB_M = 64, GB_N = 64, GB_K = 32, G_LDS = GB_K + 8;
 
+// One K step of 32 covers a single quantization group (G is a multiple of 32),
+// so each 16x16x32 MFMA sums x1 * q for one group. The codes enter the MFMA
+// exactly (|q| <= 127 fits both 16-bit formats); the group's scale and offset
+// are applied to the float32 partial when the group ends:
+//   acc += s[g, n] * sum_k x1[r, k] q[k, n] + o[g, n] * sum_k x1[r, k]
+// with the row sums from one more MFMA against a fragment of ones.
 template <int ACT, int WF>
 __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[GB_M][G_LDS];
@@ -76,7 +73,9 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
   const int64_t m0 = (int64_t)blockIdx.x * GB_M;
   const int64_t n0 = (int64_t)blockIdx.y * GB_N;
   const bool avec = (a.k & 7) == 0;
-  f32x4 acc[2][2] = {};
+  const uint32_t one2 = pack2<ACT>(1.f, 1.f);
+  const u32x4 ones = {one2, one2, one2, one2};
+  f32x4 acc[2][2] = {}, part[2][2] = {}, rsum[2] = {};
 
   for (int64_t k0 = 0; k0 < a.k; k0 += GB_K) {
     // ---- A tile: thread -> row t/4, 8 consecutive k ----
@@ -100,7 +99,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
       }
       *reinterpret_cast<u32x4*>(&As[r][kc]) = v;
     }
-    // ---- B tile, dequantized, stored [n][k] ----
+    // ---- B tile: integer codes as 16-bit floats, stored [n][k] ----
     if constexpr (WF == W_I4_B || WF == W_I8_T) {
       // thread -> column t/4, 8 consecutive k
       const int c = t >> 2, kc = (t & 3) * 8;
@@ -118,15 +117,11 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
         for (int i = 0; i < 8; ++i)
           q[i] = (col < a.n && kk + i < a.k) ? (int)(int8_t)a.x2[col * a.k + kk + i] : 0;
       }
-      float w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = (col < a.n && kk + i < a.k) ? dequant<ACT>(a, q[i], kk + i, col) : 0.f;
       u32x4 v;
-      v.x = pack2<ACT>(w[0], w[1]);
-      v.y = pack2<ACT>(w[2], w[3]);
-      v.z = pack2<ACT>(w[4], w[5]);
-      v.w = pack2<ACT>(w[6], w[7]);
+      v.x = pack2<ACT>((float)q[0], (float)q[1]);
+      v.y = pack2<ACT>((float)q[2], (float)q[3]);
+      v.z = pack2<ACT>((float)q[4], (float)q[5]);
+      v.w = pack2<ACT>((float)q[6], (float)q[7]);
       *reinterpret_cast<u32x4*>(&Bs[c][kc]) = v;
     } else {
       // row-major (k, n): thread -> k row t/8, 8 consecutive columns
@@ -135,22 +130,20 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t col = n0 + nc + i;
-        float w = 0.f;
+        int q = 0;
         if (kk < a.k && col < a.n) {
-          int q;
           if constexpr (WF == W_I4_ND) {
             const uint8_t b = a.x2[kk * (a.n / 2) + col / 2];
             q = (col & 1) ? ((int)(int8_t)b >> 4) : (((int)(int8_t)(b << 4)) >> 4);
           } else {
             q = (int)(int8_t)a.x2[kk * a.n + col];
           }
-          w = dequant<ACT>(a, q, kk, col);
         }
-        Bs[nc + i][r] = from_f32<ACT>(w);
+        Bs[nc + i][r] = from_f32<ACT>((float)q);
       }
     }
     __syncthreads();
-    // ---- MFMA: each wave 32x32 = 2x2 tiles of 16x16 ----
+    // ---- MFMA: each wave 32x32 = 2x2 tiles of 16x16, one group's partial ----
     const int kq = (lane >> 4) * 8;
     u32x4 af[2], bf[2];
 #pragma unroll
@@ -159,9 +152,35 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
       bf[i] = *reinterpret_cast<const u32x4*>(&Bs[wc * 32 + i * 16 + (lane & 15)][kq]);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<ACT>(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) part[i][j] = mfma16<ACT>(af[i], bf[j], part[i][j]);
+      if (a.offset) rsum[i] = mfma16<ACT>(af[i], ones, rsum[i]);
+    }
+    // ---- group end: fold scale and offset into the float32 accumulator ----
+    const int64_t g = k0 / a.group;
+    if ((k0 + GB_K) % a.group == 0 || k0 + GB_K >= a.k) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + wc * 32 + j * 16 + (lane & 15);
+        float sv = 0.f, ov = 0.f;
+        if (col < a.n) {
+          const int64_t si = g * a.s_row + col * a.s_col;
+          sv = to_f32<ACT>(a.scale[si]);
+          if (a.offset) ov = to_f32<ACT>(a.offset[si]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[i][j][r] = fmaf(sv, part[i][j][r], acc[i][j][r]);
+            if (a.offset) acc[i][j][r] = fmaf(ov, rsum[i][r], acc[i][j][r]);
+            part[i][j][r] = 0.f;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) rsum[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
     __syncthreads();
   }
 

@@ -164,12 +164,12 @@ wq_status wq_dynamic_quant(const void* x, wq_dtype x_dtype, int64_t rows,
  * norm_out    device (m, n) act_dtype; may not overlap any other argument.
  * workspace   device, >= wq_matmul_add_rmsnorm_workspace_size(m, k, n)
  *             bytes, no initial contents needed.
- * Numerics: each weight is dequantized in float32 (q * s + o), rounded to
- * act_dtype and fed to the MFMA; or, when the group size is a multiple of
- * 128 (and for per-channel/per-tensor scales), the integer codes go to the
- * MFMA and the scale and offset are applied to the float32 partial sums of
- * each group. Accumulation is float32; y is rounded to act_dtype once;
- * RMS uses the float32 y.
+ * Numerics: the integer codes enter the MFMA exactly (as act_dtype values)
+ * and each group's scale and offset are applied to that group's float32
+ * partial sums: mm = sum_g (s_g * sum_{k in g} x1*q + o_g * sum_{k in g} x1),
+ * which equals the Formula's x1 @ (q*s + o) without rounding the dequantized
+ * weight. Accumulation is float32; y is rounded to act_dtype once; RMS uses
+ * the float32 y; normOut = y * rstd * gamma rounded once.
  * Errors: WQ_ERR_NULLPTR, WQ_ERR_SHAPE, WQ_ERR_DTYPE, WQ_ERR_GROUP,
  * WQ_ERR_WORKSPACE, WQ_ERR_UNSUPPORTED, WQ_ERR_ALIAS (norm_out overlapping).
  * ---------------------------------------------------------------------- */

@@ -67,6 +67,10 @@ def check_wq(case, y, norm, rows=None, tol=1e-2):
         gy, gn = gy[rows], gn[rows]
     ey = oracle.rel_err_floor(gy, oy)
     en = oracle.rel_err_floor(gn, on)
+    note(f"  {case.name}: y rel err {ey:.3e}, normOut rel err {en:.3e}")
+    if ey > tol or en > tol:
+        bad = np.argsort(-np.max(np.abs(gn - on) / np.maximum(np.abs(on), 1e-3), axis=1))[:8]
+        note(f"  worst rows {bad.tolist()}")
     assert np.all(np.isfinite(gy)) and np.all(np.isfinite(gn))
     assert ey <= tol, f"{case.name}: y rel err {ey}"
     assert en <= tol, f"{case.name}: normOut rel err {en}"

@@ -42,14 +42,13 @@ def test_decode_workload(m):
     check_wq(c, y, n)
 
 
-def test_prefill_workload_sampled_rows():
+def test_prefill_workload_all_rows():
     c = workloads.prefill()
-    note("wq prefill 4096x8192x8192 (sampled rows)")
+    note("wq prefill 4096x8192x8192 (all rows against the full oracle)")
     y, n = wq_on_gpu(c)
-    rows = np.array([0, 1, 255, 256, 1023, 2048, 3071, 4094, 4095])
-    check_wq(c, y, n, rows=rows)
-    # every row: finite, and normOut has RMS(normOut / gamma) close to 1
-    nn = as_f64(n) / as_f64(c.gamma)[None, :]
+    check_wq(c, y, n)
+    # invariant on every row: RMS(normOut / gamma) = sqrt(ms / (ms + eps)) ~ 1
+    nn = as_f64(n).reshape(-1, 8192) / as_f64(c.gamma)[None, :]
     rms = np.sqrt(np.mean(nn * nn, axis=1))
     assert np.all(np.abs(rms - 1) < 1e-2)
 
@@ -147,6 +146,5 @@ def test_one_hot_rows_pin_group_indexing():
     _, oy, _ = oracle.wq_matmul_add_rmsnorm(as_f64(x1), c.w.numpy(), as_f64(c.scale),
                                             as_f64(c.offset), G, None, np.zeros((m, n)),
                                             np.ones(n), 1e-6)
-    # y is the dequantized weight row, rounded once to bf16 (plus a bf16
-    # rounding of the dequantized weight on the dequant-before-MFMA path)
-    assert oracle.rel_err_floor(y.reshape(m, n), oy) <= 8e-3
+    # y is the dequantized weight row q * s + o, rounded once to bf16
+    assert oracle.rel_err_floor(y.reshape(m, n), oy) <= 2.0 ** -8
