@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-quantized matmul hot path on one MI355X.
+
+One step runs every operator of the path once, each on its workload, on
+torch's current stream:
+  1. wq_pack_int4          prefill weight (8192, 8192) int32 -> GFX950_B
+  2. wq_matmul_add_rmsnorm prefill W4A16 group 128 + AddRmsNorm, bf16,
+                           x1 (4, 1024, 8192), x2 (8192, 8192)
+  3. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
+  4. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
+  5. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
+Every operator is timed with HIP events around its launch(es). The headline
+``value`` is the W4A16 dequant-GEMM + AddRmsNorm throughput of row 2 in
+TFLOP/s (2*M*N*K per call). A separate decode section times the HBM-bound
+W4A16 decode shapes (m in {1, 8, 16}, k 4096, n 11008) rotating 24 weight
+copies so that the 256 MB last-level cache cannot hold them.
+
+Prints one JSON line. Inputs are seeded synthetic tensors of the workloads'
+shapes and distributions, resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (the E4M3 x E2M1 MX rate)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of rows to run (profiling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_gemm_int4_amd as wq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wq.lib()                                  # fails loudly if libwq.so is missing
+    stream = torch.cuda.current_stream()
+    only = set(filter(None, args.only.split(",")))
+    want = lambda name: not only or name in only
+
+    # ---------------- inputs (untimed) ----------------
+    pf = workloads.prefill()
+    M, K, N = pf.mkn
+    w_i32 = pf.w.to(dev)
+    x1 = pf.x1.to(dev)
+    scale, offset = pf.scale.to(dev), pf.offset.to(dev)
+    bias, residual, gamma = pf.bias.to(dev), pf.residual.to(dev), pf.gamma.to(dev)
+    x2 = torch.empty(wq.wq_pack_int4_bytes(K, N, wq.WQ_LAYOUT_GFX950_B), dtype=torch.uint8,
+                     device=dev)
+    wq.wq_pack_int4(w_i32, K, N, 0, wq.WQ_LAYOUT_GFX950_B, x2)
+    y = torch.empty_like(residual)
+    norm = torch.empty_like(residual)
+    ws_n = wq.wq_matmul_add_rmsnorm_workspace_size(M, K, N)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device=dev)
+    s_rows, s_cols = scale.shape
+
+    mxc = workloads.mx(draw_w=False)
+    MM, MK, MN = mxc.mkn
+    xq_in, smooth = mxc.x.to(dev), mxc.smooth.to(dev)
+    q8 = torch.empty((MM, MK), dtype=torch.int8, device=dev)
+    q8s = torch.empty(MM, dtype=torch.float32, device=dev)
+    x1q = torch.empty((MK, MM), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((MM, MK // 32), dtype=torch.uint8, device=dev)
+    x2mx = torch.empty(wq.wq_pack_int4_bytes(MK, MN, wq.WQ_LAYOUT_GFX950_B), dtype=torch.uint8,
+                       device=dev)
+    wq.wq_pack_int4(mxc.x2_codes.to(dev), MK, MN, 0, wq.WQ_LAYOUT_GFX950_B, x2mx)
+    s2 = mxc.x2_scale.to(dev)
+    ymx = mxc.y.to(dev)
+    del mxc
+    torch.cuda.synchronize()
+
+    def op_pack():
+        wq.wq_pack_int4(w_i32, K, N, 0, wq.WQ_LAYOUT_GFX950_B, x2)
+
+    def op_wq():
+        wq.wq_matmul_add_rmsnorm(x1, M, K, wq.WQ_BF16, x2, N, wq.WQ_INT4, wq.WQ_LAYOUT_GFX950_B, 0,
+                                 scale, s_rows, s_cols, offset, pf.group_size, bias, residual,
+                                 gamma, pf.eps, y, norm, ws, ws_n)
+
+    def op_quant_tok():
+        wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_INT8, 0, 0, q8, q8s)
+
+    def op_quant_mx():
+        wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_FP8_E4M3, 32, 1, x1q, s1)
+
+    def op_mx():
+        wq.mx_quant_matmul_inplace_add(x1q, x2mx, wq.WQ_LAYOUT_GFX950_B, s1, s2, MM, MK, MN, 1, 0,
+                                       wq.MX_GROUP_SIZE, ymx)
+
+    # algorithmic work per call (inputs + outputs as passed; packed weights)
+    rows = [
+        ("pack", op_pack, 0, K * N * 4 + x2.numel(), "hbm"),
+        ("wq_matmul_add_rmsnorm", op_wq, 2 * M * N * K,
+         x1.numel() * 2 + x2.numel() + 2 * scale.numel() * 2 + N * 2 * 2 + 3 * M * N * 2, "mfma"),
+        ("dynamic_quant_int8", op_quant_tok, 0, MM * MK * 2 + MK * 2 + MM * MK + MM * 4, "hbm"),
+        ("dynamic_quant_mx", op_quant_mx, 0, MM * MK * 2 + MK * 2 + MM * MK + s1.numel(), "hbm"),
+        ("mx_matmul_inplace_add", op_mx, 2 * MM * MN * MK,
+         x1q.numel() + x2mx.numel() + s1.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
+    ]
+    rows = [r for r in rows if want(r[0])]
+
+    def step(record):
+        for name, fn, _, _, _ in rows:
+            if record is not None:
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                fn()
+                ev1.record(stream)
+                record[name].append((ev0, ev1))
+            else:
+                fn()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    rec = {r[0]: [] for r in rows}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
+
+    out_rows = {}
+    for name, _, flop, nbytes, bound in rows:
+        times = [a.elapsed_time(b) for a, b in rec[name]]
+        ms = statistics.median(times)
+        d = {"ms": round(ms, 5), "ms_mean": round(statistics.mean(times), 5),
+             "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
+        if flop:
+            d["TFLOP/s"] = round(flop / ms / 1e9, 2)
+            d["flop"] = flop
+        peak = PEAK_BF16_TFLOPS if name == "wq_matmul_add_rmsnorm" else PEAK_FP8_TFLOPS
+        d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
+                                  else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
+        out_rows[name] = d
+
+    # ---------------- decode section (HBM-bound) ----------------
+    decode = {}
+    if want("decode"):
+        dc = workloads.decode(16)
+        dm, dk, dn = dc.mkn
+        copies = 24
+        w_d = dc.w.to(dev)
+        xb = [torch.empty(wq.wq_pack_int4_bytes(dk, dn, wq.WQ_LAYOUT_GFX950_B), dtype=torch.uint8,
+                          device=dev) for _ in range(copies)]
+        for b in xb:
+            wq.wq_pack_int4(w_d, dk, dn, 0, wq.WQ_LAYOUT_GFX950_B, b)
+        del w_d
+        sd, od = dc.scale.to(dev), dc.offset.to(dev)
+        bd, gd = dc.bias.to(dev), dc.gamma.to(dev)
+        x1d, resd = dc.x1.to(dev), dc.residual.to(dev)
+        for m in (1, 8, 16):
+            xm = x1d[:m].contiguous()
+            rm = resd[:, :m].contiguous()
+            ym, nm = torch.empty_like(rm), torch.empty_like(rm)
+            wsn = wq.wq_matmul_add_rmsnorm_workspace_size(m, dk, dn)
+            wsd = torch.zeros(wsn, dtype=torch.uint8, device=dev)
+            call = lambda i: wq.wq_matmul_add_rmsnorm(
+                xm, m, dk, wq.WQ_BF16, xb[i % copies], dn, wq.WQ_INT4, wq.WQ_LAYOUT_GFX950_B, 0,
+                sd, sd.shape[0], sd.shape[1], od, dc.group_size, bd, rm, gd, dc.eps, ym, nm,
+                wsd, wsn)
+            for i in range(2 * copies):
+                call(i)
+            evs = []
+            for i in range(args.decode_iters):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                call(i)
+                b.record(stream)
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in evs)
+            med = statistics.median(ts)
+            nbytes = (xb[0].numel() + 2 * sd.numel() * 2 + m * dk * 2 + 3 * m * dn * 2 + 2 * dn * 2)
+            decode[f"m{m}"] = {"us": round(med * 1e3, 3), "us_p10": round(ts[len(ts) // 10] * 1e3, 3),
+                               "us_p90": round(ts[(9 * len(ts)) // 10] * 1e3, 3),
+                               "GB/s": round(nbytes / med / 1e6, 1), "bytes": nbytes,
+                               "frac_of_hbm_peak": round(nbytes / med / 1e6 / PEAK_HBM_GBS, 4)}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu_baseline and want("wq_matmul_add_rmsnorm"):
+        import oracle
+        sample_rows = 256
+        f = oracle.as_f64
+        x_s = f(pf.x1).reshape(M, K)[:sample_rows]
+        r_s = f(pf.residual).reshape(M, N)[:sample_rows]
+        w_np, s_np, o_np = pf.w.numpy(), f(pf.scale), f(pf.offset)
+        b_np, g_np = f(pf.bias), f(pf.gamma)
+        reps, t_cpu = 0, 0.0
+        while t_cpu < 12.0 and reps < 200:
+            c0 = time.perf_counter()
+            oracle.wq_matmul_add_rmsnorm(x_s, w_np, s_np, o_np, pf.group_size, b_np, r_s, g_np, pf.eps)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        per_call = t_cpu / reps
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count()
+        cpu = {"value": round(2 * sample_rows * N * K / per_call / 1e12, 5), "unit": "TFLOP/s",
+               "cores": cores, "kind": "oracle",
+               "sample": f"prefill W4A16 g128 + AddRmsNorm, first {sample_rows} of {M} rows "
+                         f"(k {K}, n {N}), float64 numpy, {reps} call(s), "
+                         f"{per_call:.2f} s per call", "cpu": platform.processor() or platform.machine()}
+
+    head = out_rows.get("wq_matmul_add_rmsnorm")
+    value = head["TFLOP/s"] if head else None
+    line = {
+        "metric": "W4A16 dequant-GEMM+AddRmsNorm TFLOP/s & HBM GB/s, % of MI355X roofline",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill W4A16 group-128 dequant-GEMM + AddRmsNorm, "
+                               "x1 bf16 (4,1024,8192), x2 int4 (8192,8192), offset zeros",
+                   "m": M, "k": K, "n": N, "group_size": pf.group_size,
+                   "step": [r[0] for r in rows]},
+        "roofline": None,
+        "rows": out_rows,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    if head:
+        line["roofline"] = {"bound": "mfma", "achieved": head["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(head["TFLOP/s"] / PEAK_BF16_TFLOPS, 4),
+                            "traffic": None,
+                            "kernel": "wq_matmul_add_rmsnorm (all launches of one call)"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
