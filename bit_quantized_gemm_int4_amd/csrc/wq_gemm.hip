@@ -281,10 +281,17 @@ hipError_t launch_finish(const WqProblem& p, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
-  (void)k;
+namespace {
+size_t partial_bytes(int64_t m, int64_t n) {
   const int64_t tiles = (n + 31) / 32;
-  return (size_t)(tiles * m * (int64_t)sizeof(float)) + 256;
+  return ((size_t)(tiles * m) * sizeof(float) + 255) & ~(size_t)255;
+}
+}  // namespace
+
+// Workspace: per-(32-column tile, row) partial sums of y^2, then (fast path)
+// per-group row sums of x1 as bf16 hi/lo.
+size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  return partial_bytes(m, n) + fast_rowsum_bytes(m, k) + 256;
 }
 
 hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
@@ -304,7 +311,14 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
   a.group = p.group;
   a.s_row = p.s_row;
   a.s_col = p.s_col;
-  hipError_t e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
+  hipError_t e;
+  if (fast_path_ok(p) && p.m > 32) {
+    uint16_t* rs = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.workspace) +
+                                               partial_bytes(p.m, p.n));
+    e = launch_prefill(p, a.partial, rs, s);
+  } else {
+    e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
+  }
   if (e != hipSuccess) return e;
   return p.bf16 ? launch_finish<ACT_BF16>(p, a, s) : launch_finish<ACT_F16>(p, a, s);
 }

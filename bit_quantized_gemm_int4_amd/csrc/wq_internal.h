@@ -49,6 +49,11 @@ struct WqProblem {
 size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n);
 hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s);
 
+// Fast GFX950_B INT4 path (group a multiple of 128, or per channel/tensor).
+bool fast_path_ok(const WqProblem& p);
+size_t fast_rowsum_bytes(int64_t m, int64_t k);
+hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, hipStream_t s);
+
 struct MxProblem {
   const uint8_t* x1;     // (k, m) e4m3
   const uint8_t* x2;     // GFX950_B e2m1

@@ -148,3 +148,26 @@ def test_one_hot_rows_pin_group_indexing():
                                             np.ones(n), 1e-6)
     # y is the dequantized weight row q * s + o, rounded once to bf16
     assert oracle.rel_err_floor(y.reshape(m, n), oy) <= 2.0 ** -8
+
+
+FAST = [  # m, k, n, granularity, group, offset, bias, act: the large-m GFX950_B tile
+    (300, 384, 200, "group", 128, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (257, 1024, 136, "channel", 0, (-0.5, 0.5), None, torch.bfloat16),
+    (65, 256, 48, "tensor", 0, "none", 0.1, torch.float16),
+    (512, 1024, 256, "group", 256, (-0.5, 0.5), 0.1, torch.float16),
+    (33, 128, 18, "channel2d", 0, None, 0.1, torch.bfloat16),
+    (520, 2048, 300, "group", 128, "none", None, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", FAST, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in FAST])
+def test_fast_tile_shapes(shape):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"fast{m}x{k}x{n}", m, k, n, act=act, w_bits=4, granularity=gran,
+                          group_size=g, scale_range=(0.002, 0.02), offset_range=off,
+                          bias_std=bias, seed=3 * m + k + n)
+    note(f"wq fast tile {c.name} {gran} g={g} {act}")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
+    y2, n2 = wq_on_gpu(c, inplace=True)
+    assert torch.equal(y, y2) and torch.equal(nrm, n2)
