@@ -8,8 +8,9 @@
 // 1024 + u = q + 1032, bits 0x6400 | u), a 128-deep K slab needs no per-element
 // dequantization at all:
 //   sum_k x[r,k] (q s + o) = s * sum_k x B  +  (o - 136 s) * sum_k x
-// so for every group g the float32 accumulator takes  acc += s_g * part_g
-// (part_g = MFMA sum of x * B over the group), and the rank-1 remainder
+// so the MFMAs sum x * B straight into the float32 accumulator, kept in units
+// of the current group's scale (rescaled by s_prev / s_g at each group
+// start: one multiply per element per group), and the rank-1 remainder
 // sum_g rowsum_g(x) (o_g - 136 s_g) is added once at the end with MFMAs on
 // bf16 hi/lo splits of both factors (three products; relative error ~2^-16
 // of a term that is a small multiple of the result). The row sums come from
@@ -40,17 +41,25 @@ struct Magic<ACT_F16> {
   static constexpr float bias = 1032.f;
 };
 
+// (p & mask) | bits in one VALU op (the compiler emits and + or).
+__device__ __forceinline__ uint32_t and_or(uint32_t p, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(p), "v"(mask), "v"(bits));
+  return r;
+}
+
 // Eight int4 codes (one dword, K ascending from the low nibble) -> eight
 // 16-bit values (q + bias), dword j = codes (2j, 2j+1) in (low, high) half.
-template <int ACT>
-__device__ __forceinline__ u32x4 unpack8(uint32_t w) {
+// With mask = 0x000F000F and bits = the magic exponent pattern; mask = bits =
+// 0 gives zeros (a column whose group scale is zero).
+__device__ __forceinline__ u32x4 unpack8(uint32_t w, uint32_t mask, uint32_t bits) {
   const uint32_t u = w ^ 0x88888888u;        // two's complement -> offset binary
   const uint32_t u4 = u >> 4;
   u32x4 r;
-  r.x = (__builtin_amdgcn_perm(u4, u, 0x0C040C00u) & 0x000F000Fu) | Magic<ACT>::bits;
-  r.y = (__builtin_amdgcn_perm(u4, u, 0x0C050C01u) & 0x000F000Fu) | Magic<ACT>::bits;
-  r.z = (__builtin_amdgcn_perm(u4, u, 0x0C060C02u) & 0x000F000Fu) | Magic<ACT>::bits;
-  r.w = (__builtin_amdgcn_perm(u4, u, 0x0C070C03u) & 0x000F000Fu) | Magic<ACT>::bits;
+  r.x = and_or(__builtin_amdgcn_perm(u4, u, 0x0C040C00u), mask, bits);
+  r.y = and_or(__builtin_amdgcn_perm(u4, u, 0x0C050C01u), mask, bits);
+  r.z = and_or(__builtin_amdgcn_perm(u4, u, 0x0C060C02u), mask, bits);
+  r.w = and_or(__builtin_amdgcn_perm(u4, u, 0x0C070C03u), mask, bits);
   return r;
 }
 
@@ -124,33 +133,50 @@ typedef __attribute__((address_space(1))) void glb_void;
 // lane, 1 KiB (4 rows) per wave instruction. LDS rows are 256 bytes; the
 // 16-byte chunk j of row r sits at position j ^ (r & 15), so the A-fragment
 // reads of 16 lanes (16 rows, one K chunk) hit 16 distinct bank groups.
-// Rows past m load row m-1 (their results are never stored); k is a
-// multiple of 128, so there is no K tail.
-__device__ __forceinline__ void pf_dma_a(const uint16_t* x1, int64_t m, int64_t k, int64_t m0,
-                                         int64_t k0, uint8_t* buf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Wave w, instruction j covers tile rows 4*(16w + j) + (lane / 16); its
+// element offset from the tile's first row is off[j & 3] + (j & ~3) * 4k,
+// with off[] the per-lane offsets of instructions 0..3 (the chunk swizzle
+// depends on the row only through j & 3). Rows past m are
+// clamped to m - 1 in a separate (uniform) path: their results are never
+// stored. k is a multiple of 128, so there is no K tail.
+struct ADma {
+  uint32_t off[4];      // lane offset (elements) of instructions j = 0..3 (mod 4)
+};
+
+__device__ __forceinline__ void pf_dma_a(const uint16_t* xblk, const ADma& d, uint32_t k4,
+                                         uint32_t k0, uint8_t* buf) {
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int base = (wave * 16 + j) * 4;           // first of this instruction's 4 rows
-    const int row = base + (lane >> 4);
-    const int cj = (lane & 15) ^ (row & 15);
-    int64_t gr = m0 + row;
-    gr = gr < m ? gr : m - 1;
-    const uint16_t* src = x1 + gr * k + k0 + 8 * cj;
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(buf + base * PF_LROW), 16, 0, 0);
+    const uint16_t* src = xblk + (d.off[j & 3] + (uint32_t)(j & ~3) * k4 + k0);
+    __builtin_amdgcn_global_load_lds((glb_void*)src,
+                                     (lds_void*)(buf + (wave * 16 + j) * 4 * PF_LROW), 16, 0, 0);
   }
 }
 
-// Packed weight of one slab for the wave's 64 columns: column index clamped
-// to the padded width (columns past n are computed but never stored).
-__device__ __forceinline__ void pf_load_b(const uint8_t* x2, int64_t np, int64_t ncol0,
-                                          int64_t slab, uint32_t (&b)[4][4]) {
-  const int lane = threadIdx.x & 63;
+// Ragged last row block: rows past m read row m - 1.
+__device__ __forceinline__ void pf_dma_a_clamped(const uint16_t* xblk, int rows_left, uint32_t k,
+                                                 uint32_t k0, uint8_t* buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int row = (wave * 16 + j) * 4 + (lane >> 4);
+    const int cj = (lane & 15) ^ (row & 15);
+    const int r = row < rows_left ? row : rows_left - 1;
+    const uint16_t* src = xblk + ((uint32_t)r * k + k0 + 8 * cj);
+    __builtin_amdgcn_global_load_lds((glb_void*)src,
+                                     (lds_void*)(buf + (wave * 16 + j) * 4 * PF_LROW), 16, 0, 0);
+  }
+}
+
+// Packed weight of one slab for the wave's 64 columns: xs points at the
+// slab's first column block of this wave; boff[f] is the lane's byte offset
+// (column clamped to the padded width; columns past n are never stored).
+__device__ __forceinline__ void pf_load_b(const uint8_t* xs, const int32_t (&boff)[4],
+                                          uint32_t (&b)[4][4]) {
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    int64_t col = ncol0 + 16 * f + (lane & 15);
-    col = col < np ? col : np - 1;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x2 + (slab * np + col) * 64 + (lane >> 4) * 16);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xs + boff[f]);
     b[f][0] = v.x;
     b[f][1] = v.y;
     b[f][2] = v.z;
@@ -158,24 +184,25 @@ __device__ __forceinline__ void pf_load_b(const uint8_t* x2, int64_t np, int64_t
   }
 }
 
-// One 128-deep slab: part[i][f] = sum over the slab of x1 * (q + bias).
+// One 128-deep slab accumulated into acc: acc[i][f] += sum over the slab of
+// x1 * (q + bias), the MFMAs accumulating in place.
 template <int ACT>
 __device__ __forceinline__ void pf_slab(const uint8_t* buf, int wr, const uint32_t (&b)[4][4],
-                                        f32x4 (&part)[8][4]) {
+                                        const uint32_t (&mk)[4], const uint32_t (&mg)[4],
+                                        f32x4 (&acc)[8][4]) {
   const int lane = threadIdx.x & 63;
   const uint8_t* arow = buf + (wr * 128 + (lane & 15)) * PF_LROW;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     u32x4 bf[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bf[f] = unpack8<ACT>(b[f][c]);
+    for (int f = 0; f < 4; ++f) bf[f] = unpack8(b[f][c], mk[f], mg[f]);
     const int pos = ((4 * (lane >> 4) + c) ^ (lane & 15)) * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 av = *reinterpret_cast<const u32x4*>(arow + i * 16 * PF_LROW + pos);
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        part[i][f] = mfma16<ACT>(av, bf[f], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : part[i][f]);
+      for (int f = 0; f < 4; ++f) acc[i][f] = mfma16<ACT>(av, bf[f], acc[i][f]);
     }
   }
 }
@@ -202,7 +229,8 @@ __global__ __launch_bounds__(256, 1) void gemm_b_prefill(FastArgs a, int64_t til
   const int64_t m0 = tm * PF_BM;
   const int64_t n0 = tn * PF_BN;
   const int64_t ncol0 = n0 + wc * 64;
-  const int64_t slabs = a.k / PF_KS;
+  const int slabs = (int)(a.k / PF_KS);
+  const uint32_t k = (uint32_t)a.k;
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -210,46 +238,104 @@ __global__ __launch_bounds__(256, 1) void gemm_b_prefill(FastArgs a, int64_t til
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[i][f] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  uint32_t bcur[4][4], bnext[4][4];
-  pf_dma_a(a.x1, a.m, a.k, m0, 0, smem);
-  pf_load_b(a.x2, a.np, ncol0, 0, bcur);
-  // scale index of the wave's 4 columns (clamped; weights of columns past n
-  // are zeroed at the fold)
-  int64_t scol[4];
+  // x1 DMA offsets
+  const uint16_t* xblk = a.x1 + m0 * a.k;
+  const int rows_left = (int)(a.m - m0 < PF_BM ? a.m - m0 : PF_BM);
+  const bool full_rows = rows_left == PF_BM;
+  ADma dma;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 16 + j) * 4 + (lane >> 4);
+    const int cj = (lane & 15) ^ (row & 15);
+    dma.off[j] = (uint32_t)row * k + 8 * cj;
+  }
+  auto dma_a = [&](int slab, uint8_t* buf) {
+    if (full_rows) pf_dma_a(xblk, dma, 4 * k, (uint32_t)slab * PF_KS, buf);
+    else pf_dma_a_clamped(xblk, rows_left, k, (uint32_t)slab * PF_KS, buf);
+  };
+  // packed weight offsets (bytes from the wave's column block of a slab)
+  const uint8_t* xw = a.x2 + ncol0 * 64;
+  const int64_t slab_bytes = a.np * 64;
+  int32_t boff[4];                                     // may be negative: the
+#pragma unroll                                        // clamped column can lie
+  for (int f = 0; f < 4; ++f) {                        // before ncol0
+    int64_t col = ncol0 + 16 * f + (lane & 15);
+    col = col < a.np ? col : a.np - 1;
+    boff[f] = (int32_t)((col - ncol0) * 64 + (lane >> 4) * 16);
+  }
+  // scale offsets of the wave's 4 columns (clamped; columns past n get scale 0)
+  uint32_t soff[4];
   float cmask[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int64_t col = ncol0 + 16 * f + (lane & 15);
-    scol[f] = (col < a.n ? col : a.n - 1) * a.s_col;
+    soff[f] = (uint32_t)((col < a.n ? col : a.n - 1) * a.s_col);
     cmask[f] = col < a.n ? 1.f : 0.f;
   }
+  const int spg = (int)(a.group / PF_KS);              // slabs per group (>= 1)
+
+  uint32_t bcur[4][4], bnext[4][4];
+  dma_a(0, smem);
+  pf_load_b(xw, boff, bcur);
+  float svn[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) svn[f] = to_f32<ACT>(a.scale[soff[f]]) * cmask[f];
   __syncthreads();
 
-  for (int64_t s = 0; s < slabs; ++s) {
+  // acc holds the running sum in units of the current group's scale cs:
+  // true sum = cs * acc. At a group with scale s: acc *= cs / s, then the
+  // MFMAs add that group's x1 * (q + bias) to acc, and cs = s. A zero scale
+  // zeroes the column's weight operand and leaves acc and cs unchanged.
+  float cs[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t mk[4], mg[4];
+  int gpos = 0;                                        // slab index within its group
+  const uint16_t* srow_next = a.scale + a.s_row;       // scale row of the next group
+  for (int s = 0; s < slabs; ++s) {
     const uint8_t* cur = smem + (s & 1) * PF_LBUF;
     const bool more = s + 1 < slabs;
     if (more) {
-      pf_dma_a(a.x1, a.m, a.k, m0, (s + 1) * PF_KS, smem + ((s + 1) & 1) * PF_LBUF);
-      pf_load_b(a.x2, a.np, ncol0, s + 1, bnext);
+      dma_a(s + 1, smem + ((s + 1) & 1) * PF_LBUF);
+      pf_load_b(xw + (s + 1) * slab_bytes, boff, bnext);
     }
-    const int64_t srow = ((s * PF_KS) / a.group) * a.s_row;
-    float sv[4];
+    if (gpos == 0) {                                   // group start
+      float ratio[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sv[f] = to_f32<ACT>(a.scale[srow + scol[f]]) * cmask[f];
-    f32x4 part[8][4];
-    pf_slab<ACT>(cur, wr, bcur, part);
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < 4; ++f) {
+        const float sg = svn[f];
+        const bool z = sg == 0.f;
+        ratio[f] = (z || cs[f] == 0.f) ? 1.f : cs[f] / sg;
+        cs[f] = z ? cs[f] : sg;
+        mk[f] = z ? 0u : 0x000F000Fu;
+        mg[f] = z ? 0u : Magic<ACT>::bits;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][f][r] = fmaf(sv[f], part[i][f][r], acc[i][f][r]);
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
+    }
+    if (++gpos == spg) {                               // next slab starts a group
+      gpos = 0;
+      if (more) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) svn[f] = to_f32<ACT>(srow_next[soff[f]]) * cmask[f];
+        srow_next += a.s_row;
+      }
+    }
+    pf_slab<ACT>(cur, wr, bcur, mk, mg, acc);
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int c = 0; c < 4; ++c) bcur[f][c] = bnext[f][c];
     __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][f][r] *= cs[f];
 
   // ---- rank-1 remainder: acc += rowsum_g(x) * (o_g - bias * s_g) over groups,
   //      as MFMAs over the group axis on bf16 hi/lo splits ----
