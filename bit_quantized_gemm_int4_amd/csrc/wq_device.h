@@ -69,6 +69,12 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  return v;
+}
+
 __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));

@@ -289,9 +289,9 @@ size_t partial_bytes(int64_t m, int64_t n) {
 }  // namespace
 
 // Workspace: per-(32-column tile, row) partial sums of y^2, then (fast path)
-// per-group row sums of x1 as bf16 hi/lo.
+// per-group row sums of x1 and per-group column corrections as bf16 hi/lo.
 size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
-  return partial_bytes(m, n) + fast_rowsum_bytes(m, k) + 256;
+  return partial_bytes(m, n) + fast_rowsum_bytes(m, k) + fast_corr_bytes(n, k) + 256;
 }
 
 hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
@@ -313,9 +313,11 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
   a.s_col = p.s_col;
   hipError_t e;
   if (fast_path_ok(p) && p.m > 32) {
-    uint16_t* rs = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.workspace) +
-                                               partial_bytes(p.m, p.n));
-    e = launch_prefill(p, a.partial, rs, s);
+    uint8_t* ws = static_cast<uint8_t*>(p.workspace);
+    uint16_t* rs = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n));
+    uint16_t* corr = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n) +
+                                                 fast_rowsum_bytes(p.m, p.k));
+    e = launch_prefill(p, a.partial, rs, corr, s);
   } else {
     e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
   }

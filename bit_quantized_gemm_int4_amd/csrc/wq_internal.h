@@ -52,7 +52,9 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s);
 // Fast GFX950_B INT4 path (group a multiple of 128, or per channel/tensor).
 bool fast_path_ok(const WqProblem& p);
 size_t fast_rowsum_bytes(int64_t m, int64_t k);
-hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, hipStream_t s);
+size_t fast_corr_bytes(int64_t n, int64_t k);
+hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint16_t* corr,
+                          hipStream_t s);
 
 struct MxProblem {
   const uint8_t* x1;     // (k, m) e4m3
