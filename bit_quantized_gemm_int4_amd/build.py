@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
-           "mx_gemm.hip"]
+           "wq_gemm_decode.hip", "mx_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,8 +32,15 @@ FLAGS = [
 
 
 # Per-file flags: the MFMA-bound tile rescales its accumulators with VALU
-# multiplies, so its MFMAs keep accumulators in ordinary VGPRs (no AGPR copies).
+# multiplies, so its MFMAs keep accumulators in ordinary VGPRs (no AGPR
+# copies). Its accumulators are long-lived and updated in place; the decode
+# kernel, whose per-block partial sums are short-lived, keeps them in AGPRs.
 FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+# Sources with MFMA kernels: their device assembly is checked for MFMA
+# destinations that partially overlap a source operand (codegen_check).
+MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "mx_gemm.hip"]
 
 
 def _compile(src: str) -> str:
@@ -46,10 +53,33 @@ def _compile(src: str) -> str:
     return obj
 
 
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one source, compiled with the library's flags."""
+    out = os.path.join(BUILD_DIR, os.path.basename(src) + ".s")
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    with open(out) as f:
+        return f.read()
+
+
+def _check_mfma(src: str) -> list:
+    from .codegen_check import partial_overlaps
+    return partial_overlaps(device_asm(src))
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs_f = ex.map(_compile, SOURCES)
+        checks = list(ex.map(_check_mfma, MFMA_SOURCES))
+        objs = list(objs_f)
+    bad = [b for c in checks for b in c]
+    if bad:
+        raise RuntimeError("MFMA destination partially overlaps a source operand (wrong results "
+                           "on gfx950):\n" + "\n".join(bad))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,5 +92,8 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
+    if __package__ in (None, ""):
+        sys.path.insert(0, ROOT)
+        __package__ = "bit_quantized_gemm_int4_amd"
     build(verbose=True)
     sys.exit(0)

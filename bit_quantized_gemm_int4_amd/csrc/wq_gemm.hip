@@ -5,11 +5,15 @@
 //
 // Two launches on the caller's stream:
 //   1. a GEMM kernel whose epilogue adds bias and residual, stores y and
-//      writes per-(32-column tile, row) partial sums of y^2 (float32 y) to
-//      the workspace;
+//      writes per-(column tile, row) partial sums of y^2 (float32 y) to
+//      the workspace (32-column tiles; 16 for the decode kernel);
 //   2. rmsnorm_finish: sums a row's partials in a fixed order, forms
 //      1/RMS and writes normOut = y * rstd * gamma.
 // GEMM kernels:
+//   - gemm_decode (wq_gemm_decode.hip): m <= 32, INT4 GFX950_B, group a
+//     multiple of 128 (or per channel / tensor): a weight stream;
+//   - gemm_b_wide (wq_gemm_fast.hip): the same weights at larger m, the
+//     MFMA-bound tile;
 //   - gemm_generic: any weight layout (INT4 ND / GFX950_B, INT8 ND /
 //     transposed), any group size, 64x64x32 tiles with both operands staged
 //     in LDS; integer codes go to the MFMA and each group's scale and
@@ -209,19 +213,21 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // RMSNorm finish: grid (m rows, column chunks). Every workgroup of a row sums
-// the same partials in the same order, so all of them agree on rstd.
+// the same partials in the same order, so all of them agree on rstd. Partial
+// (tile i, row r) sits at i * ts + r * rstride.
 // ---------------------------------------------------------------------------
 template <int ACT>
 __global__ __launch_bounds__(256) void rmsnorm_finish(const uint16_t* __restrict__ y,
                                                       const float* __restrict__ partial,
-                                                      int64_t tiles, const uint16_t* __restrict__ gamma,
+                                                      int64_t tiles, int64_t ts, int64_t rstride,
+                                                      const uint16_t* __restrict__ gamma,
                                                       uint16_t* __restrict__ out, int64_t m, int64_t n,
                                                       float eps, int64_t chunk) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   float s = 0.f;
-  for (int64_t i = t; i < tiles; i += 256) s += partial[i * m + row];
+  for (int64_t i = t; i < tiles; i += 256) s += partial[i * ts + row * rstride];
   s = wave_sum(s);
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
@@ -267,13 +273,14 @@ hipError_t launch_generic(const WqProblem& p, const GemmArgs& a, hipStream_t s) 
 }
 
 template <int ACT>
-hipError_t launch_finish(const WqProblem& p, const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles = (p.n + 31) / 32;
+hipError_t launch_finish(const WqProblem& p, const GemmArgs& a, int64_t tiles, int64_t ts,
+                         int64_t rstride, hipStream_t s) {
   int64_t chunk = 2048;
   if (p.m < 256) chunk = 512;
   if (chunk > p.n) chunk = p.n;
   dim3 grid((unsigned)p.m, (unsigned)((p.n + chunk - 1) / chunk));
-  rmsnorm_finish<ACT><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(p.y), a.partial, tiles,
+  rmsnorm_finish<ACT><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(p.y), a.partial, tiles, ts,
+                                           rstride,
                                            static_cast<const uint16_t*>(p.gamma),
                                            static_cast<uint16_t*>(p.norm_out), p.m, p.n, p.eps, chunk);
   return hipGetLastError();
@@ -282,8 +289,10 @@ hipError_t launch_finish(const WqProblem& p, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 namespace {
+// room for one partial per (16-column tile, row): the finest granularity any
+// GEMM kernel writes
 size_t partial_bytes(int64_t m, int64_t n) {
-  const int64_t tiles = (n + 31) / 32;
+  const int64_t tiles = (n + 15) / 16;
   return ((size_t)(tiles * m) * sizeof(float) + 255) & ~(size_t)255;
 }
 }  // namespace
@@ -312,7 +321,13 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
   a.s_row = p.s_row;
   a.s_col = p.s_col;
   hipError_t e;
-  if (fast_path_ok(p) && p.m > 32) {
+  int64_t tiles = (p.n + 31) / 32, ts = p.m, rstride = 1;   // [tile][row]
+  if (fast_path_ok(p) && p.m <= 32) {
+    tiles = decode_tiles(p.n);                                 // [row][tile]
+    ts = 1;
+    rstride = tiles;
+    e = launch_decode(p, a.partial, s);
+  } else if (fast_path_ok(p)) {
     uint8_t* ws = static_cast<uint8_t*>(p.workspace);
     uint16_t* rs = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n));
     uint16_t* corr = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n) +
@@ -322,7 +337,8 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
     e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
   }
   if (e != hipSuccess) return e;
-  return p.bf16 ? launch_finish<ACT_BF16>(p, a, s) : launch_finish<ACT_F16>(p, a, s);
+  return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, ts, rstride, s)
+                : launch_finish<ACT_F16>(p, a, tiles, ts, rstride, s);
 }
 
 }  // namespace wq

@@ -29,44 +29,10 @@
 // y stores are 16-byte, row-contiguous accesses.
 #include "wq_device.h"
 #include "wq_internal.h"
+#include "wq_unpack.h"
 
 namespace wq {
 namespace {
-
-template <int ACT>
-struct Magic;
-template <>
-struct Magic<ACT_BF16> {
-  static constexpr uint32_t bits = 0x43004300u;
-  static constexpr float bias = 136.f;
-};
-template <>
-struct Magic<ACT_F16> {
-  static constexpr uint32_t bits = 0x64006400u;
-  static constexpr float bias = 1032.f;
-};
-
-// (p & mask) | bits in one VALU op (the compiler emits and + or).
-__device__ __forceinline__ uint32_t and_or(uint32_t p, uint32_t mask, uint32_t bits) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(p), "v"(mask), "v"(bits));
-  return r;
-}
-
-// Eight int4 codes (one dword, K ascending from the low nibble) -> eight
-// 16-bit values (q + bias), dword j = codes (2j, 2j+1) in (low, high) half.
-// With mask = 0x000F000F and bits = the magic exponent pattern; mask = bits =
-// 0 gives zeros (a column whose group scale is zero).
-__device__ __forceinline__ u32x4 unpack8(uint32_t w, uint32_t mask, uint32_t bits) {
-  const uint32_t u = w ^ 0x88888888u;        // two's complement -> offset binary
-  const uint32_t u4 = u >> 4;
-  u32x4 r;
-  r.x = and_or(__builtin_amdgcn_perm(u4, u, 0x0C040C00u), mask, bits);
-  r.y = and_or(__builtin_amdgcn_perm(u4, u, 0x0C050C01u), mask, bits);
-  r.z = and_or(__builtin_amdgcn_perm(u4, u, 0x0C060C02u), mask, bits);
-  r.w = and_or(__builtin_amdgcn_perm(u4, u, 0x0C070C03u), mask, bits);
-  return r;
-}
 
 // bf16 hi/lo split of a float: v ~= hi + lo with |v - hi - lo| <= 2^-16 |v|.
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {

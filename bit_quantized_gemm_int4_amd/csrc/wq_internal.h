@@ -56,6 +56,11 @@ size_t fast_corr_bytes(int64_t n, int64_t k);
 hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint16_t* corr,
                           hipStream_t s);
 
+// Weight-streaming kernel for m <= 32 on the same fast-path problems; writes
+// sums of y^2 per (row, 16-column tile), row-major: decode_tiles(n) per row.
+int64_t decode_tiles(int64_t n);
+hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s);
+
 struct MxProblem {
   const uint8_t* x1;     // (k, m) e4m3
   const uint8_t* x2;     // GFX950_B e2m1

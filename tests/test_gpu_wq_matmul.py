@@ -171,3 +171,42 @@ def test_fast_tile_shapes(shape):
     check_wq(c, y, nrm)
     y2, n2 = wq_on_gpu(c, inplace=True)
     assert torch.equal(y, y2) and torch.equal(nrm, n2)
+
+
+DECODE = [  # m, k, n, granularity, group, offset, bias, act: the m <= 32 weight stream
+    (1, 128, 16, "tensor", 0, "none", None, torch.bfloat16),
+    (2, 384, 48, "group", 128, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (7, 1024, 130, "channel", 0, (-0.5, 0.5), 0.1, torch.float16),
+    (9, 256, 777, "group", 128, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (16, 4096, 4100, "group", 128, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (17, 2048, 8210, "group", 256, None, None, torch.bfloat16),
+    (31, 640, 13000, "group", 128, "none", 0.1, torch.bfloat16),
+    (32, 8192, 1000, "channel2d", 0, (-0.5, 0.5), 0.1, torch.float16),
+    (5, 1152, 2000, "group", 384, (-1.0, 1.0), None, torch.float16),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in DECODE])
+def test_decode_kernel_shapes(shape):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"dec{m}x{k}x{n}", m, k, n, act=act, w_bits=4, granularity=gran,
+                          group_size=g, scale_range=(0.002, 0.02), offset_range=off,
+                          bias_std=bias, seed=7 * m + k + n)
+    note(f"wq decode kernel {c.name} {gran} g={g} {act}")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
+    y2, n2 = wq_on_gpu(c, inplace=True)
+    assert torch.equal(y, y2) and torch.equal(nrm, n2)
+
+
+def test_decode_zero_scale_columns():
+    # a zero group scale leaves only the offset: w = o for that group
+    m, k, n, G = 4, 512, 64, 128
+    c = workloads.wq_case("dec_zero_scale", m, k, n, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=G, scale_range=(0.002, 0.02),
+                          offset_range=(-1.0, 1.0), bias_std=0.1, seed=11)
+    c.scale[1, :] = 0
+    c.scale[:, 5] = 0
+    note("wq decode zero-scale groups and columns")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
