@@ -34,6 +34,42 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (the E4M3 x E2M1 MX rate)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+COPY_BYTES = 256 << 20         # calibration copy (--only copy)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
+
+
+def source_hash() -> str:
+    """Hash of the sources of the prefill call's kernels: traffic counters
+    taken on other sources do not describe this build."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_gemm_int4_amd", "csrc")
+    for f in ("wq_gemm_fast.hip", "wq_gemm.hip", "wq_unpack.h", "wq_device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill call from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel's reading),
+    or None when the summary is missing or was taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for ln in text.splitlines():
+        if ln.startswith("- ") and ": " in ln:
+            key, _, val = ln[2:].partition(": ")
+            vals[key.strip()] = val.strip().strip("`")
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -127,6 +163,12 @@ def main():
          x1q.numel() + x2mx.numel() + s1.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
     ]
     rows = [r for r in rows if want(r[0])]
+    if "copy" in only:
+        # Not part of the step: a plain device copy of known size, whose
+        # FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures.
+        cp_src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        cp_dst = torch.empty_like(cp_src)
+        rows.append(("copy", lambda: cp_dst.copy_(cp_src), 0, 2 * COPY_BYTES, "hbm"))
 
     def step(record):
         for name, fn, _, _, _ in rows:
@@ -263,7 +305,7 @@ def main():
     if head:
         line["roofline"] = {"bound": "mfma", "achieved": head["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(head["TFLOP/s"] / PEAK_BF16_TFLOPS, 4),
-                            "traffic": None,
+                            "traffic": measured_traffic(),
                             "kernel": "wq_matmul_add_rmsnorm (all launches of one call)"}
     print(json.dumps(line), flush=True)
 

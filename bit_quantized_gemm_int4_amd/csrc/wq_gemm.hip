@@ -5,8 +5,9 @@
 //
 // Two launches on the caller's stream:
 //   1. a GEMM kernel whose epilogue adds bias and residual, stores y and
-//      writes per-(column tile, row) partial sums of y^2 (float32 y) to
-//      the workspace (32-column tiles; 16 for the decode kernel);
+//      writes per-(row, column tile) partial sums of y^2 (float32 y),
+//      row-major, to the workspace (32-column tiles; 16 for the decode
+//      kernel);
 //   2. rmsnorm_finish: sums a row's partials in a fixed order, forms
 //      1/RMS and writes normOut = y * rstd * gamma.
 // GEMM kernels:
@@ -34,7 +35,7 @@ struct GemmArgs {
   const uint16_t* bias;
   const uint16_t* residual;
   uint16_t* y;
-  float* partial;        // [ceil(n/32)][m]
+  float* partial;        // [m][ceil(n/32)]
   int64_t m, k, n, np;   // np: padded N of the GFX950_B layout
   int64_t group, s_row, s_col;
 };
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + wr * 32 + i * 16 + 4 * (lane >> 4) + r;
-        if (row < a.m) a.partial[tile32 * a.m + row] = ss[i][r];
+        if (row < a.m) a.partial[row * ((a.n + 31) / 32) + tile32] = ss[i][r];
       }
   }
 }
@@ -226,6 +227,19 @@ __global__ __launch_bounds__(256) void rmsnorm_finish(const uint16_t* __restrict
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
+  const int64_t c_begin = (int64_t)blockIdx.y * chunk;
+  const int64_t c_end = c_begin + chunk < n ? c_begin + chunk : n;
+  const uint16_t* yr = y + row * n;
+  uint16_t* orow = out + row * n;
+  const bool vec = (n & 7) == 0 && chunk <= 256 * 8;
+  // y and gamma do not depend on the row's sum: fetch them first (vector
+  // case: one 8-column group per thread), then reduce the partials.
+  u32x4 yv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+  const int64_t cv = c_begin + t * 8;
+  if (vec && cv < c_end) {
+    yv = *reinterpret_cast<const u32x4*>(yr + cv);
+    gv = *reinterpret_cast<const u32x4*>(gamma + cv);
+  }
   float s = 0.f;
   for (int64_t i = t; i < tiles; i += 256) s += partial[i * ts + row * rstride];
   s = wave_sum(s);
@@ -233,14 +247,8 @@ __global__ __launch_bounds__(256) void rmsnorm_finish(const uint16_t* __restrict
   __syncthreads();
   s = (red[0] + red[1]) + (red[2] + red[3]);
   const float rstd = 1.0f / sqrtf(s / (float)n + eps);
-  const int64_t c_begin = (int64_t)blockIdx.y * chunk;
-  const int64_t c_end = c_begin + chunk < n ? c_begin + chunk : n;
-  const uint16_t* yr = y + row * n;
-  uint16_t* orow = out + row * n;
-  if ((n & 7) == 0) {
-    for (int64_t c = c_begin + t * 8; c < c_end; c += 256 * 8) {
-      const u32x4 yv = *reinterpret_cast<const u32x4*>(yr + c);
-      const u32x4 gv = *reinterpret_cast<const u32x4*>(gamma + c);
+  if (vec) {
+    if (cv < c_end) {
       uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w}, ow[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(256) void rmsnorm_finish(const uint16_t* __restrict
       o.y = ow[1];
       o.z = ow[2];
       o.w = ow[3];
-      *reinterpret_cast<u32x4*>(orow + c) = o;
+      *reinterpret_cast<u32x4*>(orow + cv) = o;
     }
   } else {
     for (int64_t c = c_begin + t; c < c_end; c += 256)
@@ -275,8 +283,10 @@ hipError_t launch_generic(const WqProblem& p, const GemmArgs& a, hipStream_t s) 
 template <int ACT>
 hipError_t launch_finish(const WqProblem& p, const GemmArgs& a, int64_t tiles, int64_t ts,
                          int64_t rstride, hipStream_t s) {
+  // one 8-column group per thread (256 x 8 = 2048 columns per workgroup);
+  // narrower chunks for few rows so that the grid still spreads over the CUs
   int64_t chunk = 2048;
-  if (p.m < 256) chunk = 512;
+  if (p.m < 64) chunk = 512;
   if (chunk > p.n) chunk = p.n;
   dim3 grid((unsigned)p.m, (unsigned)((p.n + chunk - 1) / chunk));
   rmsnorm_finish<ACT><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(p.y), a.partial, tiles, ts,
@@ -321,11 +331,10 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
   a.s_row = p.s_row;
   a.s_col = p.s_col;
   hipError_t e;
-  int64_t tiles = (p.n + 31) / 32, ts = p.m, rstride = 1;   // [tile][row]
+  // partials are row-major: [row][tile], 32-column tiles (16 for decode)
+  int64_t tiles = (p.n + 31) / 32;
   if (fast_path_ok(p) && p.m <= 32) {
-    tiles = decode_tiles(p.n);                                 // [row][tile]
-    ts = 1;
-    rstride = tiles;
+    tiles = decode_tiles(p.n);
     e = launch_decode(p, a.partial, s);
   } else if (fast_path_ok(p)) {
     uint8_t* ws = static_cast<uint8_t*>(p.workspace);
@@ -337,8 +346,8 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
     e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
   }
   if (e != hipSuccess) return e;
-  return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, ts, rstride, s)
-                : launch_finish<ACT_F16>(p, a, tiles, ts, rstride, s);
+  return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, 1, tiles, s)
+                : launch_finish<ACT_F16>(p, a, tiles, 1, tiles, s);
 }
 
 }  // namespace wq

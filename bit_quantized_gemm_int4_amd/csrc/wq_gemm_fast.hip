@@ -50,7 +50,7 @@ struct FastArgs {
   const uint16_t* bias;
   const uint16_t* residual;
   uint16_t* y;
-  float* partial;          // [ceil(n/32)][m]
+  float* partial;          // [m][ceil(n/32)]
   const uint16_t* rs;      // [m][2][gp]  per-group row sums of x1, bf16 hi then lo
   const uint16_t* corr;    // [np][2][gp] per-group o - bias*s per column, hi then lo
   int64_t m, k, n, np;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_
       }
       ss = quad_sum(ss);                               // the 4 lanes of 32 columns
       const int64_t c32 = ncol0 + (lc & 32);
-      if ((lane & 3) == 0 && row < a.m && c32 < a.n) a.partial[(c32 / 32) * a.m + row] = ss;
+      if ((lane & 3) == 0 && row < a.m && c32 < a.n) a.partial[row * ((a.n + 31) / 32) + c32 / 32] = ss;
     }
     __syncthreads();
   }
