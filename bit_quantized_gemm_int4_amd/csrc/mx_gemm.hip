@@ -13,8 +13,23 @@
 // the A lane (E4M3) holds K 16*(l/16) .. +16 in bytes 0..15 and
 // K 64 + 16*(l/16) .. +16 in bytes 16..31.
 // Since GFX950_B stores each column's 32-deep block as 16 contiguous bytes,
-// a B fragment is one dwordx4 load straight from global memory. A arrives
-// K-major, so the workgroup transposes its A tile into LDS ([m][k] bytes).
+// a B fragment is one 16-byte load. A arrives K-major.
+//
+// Two kernels:
+//   - mx_gemm_tile: M, N multiples of 256 and K a multiple of 128. A
+//     256 x 256 workgroup tile, 8 waves of 64 (m) x 128 (n). Per 128-deep
+//     step the x1 tile (128 k-rows x 256 m bytes), the weight slab (256
+//     columns x 64 bytes) and both scale tiles move by direct global->LDS DMA,
+//     double-buffered. A operands come out of LDS with the gfx950 transpose
+//     read ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives
+//     byte c of the 8 bytes that in-group lane 2b + h fetched, as byte b,
+//     where i = 8h + c. Pointing in-group lane j at k-row k0 + j/2, m column
+//     m0 + 8 (j%2) therefore hands lane i the 8 consecutive K values of row
+//     m0 + i. The x1 rows' 16-byte chunks are XOR-swizzled by k so that the
+//     32 rows one such read touches spread over all LDS banks. The
+//     accumulators start as y, so the in-place add costs no extra pass.
+//   - mx_gemm_kernel: any shape (partial K blocks, ragged M and N); a small
+//     64 x 64 tile that transposes A byte-wise.
 #include "wq_device.h"
 #include "wq_internal.h"
 
@@ -91,10 +106,175 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict_
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Tiled kernel
+// ---------------------------------------------------------------------------
+constexpr int MF_BM = 256, MF_BN = 256, MF_BK = 128;
+constexpr int MF_ABYTES = MF_BK * MF_BM;   // 32 KiB: 128 k-rows x 256 m
+constexpr int MF_BBYTES = MF_BN * 64;      // 16 KiB: 256 columns x (128 K / 2)
+constexpr int MF_SBYTES = 1024;            // 256 x 4 scale bytes
+
+// physical 16-byte chunk of logical chunk c in k-row r: c ^ swz(r). The 32
+// rows of one transpose read, {off + 16 g + u : g < 4, u < 8} with off a
+// multiple of 8 below 128, hit each value of (r & 7) | ((r & 16) >> 1) twice.
+__device__ __forceinline__ int mf_swz(int r) { return (r & 7) | ((r & 16) >> 1); }
+
+struct MfBufs {
+  uint8_t* a;
+  uint8_t* b;
+  uint8_t* s1;
+  uint8_t* s2;
+};
+
+// DMA of one 128-deep step into the given buffers: 7 instructions per wave
+// (x1: 4 KiB in four 1 KiB pieces; weights: 2 KiB; one 256-byte scale row).
+__device__ __forceinline__ void mf_dma(const uint8_t* __restrict__ x1t, const uint8_t* __restrict__ x2,
+                                       const uint8_t* __restrict__ s1, const uint8_t* __restrict__ s2,
+                                       const MfBufs& bf, int64_t M, int64_t N, int64_t Np, int64_t KB,
+                                       int64_t m0, int64_t n0, int step, int wave, int lane) {
+  const int64_t k0 = (int64_t)step * MF_BK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * wave + i;                 // k-rows 4q .. 4q + 3
+    const int r = 4 * q + (lane >> 4);
+    const int c = (lane & 15) ^ mf_swz(r);      // logical chunk for this physical slot
+    __builtin_amdgcn_global_load_lds((glb_void*)(x1t + (k0 + r) * M + m0 + 16 * c),
+                                     (lds_void*)(bf.a + q * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = 2 * wave + i;
+    __builtin_amdgcn_global_load_lds((glb_void*)(x2 + ((int64_t)step * Np + n0) * 64 + q * 1024 + lane * 16),
+                                     (lds_void*)(bf.b + q * 1024), 16, 0, 0);
+  }
+  if (wave < 4) {   // scale1 rows m0 + 64 wave + lane, blocks 4 step .. 4 step + 3
+    __builtin_amdgcn_global_load_lds((glb_void*)(s1 + (m0 + 64 * wave + lane) * KB + 4 * step),
+                                     (lds_void*)(bf.s1 + wave * 256), 4, 0, 0);
+  } else {          // scale2 block row 4 step + (wave - 4), columns n0 .. n0 + 255
+    __builtin_amdgcn_global_load_lds((glb_void*)(s2 + (4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane),
+                                     (lds_void*)(bf.s2 + (wave - 4) * 256), 4, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict__ x1t,
+                                                       const uint8_t* __restrict__ x2,
+                                                       const uint8_t* __restrict__ s1,
+                                                       const uint8_t* __restrict__ s2,
+                                                       float* __restrict__ y, int64_t M, int64_t K,
+                                                       int64_t N, int64_t Np, int64_t tiles_m,
+                                                       int64_t tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[MF_ABYTES], a1[MF_ABYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[MF_BBYTES], b1[MF_BBYTES];
+  __shared__ __attribute__((aligned(256))) uint8_t s10[MF_SBYTES], s11[MF_SBYTES];
+  __shared__ __attribute__((aligned(256))) uint8_t s20[MF_SBYTES], s21[MF_SBYTES];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 3, wn = wave >> 2;      // 64-row and 128-column blocks of the tile
+
+  // tiles in XCD-major order: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous run of tiles so that the tiles sharing x1 rows share an L2
+  int64_t id = blockIdx.x;
+  const int64_t T = tiles_m * tiles_n;
+  if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
+  const int64_t m0 = (id / tiles_n) * MF_BM, n0 = (id % tiles_n) * MF_BN;
+  const int64_t KB = K / 32;
+  const int steps = (int)(K / MF_BK);
+  MfBufs buf0, buf1;
+  buf0.a = a0; buf0.b = b0; buf0.s1 = s10; buf0.s2 = s20;
+  buf1.a = a1; buf1.b = b1; buf1.s1 = s11; buf1.s2 = s21;
+
+  // accumulators start as y (the in-place add). y goes through a buffer
+  // resource: a per-lane offset, a uniform row offset and an immediate column
+  // offset, so no per-element address is kept across the K loop.
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)(M * N * 4), 0x00020000);
+  const uint32_t yl = (uint32_t)((4 * (lane >> 4)) * N + (lane & 15)) * 4u;
+  const uint32_t yw = (uint32_t)(((m0 + 64 * wm) * N + n0 + 128 * wn) * 4);
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ry, yl + 64u * j, so, 0));
+    }
+
+  mf_dma(x1t, x2, s1, s2, buf0, M, N, Np, KB, m0, n0, 0, wave, lane);
+  wait_vm<0>();
+  __syncthreads();
+
+  // per-lane LDS read offsets (independent of the step)
+  const int g = lane >> 4, jl = lane & 15;
+  // transpose read tt of A fragment i: k-row r(tt), logical chunk 4 wm + i;
+  // the four rows differ by multiples of 8 below 128, so they share
+  // (r & 7) | ((r & 16) >> 1) and one swizzle value serves all four reads
+  const int r0 = 16 * g + (jl >> 1);
+  const int swz = mf_swz(r0);
+  const int abase = r0 * 256 + 8 * (jl & 1);
+  const int boff = (128 * wn + jl) * 64 + g * 16;       // + 1024 j
+  const int s1off = (64 * wm + jl) * 4 + g;             // + 64 i
+  const int s2off = g * 256 + 128 * wn + jl;            // + 16 j
+
+  // One 128-deep step on buffer `cur` while the next step streams into
+  // `nxt`. The single barrier at the end both publishes every wave's DMA into
+  // `nxt` and frees `cur`, which the next step's DMA refills.
+  auto do_step = [&](int step, const MfBufs& cur, const MfBufs& nxt) {
+    if (step + 1 < steps) mf_dma(x1t, x2, s1, s2, nxt, M, N, Np, KB, m0, n0, step + 1, wave, lane);
+    u32x4 bv[8];
+    int sb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bv[j] = *reinterpret_cast<const u32x4*>(cur.b + boff + 1024 * j);
+      sb[j] = cur.s2[s2off + 16 * j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      typedef int v2i __attribute__((ext_vector_type(2)));
+      v2i p[4];
+      const int achunk = 16 * ((4 * wm + i) ^ swz);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        p[tt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(
+            cur.a + abase + achunk + ((tt & 1) * 8 + (tt >> 1) * 64) * 256));
+      const i32x8 af = {p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+      const int sa = cur.s1[s1off + 64 * i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af, (i32x8){(int)bv[j].x, (int)bv[j].y, (int)bv[j].z, (int)bv[j].w, 0, 0, 0, 0}, acc[i][j],
+            0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, sa, 0, sb[j]);
+    }
+    wait_vm<0>();            // this wave's DMA into `nxt` has landed
+    __syncthreads();
+  };
+  for (int step = 0; step < steps; step += 2) {
+    do_step(step, buf0, buf1);
+    if (step + 1 < steps) do_step(step + 1, buf1, buf0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, yl + 64u * j, so, 0);
+    }
+}
 }  // namespace
 
 hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s) {
   const int64_t Np = 16 * ((p.n + 15) / 16);
+  // the tiled kernel addresses y through a buffer resource (32-bit offsets)
+  if (p.m % MF_BM == 0 && p.n % MF_BN == 0 && p.k % MF_BK == 0 && p.m * p.n * 4 < (int64_t(1) << 31)) {
+    const int64_t tm = p.m / MF_BM, tn = p.n / MF_BN;
+    mx_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
+                                                         Np, tm, tn);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((p.n + MX_BN - 1) / MX_BN), (unsigned)((p.m + MX_BM - 1) / MX_BM));
   mx_gemm_kernel<<<grid, 256, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n, Np);
   return hipGetLastError();

@@ -103,6 +103,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// s_waitcnt that waits until at most N vector-memory operations are
+// outstanding (they complete in issue order) and leaves the other counters
+// alone. The compiler does not order LDS reads after an LDS DMA by itself.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 // ---- MFMA (16x16x32, 16-bit inputs, fp32 accumulate) --------------------
 // Operand layout for lane l: A row l%16, B column l%16, eight consecutive K
 // values starting at 8*(l/16); D column l%16, rows 4*(l/16)+i.

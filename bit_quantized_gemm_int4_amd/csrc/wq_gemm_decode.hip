@@ -77,16 +77,7 @@ struct DecodeAcc {
   f32x4 rs;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 
-// s_waitcnt that waits until at most N vector-memory operations are
-// outstanding (they complete in issue order) and leaves the other counters
-// alone. The compiler does not order LDS reads after an LDS DMA by itself.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Vector-memory loads decode_blocks issues after block j's four x1 DMAs.
 constexpr int loads_after_dma(int nb, int ctw, int j) {

@@ -40,8 +40,6 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = from_f32<ACT_BF16>(v - to_f32<ACT_BF16>(hi));
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 struct FastArgs {
   const uint16_t* x1;
