@@ -187,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   // accumulators start as y (the in-place add). y goes through a buffer
   // resource: a per-lane offset, a uniform row offset and an immediate column
   // offset, so no per-element address is kept across the K loop.
-  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y, (short)0, (int)(M * N * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ry = buf_rsrc(y, (uint32_t)(M * N * 4));
   const uint32_t yl = (uint32_t)((4 * (lane >> 4)) * N + (lane & 15)) * 4u;
   const uint32_t yw = (uint32_t)(((m0 + 64 * wm) * N + n0 + 128 * wn) * 4);
   f32x4 acc[4][8];

@@ -63,6 +63,9 @@ wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n, int transpos
   if (k < 0 || n < 0) return WQ_ERR_SHAPE;
   if (layout == WQ_LAYOUT_ND && (n % 2)) return WQ_ERR_SHAPE;
   if ((k + 127) / 128 > 65535 || (n + 63) / 64 > 2147483647LL) return WQ_ERR_SHAPE;
+  // GFX950_B kernels address one 128 x 256 tile with 32-bit byte offsets
+  if (layout == WQ_LAYOUT_GFX950_B && (transpose ? 256 * k : 128 * n) >= (int64_t(1) << 29))
+    return WQ_ERR_SHAPE;
   if (k == 0 || n == 0) return WQ_OK;
   if (!weight || !out) return WQ_ERR_NULLPTR;
   if (!aligned16(out)) return WQ_ERR_SHAPE;
@@ -84,6 +87,7 @@ wq_status wq_dynamic_quant(const void* x, wq_dtype x_dtype, int64_t rows, int64_
     // Constraints: INT4 needs an even last dim, INT32 one divisible by 8.
     if (y_dtype == WQ_INT4 && (cols % 2)) return WQ_ERR_SHAPE;
     if (y_dtype == WQ_INT32 && (cols % 8)) return WQ_ERR_SHAPE;
+    if (cols >= (int64_t(1) << 30)) return WQ_ERR_SHAPE;   // row byte offsets are 32-bit
     if (rows == 0 || cols == 0) return WQ_OK;
     if (!x || !y || !scale) return WQ_ERR_NULLPTR;
     if (!aligned16(x) || (smooth && !aligned16(smooth)) || !aligned16(y)) return WQ_ERR_SHAPE;

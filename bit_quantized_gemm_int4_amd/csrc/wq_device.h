@@ -115,6 +115,16 @@ __device__ __forceinline__ void wait_vm() {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
+// Buffer resources: loads take a per-lane VGPR byte offset plus a
+// wave-uniform SGPR offset, so no 64-bit address arithmetic runs per load.
+// An offset at or past the resource's byte count reads zero; BUF_OOB is such
+// an offset for every resource of at most 2 GiB.
+constexpr uint32_t BUF_OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // ---- MFMA (16x16x32, 16-bit inputs, fp32 accumulate) --------------------
 // Operand layout for lane l: A row l%16, B column l%16, eight consecutive K
 // values starting at 8*(l/16); D column l%16, rows 4*(l/16)+i.

@@ -21,8 +21,9 @@
 //   acc += s * sum_k x B  +  (o - 136 s) * sum_k x
 // with s, o the block's group scale and offset for the column.
 //
-// Epilogue: y = acc + bias + residual (rounded to the activation dtype) and
-// per-(16-column tile, row) sums of y^2 in float32 for the RMSNorm finish.
+// Epilogue: y = acc + bias + residual (stored rounded to the activation
+// dtype) and per-(row, 16-column tile) sums of the float32 y^2 for the
+// RMSNorm finish.
 #include "wq_device.h"
 #include "wq_internal.h"
 #include "wq_unpack.h"
@@ -31,7 +32,6 @@ namespace wq {
 namespace {
 
 constexpr int DC_WAVES = 16;
-constexpr uint32_t DC_OOB = 0x80000000u;   // buffer offset past every bound: reads 0
 
 struct DecodeArgs {
   const uint16_t* x1;
@@ -51,18 +51,11 @@ struct DecodeArgs {
   float omul;                // 1 with an offset, 0 without
 };
 
-// Buffer resources: loads take a per-lane VGPR offset plus a wave-uniform
-// SGPR offset (the K block), so no per-load address arithmetic runs on the
-// VALU; an offset at or beyond the resource's byte count reads zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
 template <int CTW>
 struct DecodeLane {
   __amdgpu_buffer_rsrc_t w, x, s, o;
   uint32_t woff[CTW];        // lane's 16 weight bytes in a K block, per column tile
-  uint32_t xoff;             // x1 row l%16 + 32-deep sub-block l/16 (DC_OOB for rows >= m)
+  uint32_t xoff;             // x1 row l%16 + 32-deep sub-block l/16 (BUF_OOB for rows >= m)
   uint32_t soff[CTW];        // lane's scale element per tile (columns clamped to n - 1)
 };
 
@@ -181,12 +174,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   // l/16; x1 row row0 + l%16 (rows >= m read zeros); scale column clamped to
   // n - 1. Every offset a valid lane uses stays inside its buffer.
   DecodeLane<CTW> ln;
-  ln.w = rsrc(a.x2, a.x2_bytes);
-  ln.x = rsrc(a.x1, a.x1_bytes);
-  ln.s = rsrc(a.scale, a.s_bytes);
-  ln.o = rsrc(a.offset, a.s_bytes);
+  ln.w = buf_rsrc(a.x2, a.x2_bytes);
+  ln.x = buf_rsrc(a.x1, a.x1_bytes);
+  ln.s = buf_rsrc(a.scale, a.s_bytes);
+  ln.o = buf_rsrc(a.offset, a.s_bytes);
   const int64_t row = a.row0 + col;
-  ln.xoff = row < a.m ? (uint32_t)(row * a.k * 2 + kq * 64) : DC_OOB;
+  ln.xoff = row < a.m ? (uint32_t)(row * a.k * 2 + kq * 64) : BUF_OOB;
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
     const int64_t ct = ct0 + c < a.nct ? ct0 + c : a.nct - 1;
@@ -210,12 +203,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const int64_t idx = orow * a.n + col0;
   // Unconditional buffer loads (an invalid element reads zero; no bias is a
   // zero-size buffer), so nothing forces a wait before the stream is issued.
-  const __amdgpu_buffer_rsrc_t rres = rsrc(a.residual, (uint32_t)(a.m * a.n * 2));
-  const __amdgpu_buffer_rsrc_t rbias = rsrc(a.bias ? a.bias : a.residual, a.bias ? (uint32_t)(a.n * 2) : 0u);
-  const uint32_t r0 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c0ok ? (uint32_t)(idx * 2) : DC_OOB, 0, 0);
-  const uint32_t r1 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c1ok ? (uint32_t)(idx * 2 + 2) : DC_OOB, 0, 0);
-  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b16(rbias, c0ok ? (uint32_t)(col0 * 2) : DC_OOB, 0, 0);
-  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b16(rbias, c1ok ? (uint32_t)(col0 * 2 + 2) : DC_OOB, 0, 0);
+  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual, (uint32_t)(a.m * a.n * 2));
+  const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias ? a.bias : a.residual, a.bias ? (uint32_t)(a.n * 2) : 0u);
+  const uint32_t r0 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c0ok ? (uint32_t)(idx * 2) : BUF_OOB, 0, 0);
+  const uint32_t r1 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c1ok ? (uint32_t)(idx * 2 + 2) : BUF_OOB, 0, 0);
+  const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b16(rbias, c0ok ? (uint32_t)(col0 * 2) : BUF_OOB, 0, 0);
+  const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b16(rbias, c1ok ? (uint32_t)(col0 * 2 + 2) : BUF_OOB, 0, 0);
 
   const int kbs = (int)(a.k / 128);
   const int kb0 = wave * a.kpw;
@@ -263,8 +256,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
       if (c0ok) a.y[idx] = (uint16_t)(o2 & 0xFFFFu);
       if (c1ok) a.y[idx + 1] = (uint16_t)(o2 >> 16);
     }
-    y0 = c0ok ? lo_f32<ACT>(o2) : 0.f;
-    y1 = c1ok ? hi_f32<ACT>(o2) : 0.f;
+    y0 = c0ok ? y0 : 0.f;                 // the sum of squares uses float32 y
+    y1 = c1ok ? y1 : 0.f;
   }
   // sum of y^2 over the 16 columns of the tile: 8 aligned lanes
   float ss = y0 * y0 + y1 * y1;

@@ -2,11 +2,12 @@
 // one 4-bit value per int32 in, tightly packed nibbles out, in the ND layout
 // or the gfx950 MFMA-operand layout GFX950_B (byte formula in wq.h).
 //
-// One workgroup packs a 128 (K) x 64 (N) tile. The tile's codes are staged in
-// LDS as bytes [n][k], loaded so that global reads are coalesced for either
-// input orientation, then written out in the target layout: GFX950_B as one
-// 16-byte chunk per thread (a column's 32-deep K block), ND as 16-byte runs
-// of a packed row. The op is HBM-bound: 4 bytes read per 0.5 byte written.
+// GFX950_B is built in registers (each word's eight codes come from eight
+// coalesced loads or one 32-byte run) and leaves as one contiguous run per
+// workgroup. ND stages a 128 (K) x 64 (N) tile of codes in LDS as bytes, so
+// global reads are coalesced for either input orientation, then writes
+// 16-byte runs of packed rows. The op is HBM-bound: 4 bytes read per 0.5
+// byte written.
 #include "wq_device.h"
 #include "wq_internal.h"
 
@@ -44,35 +45,95 @@ __device__ __forceinline__ void stage_tile(const int32_t* __restrict__ w, int64_
   }
 }
 
-// Eight byte-sized codes (two dwords read from LDS) -> one word of nibbles,
-// the first code in the lowest nibble.
-__device__ __forceinline__ uint32_t nibbles8(uint32_t d0, uint32_t d1) {
-  auto pack4 = [](uint32_t d) {
-    return (d & 0xFu) | ((d >> 4) & 0xF0u) | ((d >> 8) & 0xF00u) | ((d >> 12) & 0xF000u);
-  };
-  return pack4(d0) | (pack4(d1) << 16);
+// ---- GFX950_B ------------------------------------------------------------
+// In GFX950_B a column's 128-deep K block is one 64-byte record of sixteen
+// words, word w holding K rows 8w..8w+7 (row 8w+j in nibble j), and the
+// records of consecutive columns are consecutive. One workgroup of 16 waves
+// packs one K block of PB_N columns: wave w builds word w of every column
+// straight from registers, the words meet in LDS, and the workgroup's output
+// (PB_N records, one contiguous 16 KiB run) leaves as 16-byte stores.
+constexpr int PB_N = 256;
+
+// LDS slot of word w of tile column c: records stay 64 bytes apart, but the
+// word order inside a record is XOR-swizzled by c/4 so that both ways of
+// building the words write without bank conflicts, and a 16-byte read-back of
+// a record quarter still hits one aligned quarter (with its words permuted).
+__device__ __forceinline__ int pb_slot(int c, int w) { return c * 16 + (w ^ ((c >> 2) & 15)); }
+
+// Eight codes (one per int32, low nibble) -> one word, the first code lowest.
+__device__ __forceinline__ uint32_t nibbles_of(const uint32_t (&v)[8]) {
+  uint32_t word = v[0] & 0xFu;
+#pragma unroll
+  for (int j = 1; j < 8; ++j) word |= (v[j] & 0xFu) << (4 * j);
+  return word;
 }
 
 template <bool TRANSPOSED>
-__global__ __launch_bounds__(256) void pack_gfx950b_kernel(const int32_t* __restrict__ w,
-                                                           int64_t K, int64_t N, int64_t Np,
-                                                           uint8_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[TN][LROW];
-  const int64_t k0 = (int64_t)blockIdx.y * TK;
-  const int64_t n0 = (int64_t)blockIdx.x * TN;
-  stage_tile<TRANSPOSED>(w, K, N, k0, n0, tile);
-  __syncthreads();
+__global__ __launch_bounds__(1024) void pack_gfx950b_kernel(const int32_t* __restrict__ w,
+                                                            int64_t K, int64_t N, int64_t Np,
+                                                            uint8_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint32_t rec[PB_N * 16];
   const int t = threadIdx.x;
-  const int nn = t >> 2, blk = t & 3;
-  const int64_t n = n0 + nn;
-  if (n >= Np) return;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(&tile[nn][blk * 32]);
-  u32x4 v;
-  v.x = nibbles8(src[0], src[1]);
-  v.y = nibbles8(src[2], src[3]);
-  v.z = nibbles8(src[4], src[5]);
-  v.w = nibbles8(src[6], src[7]);
-  *reinterpret_cast<u32x4*>(out + ((k0 / TK) * Np + n) * 64 + blk * 16) = v;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t k0 = (int64_t)blockIdx.y * 128;
+  const int64_t n0 = (int64_t)blockIdx.x * PB_N;
+  if constexpr (!TRANSPOSED) {
+    // weight (K, N): wave `wave` reads rows k0+8*wave.. +7; lane takes tile
+    // columns lane + 64c, so every load instruction reads 256 contiguous bytes.
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(w + k0 * N + n0, 0x7FFFFFFFu);
+    const int kr = 8 * wave;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = lane + 64 * c;
+      const bool nok = n0 + col < N;
+      uint32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = nok && k0 + kr + j < K;
+        v[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, ok ? (uint32_t)(((kr + j) * N + col) * 4) : BUF_OOB, 0, 0);
+      }
+      rec[pb_slot(col, wave)] = nibbles_of(v);
+    }
+  } else {
+    // weight (N, K): a column's 8 codes of one word are 32 contiguous bytes;
+    // 16 lanes cover one column's K block, 4 columns per wave per pass.
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(w + n0 * K + k0, 0x7FFFFFFFu);
+    const int wd = lane & 15;
+    const bool kfull = (K & 7) == 0;   // then a word is wholly in or out of range
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = 4 * wave + (lane >> 4) + 64 * c;
+      const bool nok = n0 + col < N;
+      const uint32_t off = (uint32_t)((col * K + 8 * wd) * 4);
+      uint32_t v[8];
+      if (kfull) {
+        const uint32_t o = nok && k0 + 8 * wd < K ? off : BUF_OOB;
+        const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+        const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 16, 0));
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool ok = nok && k0 + 8 * wd + j < K;
+          v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? off + 4 * j : BUF_OOB, 0, 0);
+        }
+      }
+      rec[pb_slot(col, wd)] = nibbles_of(v);
+    }
+  }
+  __syncthreads();
+  // thread t stores bytes 16t..16t+15 of the run: quarter q of column t/4
+  const int col = t >> 2, q = t & 3;
+  if (n0 + col >= Np) return;
+  const int sw = (col >> 2) & 15;
+  const u32x4 r = *reinterpret_cast<const u32x4*>(&rec[col * 16 + 4 * (q ^ (sw >> 2))]);
+  // word j of the quarter sits at element j ^ (sw & 3)
+  u32x4 v = r;
+  if (sw & 1) v = u32x4{v.y, v.x, v.w, v.z};
+  if (sw & 2) v = u32x4{v.z, v.w, v.x, v.y};
+  *reinterpret_cast<u32x4*>(out + ((k0 / 128) * Np + n0) * 64 + 16 * t) = v;
 }
 
 template <bool TRANSPOSED>
@@ -117,11 +178,13 @@ hipError_t launch_pack_int4(const int32_t* w, int64_t k, int64_t n, bool transpo
   if (layout == WQ_LAYOUT_GFX950_B) {
     const int64_t Kp = 128 * ((k + 127) / 128);
     const int64_t Np = 16 * ((n + 15) / 16);
-    dim3 grid((unsigned)((Np + TN - 1) / TN), (unsigned)(Kp / TK));
+    // tile-relative byte offsets stay below 2^31 (the buffer bound)
+    if ((transpose ? (PB_N * k) : (128 * n)) >= (int64_t(1) << 29)) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((Np + PB_N - 1) / PB_N), (unsigned)(Kp / 128));
     if (transpose)
-      pack_gfx950b_kernel<true><<<grid, 256, 0, s>>>(w, k, n, Np, out);
+      pack_gfx950b_kernel<true><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
     else
-      pack_gfx950b_kernel<false><<<grid, 256, 0, s>>>(w, k, n, Np, out);
+      pack_gfx950b_kernel<false><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
   } else {
     dim3 grid((unsigned)((n + TN - 1) / TN), (unsigned)((k + TK - 1) / TK));
     if (transpose)

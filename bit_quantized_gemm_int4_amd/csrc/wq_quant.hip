@@ -16,58 +16,160 @@ namespace wq {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Per-token. One 256-thread workgroup per row; the row is read twice (max,
-// then codes); the second read is served by L2.
+// Per-token: one workgroup per row (below). MX: one workgroup per 128 x 64
+// tile (further down).
 // ---------------------------------------------------------------------------
 enum OutKind { OUT_INT8 = 0, OUT_NIBBLES = 1 };  // INT4 and INT32 share bytes
 
+// Eight consecutive 16-bit values at byte offset `off` of a buffer, with no
+// branch, so a caller can issue all of its loads before it uses any: an
+// offset of BUF_OOB reads zeros. VEC: `off` is 16-byte aligned and the eight
+// values are all in range or all out; otherwise only the first `lim` are
+// read and the rest are zero.
+template <bool VEC>
+__device__ __forceinline__ u32x4 fetch8(__amdgpu_buffer_rsrc_t r, uint32_t off, int64_t lim) {
+  if constexpr (VEC) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      h[i] = __builtin_amdgcn_raw_buffer_load_b16(r, i < lim ? off + 2 * i : BUF_OOB, 0, 0);
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  }
+}
+
 template <int ACT>
-__device__ __forceinline__ void load8(const uint16_t* __restrict__ x, const uint16_t* __restrict__ sm,
-                                      int64_t c, int64_t cols, bool vec, float v[8]) {
-  if (vec) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + c);
-    uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+__device__ __forceinline__ void widen8(const u32x4& raw, float v[8]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = lo_f32<ACT>(xw[i]);
-      v[2 * i + 1] = hi_f32<ACT>(xw[i]);
-    }
-    if (sm) {
-      const u32x4 sv = *reinterpret_cast<const u32x4*>(sm + c);
-      uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = lo_f32<ACT>(w[i]);
+    v[2 * i + 1] = hi_f32<ACT>(w[i]);
+  }
+}
+
+// Row scale and its reciprocal. The code of v is RNE(fl(v / sc)), the
+// correctly rounded fp32 quotient rounded to an integer. With |v| <= amax and
+// sc = fl(amax / dmax), |v / sc| <= 128; both v * fl(1 / sc) and fl(v / sc)
+// are within 2^-23 relative (so 2.4e-5 absolute) of the exact quotient, and
+// the integer rounding of either one can only differ when the product lies
+// that close to a half-integer. Such values, and rows whose reciprocal
+// overflows (sc subnormal), take the division.
+struct RowScale {
+  float sc, inv;
+  bool fast;
+};
+
+__device__ __forceinline__ RowScale row_scale(float sc) {
+  const float inv = 1.f / sc;
+  return {sc, inv, sc > 0.f && inv < 0x1p126f};
+}
+
+// Quantize 8 values with the row scale and store them at column c.
+template <int OUT>
+__device__ __forceinline__ void store_codes8(void* __restrict__ y, int64_t row, int64_t cols, int64_t c,
+                                             bool vec, const RowScale& rs, float dmax, const float v[8]) {
+  float qf[8];
+  bool slow = !rs.fast;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] *= lo_f32<ACT>(sw[i]);
-        v[2 * i + 1] *= hi_f32<ACT>(sw[i]);
-      }
+  for (int i = 0; i < 8; ++i) {
+    qf[i] = v[i] * rs.inv;
+    const float fr = qf[i] - floorf(qf[i]);   // exact for |qf| < 2^23
+    slow |= fabsf(fr - 0.5f) < 1e-4f;
+  }
+  if (slow) {                                 // rare: recompute with the division
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[i] = rs.sc == 0.f ? 0.f : v[i] / rs.sc;
+  }
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float r = __builtin_rintf(qf[i]);
+    r = fminf(fmaxf(r, -dmax), dmax);
+    q[i] = (int)r;
+  }
+  if constexpr (OUT == OUT_INT8) {
+    int8_t* yr = reinterpret_cast<int8_t*>(y) + row * cols;
+    if (vec) {
+      u32x2 o;
+      o.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((uint32_t)(q[3] & 0xFF) << 24);
+      o.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) | ((uint32_t)(q[7] & 0xFF) << 24);
+      *reinterpret_cast<u32x2*>(yr + c) = o;
+    } else {
+      for (int i = 0; i < 8 && c + i < cols; ++i) yr[c + i] = (int8_t)q[i];
     }
   } else {
+    // two codes per byte, even column in the low nibble (cols is even)
+    uint8_t* yr = reinterpret_cast<uint8_t*>(y) + row * (cols / 2);
+    uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool in = c + i < cols;
-      float t = in ? to_f32<ACT>(x[c + i]) : 0.f;
-      if (sm) t *= in ? to_f32<ACT>(sm[c + i]) : 0.f;
-      v[i] = t;
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)(q[i] & 0xF) << (4 * i);
+    if (vec) {
+      *reinterpret_cast<uint32_t*>(yr + c / 2) = word;
+    } else {
+      for (int i = 0; i < 4 && c + 2 * i < cols; ++i) yr[c / 2 + i] = (uint8_t)(word >> (8 * i));
     }
   }
 }
 
-template <int ACT, int OUT>
+// One 256-thread workgroup per row, read in batches of PT_CACHE 8-column
+// chunks per thread (all loads of a batch in flight together). The first
+// batch (the whole row up to 8192 columns) stays in registers for the codes;
+// later batches are read again.
+constexpr int PT_CACHE = 4;
+constexpr int PT_SPAN = PT_CACHE * 256 * 8;   // columns per batch
+
+// x * smooth for the batch starting at column `base`, zero past the row.
+template <int ACT, bool VEC, bool SMOOTH>
+__device__ __forceinline__ void fetch_batch(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rs,
+                                            int64_t base, int64_t cols, int t,
+                                            float (&v)[PT_CACHE][8]) {
+  u32x4 xr[PT_CACHE], sr[PT_CACHE];
+#pragma unroll
+  for (int j = 0; j < PT_CACHE; ++j) {
+    const int64_t c = base + (j * 256 + t) * 8;
+    const uint32_t off = c < cols ? (uint32_t)(c * 2) : BUF_OOB;
+    xr[j] = fetch8<VEC>(rx, off, cols - c);
+    if constexpr (SMOOTH) sr[j] = fetch8<VEC>(rs, off, cols - c);
+  }
+#pragma unroll
+  for (int j = 0; j < PT_CACHE; ++j) {
+    widen8<ACT>(xr[j], v[j]);
+    if constexpr (SMOOTH) {
+      float sm[8];
+      widen8<ACT>(sr[j], sm);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] *= sm[i];
+    }
+  }
+}
+
+template <int ACT, int OUT, bool VEC, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_per_token_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ smooth, int64_t cols,
     float dmax, void* __restrict__ y, float* __restrict__ scale) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const uint16_t* xr = x + row * cols;
-  const bool vec = (cols & 7) == 0;
   const int t = threadIdx.x;
+  const uint32_t row_bytes = (uint32_t)(cols * 2);
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x + row * cols, row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(SMOOTH ? smooth : x, SMOOTH ? row_bytes : 0u);
 
+  float vc[PT_CACHE][8];
+  fetch_batch<ACT, VEC, SMOOTH>(rx, rs, 0, cols, t, vc);
   float amax = 0.f;
-  for (int64_t c = (int64_t)t * 8; c < cols; c += 256 * 8) {
-    float v[8];
-    load8<ACT>(xr, smooth, c, cols, vec, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int j = 0; j < PT_CACHE; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(vc[j][i]));
+  for (int64_t base = PT_SPAN; base < cols; base += PT_SPAN) {
+    float v[PT_CACHE][8];
+    fetch_batch<ACT, VEC, SMOOTH>(rx, rs, base, cols, t, v);
+#pragma unroll
+    for (int j = 0; j < PT_CACHE; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
   }
   amax = wave_max(amax);
   if ((t & 63) == 0) red[t >> 6] = amax;
@@ -75,38 +177,20 @@ __global__ __launch_bounds__(256) void quant_per_token_kernel(
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc = amax / dmax;                 // correctly rounded fp32 divide
   if (t == 0) scale[row] = sc;
+  const RowScale rsc = row_scale(sc);
 
-  for (int64_t c = (int64_t)t * 8; c < cols; c += 256 * 8) {
-    float v[8];
-    load8<ACT>(xr, smooth, c, cols, vec, v);
-    int q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float r = sc == 0.f ? 0.f : __builtin_rintf(v[i] / sc);   // RNE of the fp32 quotient
-      r = fminf(fmaxf(r, -dmax), dmax);
-      q[i] = (int)r;
-    }
-    if constexpr (OUT == OUT_INT8) {
-      int8_t* yr = reinterpret_cast<int8_t*>(y) + row * cols;
-      if (vec) {
-        u32x2 o;
-        o.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((uint32_t)(q[3] & 0xFF) << 24);
-        o.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) | ((uint32_t)(q[7] & 0xFF) << 24);
-        *reinterpret_cast<u32x2*>(yr + c) = o;
-      } else {
-        for (int i = 0; i < 8 && c + i < cols; ++i) yr[c + i] = (int8_t)q[i];
-      }
-    } else {
-      // two codes per byte, even column in the low nibble (cols is even)
-      uint8_t* yr = reinterpret_cast<uint8_t*>(y) + row * (cols / 2);
-      uint32_t word = 0;
+  for (int j = 0; j < PT_CACHE; ++j) {
+    const int64_t c = (j * 256 + t) * 8;
+    if (c < cols) store_codes8<OUT>(y, row, cols, c, VEC, rsc, dmax, vc[j]);
+  }
+  for (int64_t base = PT_SPAN; base < cols; base += PT_SPAN) {
+    float v[PT_CACHE][8];
+    fetch_batch<ACT, VEC, SMOOTH>(rx, rs, base, cols, t, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) word |= (uint32_t)(q[i] & 0xF) << (4 * i);
-      if (vec) {
-        *reinterpret_cast<uint32_t*>(yr + c / 2) = word;
-      } else {
-        for (int i = 0; i < 4 && c + 2 * i < cols; ++i) yr[c / 2 + i] = (uint8_t)(word >> (8 * i));
-      }
+    for (int j = 0; j < PT_CACHE; ++j) {
+      const int64_t c = base + (j * 256 + t) * 8;
+      if (c < cols) store_codes8<OUT>(y, row, cols, c, VEC, rsc, dmax, v[j]);
     }
   }
 }
@@ -156,7 +240,7 @@ __device__ __forceinline__ uint32_t e2m1(float v) {
   return m | ((__float_as_uint(v) >> 28) & 0x8u);
 }
 
-template <int ACT, int FMT, bool TRANS>
+template <int ACT, int FMT, bool TRANS, bool VEC, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_mx_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ smooth, int64_t rows,
     int64_t cols, uint8_t* __restrict__ y, uint8_t* __restrict__ scale) {
@@ -167,29 +251,29 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
   const int64_t r0 = (int64_t)blockIdx.x * 128 + rg * 4;
   const int64_t c0 = (int64_t)blockIdx.y * 64 + cc * 8;
   const int64_t nb = (cols + 31) / 32;
-  const bool vec = (cols & 7) == 0 && c0 + 8 <= cols;
-
-  float sm[8];
-  if (smooth) {
-    float ones[8];
-    load8<ACT>(smooth, nullptr, c0, cols, vec, ones);
+  // One resource over the workgroup's 128 rows; tile-relative byte offsets
+  // stay below 2^31 for cols < 2^22. All loads are issued before any use.
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x + (int64_t)blockIdx.x * 128 * cols, 0x7FFFFFFFu);
+  const bool cin = c0 < cols;
+  u32x4 raw[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm[i] = ones[i];
+  for (int r = 0; r < 4; ++r) {
+    const bool ok = cin && r0 + r < rows;
+    raw[r] = fetch8<VEC>(rx, ok ? (uint32_t)(((rg * 4 + r) * cols + c0) * 2) : BUF_OOB, cols - c0);
   }
+  float sm[8];
+  if constexpr (SMOOTH)
+    widen8<ACT>(fetch8<VEC>(buf_rsrc(smooth, (uint32_t)(cols * 2)), cin ? (uint32_t)(c0 * 2) : BUF_OOB,
+                            cols - c0), sm);
   uint32_t codes[4][2];                          // 4 rows x 8 codes (bytes or nibbles)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t row = r0 + r;
     float v[8];
-    if (row < rows && c0 < cols) {
-      load8<ACT>(x + row * cols, nullptr, c0, cols, vec, v);
-      if (smooth) {
+    widen8<ACT>(raw[r], v);
+    if constexpr (SMOOTH) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= sm[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      for (int i = 0; i < 8; ++i) v[i] *= sm[i];
     }
     float amax = 0.f;
 #pragma unroll
@@ -219,7 +303,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
       if (row >= rows || c0 >= cols) continue;
       if constexpr (FMT == MX_E4M3) {
         uint8_t* dst = y + row * cols + c0;
-        if (vec) {
+        if (VEC) {
           u32x2 o;
           o.x = codes[r][0];
           o.y = codes[r][1];
@@ -230,7 +314,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
         }
       } else {
         uint8_t* dst = y + row * (cols / 2) + c0 / 2;
-        if (vec) {
+        if (VEC) {
           *reinterpret_cast<uint32_t*>(dst) = codes[r][0];
         } else {
           for (int i = 0; 2 * i < 8 && c0 + 2 * i < cols; ++i) dst[i] = (uint8_t)(codes[r][0] >> (8 * i));
@@ -277,13 +361,20 @@ hipError_t launch_quant_per_token(const void* x, bool bf16, int64_t rows, int64_
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* sp = static_cast<const uint16_t*>(smooth);
   dim3 grid((unsigned)rows);
+  const bool vec = (cols & 7) == 0;
+#define WQ_PT_LAUNCH(A, O)                                                                        \
+  do {                                                                                            \
+    if (vec && sp) quant_per_token_kernel<A, O, true, true><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);   \
+    else if (vec) quant_per_token_kernel<A, O, true, false><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);   \
+    else if (sp) quant_per_token_kernel<A, O, false, true><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);    \
+    else quant_per_token_kernel<A, O, false, false><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);           \
+  } while (0)
   if (y_dtype == WQ_INT8) {
-    if (bf16) quant_per_token_kernel<ACT_BF16, OUT_INT8><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);
-    else quant_per_token_kernel<ACT_F16, OUT_INT8><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);
+    if (bf16) WQ_PT_LAUNCH(ACT_BF16, OUT_INT8); else WQ_PT_LAUNCH(ACT_F16, OUT_INT8);
   } else {
-    if (bf16) quant_per_token_kernel<ACT_BF16, OUT_NIBBLES><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);
-    else quant_per_token_kernel<ACT_F16, OUT_NIBBLES><<<grid, 256, 0, s>>>(xp, sp, cols, dmax, y, scale);
+    if (bf16) WQ_PT_LAUNCH(ACT_BF16, OUT_NIBBLES); else WQ_PT_LAUNCH(ACT_F16, OUT_NIBBLES);
   }
+#undef WQ_PT_LAUNCH
   return hipGetLastError();
 }
 
@@ -293,7 +384,14 @@ hipError_t launch_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols,
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* sp = static_cast<const uint16_t*>(smooth);
   dim3 grid((unsigned)((rows + 127) / 128), (unsigned)((cols + 63) / 64));
-#define WQ_MX_LAUNCH(A, F, T) quant_mx_kernel<A, F, T><<<grid, 256, 0, s>>>(xp, sp, rows, cols, y, scale)
+  const bool vec = (cols & 7) == 0;
+#define WQ_MX_LAUNCH(A, F, T)                                                                     \
+  do {                                                                                            \
+    if (vec && sp) quant_mx_kernel<A, F, T, true, true><<<grid, 256, 0, s>>>(xp, sp, rows, cols, y, scale);   \
+    else if (vec) quant_mx_kernel<A, F, T, true, false><<<grid, 256, 0, s>>>(xp, sp, rows, cols, y, scale);   \
+    else if (sp) quant_mx_kernel<A, F, T, false, true><<<grid, 256, 0, s>>>(xp, sp, rows, cols, y, scale);    \
+    else quant_mx_kernel<A, F, T, false, false><<<grid, 256, 0, s>>>(xp, sp, rows, cols, y, scale);           \
+  } while (0)
   if (y_dtype == WQ_FP8_E4M3) {
     if (transpose_y) {
       if (bf16) WQ_MX_LAUNCH(ACT_BF16, MX_E4M3, true); else WQ_MX_LAUNCH(ACT_F16, MX_E4M3, true);

@@ -90,8 +90,9 @@ int wq_abi_version(void);
  * Stores v & 0xF for each value v (two's complement of an int4 in [-8, 7],
  * or an FP4 E2M1 code 0..15). Values outside [-8, 15] are outside the
  * contract: their low nibble is stored.
- * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE if k < 0, n < 0, or layout ND with n
- * odd; WQ_ERR_UNSUPPORTED for an unknown layout. k == 0 or n == 0 is a no-op.
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE if k < 0, n < 0, layout ND with n
+ * odd, or layout GFX950_B with n >= 2^22 (k >= 2^21 when transposed);
+ * WQ_ERR_UNSUPPORTED for an unknown layout. k == 0 or n == 0 is a no-op.
  * ---------------------------------------------------------------------- */
 size_t wq_pack_int4_bytes(int64_t k, int64_t n, wq_layout layout);
 wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n,
@@ -126,7 +127,8 @@ wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n,
  *            the transposeX1 layout of the MX matmul.
  * Products x * smooth must be exact in float32 (always true for fp16).
  * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (negative sizes, odd cols for INT4 or
- * FP4, cols % 8 for INT32); WQ_ERR_DTYPE; WQ_ERR_UNSUPPORTED (other block_k,
+ * FP4, cols % 8 for INT32, cols >= 2^30 per token, more than 65535 column
+ * tiles of 64 for MX); WQ_ERR_DTYPE; WQ_ERR_UNSUPPORTED (other block_k,
  * transpose with a non-FP8 output). rows == 0 or cols == 0 is a no-op.
  * ---------------------------------------------------------------------- */
 wq_status wq_dynamic_quant(const void* x, wq_dtype x_dtype, int64_t rows,

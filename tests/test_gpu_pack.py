@@ -17,7 +17,8 @@ def _oracle_pack(w, layout, transpose):
     return oracle.pack_int4_gfx950b(w, transpose)
 
 
-@pytest.mark.parametrize("k,n", [(256, 128), (80, 20), (1, 2), (300, 50), (128, 64), (129, 18)])
+@pytest.mark.parametrize("k,n", [(256, 128), (80, 20), (1, 2), (300, 50), (128, 64), (129, 18),
+                                 (200, 530), (1031, 300), (384, 1024)])
 @pytest.mark.parametrize("layout", [wq.WQ_LAYOUT_ND, wq.WQ_LAYOUT_GFX950_B])
 @pytest.mark.parametrize("transpose", [False, True])
 def test_pack_bit_exact(k, n, layout, transpose):

@@ -27,7 +27,8 @@ def _x(rows, cols, dtype, seed, spread=True):
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("y_dtype", [wq.WQ_INT8, wq.WQ_INT4, wq.WQ_INT32])
 @pytest.mark.parametrize("rows,cols,smooth", [(7, 64, True), (33, 2056, False), (5, 24, True),
-                                              (3, 4104, True), (2, 16, False)])
+                                              (3, 4104, True), (2, 16, False), (4, 30, True),
+                                              (6, 8202, False), (3, 16400, True), (2, 8194, True)])
 def test_per_token_bit_exact(dtype, y_dtype, rows, cols, smooth):
     if y_dtype == wq.WQ_INT32 and cols % 8:
         pytest.skip("INT32 needs cols % 8 == 0")
@@ -53,16 +54,49 @@ def test_per_token_zero_rows_and_ties():
     assert s8.cpu()[2].item() == 1.0 and y8.cpu()[2, :4].tolist() == [127, 0, 2, -2]
 
 
+def _all_values_up_to(dtype, amax_bits):
+    """Every finite non-negative value of the 16-bit type up to the one with
+    bits amax_bits, both signs, as float32 (exact)."""
+    if dtype == torch.float16:
+        v = np.arange(0, amax_bits + 1, dtype=np.uint16).view(np.float16).astype(np.float32)
+    else:
+        v = (np.arange(0, amax_bits + 1, dtype=np.uint32) << 16).view(np.float32)
+    return np.concatenate([v, -v[1:]])
+
+
+# Row scales where v * (1 / scale) and the correctly rounded v / scale round
+# to different integers for a few v (found by enumeration), so every such
+# quotient is checked against the division the operator defines.
+@pytest.mark.parametrize("dtype,amax_bits,y_dtype", [
+    (torch.float16, 0x63D0, wq.WQ_INT4),      # amax 1000, dmax 7
+    (torch.float16, 0x1F45, wq.WQ_INT8),      # amax 0.0071, dmax 127
+    (torch.bfloat16, 0x3C15, wq.WQ_INT8),
+    (torch.bfloat16, 0x3C23, wq.WQ_INT4)])
+def test_per_token_every_value_near_half_quotients(dtype, amax_bits, y_dtype):
+    note(f"quant per-token every value up to 0x{amax_bits:04x} {dtype} {OUT[y_dtype]}")
+    v = _all_values_up_to(dtype, amax_bits)
+    v = np.concatenate([v, np.zeros((-v.size) % 8, np.float32)])   # 16-byte rows as well
+    for x_np in (v[None, :], v[None, : v.size - 6]):
+        x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dtype)
+        assert np.array_equal(x.float().numpy(), x_np)
+        y, scale = wq.dynamic_quant(x.to(DEV), None, y_dtype)
+        q, sc = oracle.dynamic_quant_per_token(as_f64(x), None, OUT[y_dtype])
+        assert np.array_equal(scale.cpu().numpy(), sc)
+        assert np.array_equal(y.cpu().numpy(), encode_quant_output(q, OUT[y_dtype]))
+
+
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("fmt,transpose", [("e4m3", False), ("e4m3", True), ("e2m1", False)])
-@pytest.mark.parametrize("rows,cols", [(128, 64), (200, 96), (37, 80), (5, 8), (130, 200)])
-def test_mx_bit_exact(dtype, fmt, transpose, rows, cols):
-    note(f"quant mx {fmt} transpose={transpose} {dtype} {rows}x{cols}")
+@pytest.mark.parametrize("rows,cols,smooth", [(128, 64, True), (200, 96, True), (37, 80, True),
+                                              (5, 8, True), (130, 200, True), (129, 90, True),
+                                              (37, 20, False), (260, 136, False)])
+def test_mx_bit_exact(dtype, fmt, transpose, rows, cols, smooth):
+    note(f"quant mx {fmt} transpose={transpose} {dtype} {rows}x{cols} smooth={smooth}")
     x = _x(rows, cols, dtype, rows + cols)
-    sm = workloads.cast(np.random.default_rng(2).uniform(0.5, 2.0, cols), dtype)
+    sm = workloads.cast(np.random.default_rng(2).uniform(0.5, 2.0, cols), dtype) if smooth else None
     ydt = wq.WQ_FP8_E4M3 if fmt == "e4m3" else wq.WQ_FP4_E2M1
-    y, sc = wq.dynamic_quant(x.to(DEV), sm.to(DEV), ydt, 32, transpose)
-    codes, scales = oracle.dynamic_quant_mx(as_f64(x), as_f64(sm), fmt)
+    y, sc = wq.dynamic_quant(x.to(DEV), None if sm is None else sm.to(DEV), ydt, 32, transpose)
+    codes, scales = oracle.dynamic_quant_mx(as_f64(x), None if sm is None else as_f64(sm), fmt)
     assert np.array_equal(sc.cpu().numpy(), scales)
     got = y.cpu().numpy()
     if fmt == "e2m1":
