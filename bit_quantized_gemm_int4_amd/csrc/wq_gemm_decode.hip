@@ -140,7 +140,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs& a, const DecodeL
       ma.rs = mfma16<ACT>(av, ones, ma.rs);
 #pragma unroll
       for (int c = 0; c < CTW; ++c) {
-        const u32x4 b = unpack8(wv[j][c][w4], 0x000F000Fu, Magic<ACT>::bits);
+        const u32x4 b = unpack8(wv[j][c][w4], NIBBLE_MASK, Magic<ACT>::xbits);
         ma.part[c] = mfma16<ACT>(av, b, ma.part[c]);
       }
     }

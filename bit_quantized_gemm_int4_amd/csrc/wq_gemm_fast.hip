@@ -55,6 +55,8 @@ struct FastArgs {
   int64_t group;           // K length of a group (multiple of 128, or >= k)
   int64_t s_row, s_col;
   int64_t groups, gp;      // groups = ceil(k / group); gp = 32 * ceil(groups / 32)
+  uint32_t s_bytes;        // extent of the scale tensor in bytes
+  uint32_t* zflag;         // [ceil(np / 512)] nonzero: a zero group scale in that column strip
 };
 
 // ---------------------------------------------------------------------------
@@ -65,9 +67,12 @@ struct FastArgs {
 template <int ACT>
 __global__ __launch_bounds__(256) void group_rowsum_kernel(const uint16_t* __restrict__ x1, int64_t k,
                                                            int64_t group, int64_t groups, int64_t gp,
-                                                           uint16_t* __restrict__ rs) {
+                                                           uint16_t* __restrict__ rs,
+                                                           uint32_t* __restrict__ zflag, int nstrips) {
   extern __shared__ float chunk_sum[];        // k / 8 floats
   const int64_t row = blockIdx.x;
+  if (row == 0)                               // cleared here, set by the correction pass
+    for (int i = threadIdx.x; i < nstrips; i += 256) zflag[i] = 0u;
   const uint16_t* xr = x1 + row * k;
   const int64_t chunks = k / 8;
   for (int64_t c = threadIdx.x; c < chunks; c += 256) {
@@ -96,13 +101,15 @@ __global__ __launch_bounds__(256) void group_rowsum_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // Pre-pass 2: per-group column corrections o[g][n] - bias * s[g][n] (zero for
 // padding), written [np][2][gp] as bf16 hi/lo. One thread per (column, group).
+// Also flags each 512-column strip that holds a zero group scale.
 // ---------------------------------------------------------------------------
 template <int ACT>
 __global__ __launch_bounds__(256) void group_corr_kernel(const uint16_t* __restrict__ scale,
                                                          const uint16_t* __restrict__ offset,
                                                          int64_t n, int64_t np, int64_t groups,
                                                          int64_t gp, int64_t s_row, int64_t s_col,
-                                                         uint16_t* __restrict__ corr) {
+                                                         uint16_t* __restrict__ corr,
+                                                         uint32_t* __restrict__ zflag) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= np * gp) return;
   const int64_t col = idx / gp, g = idx % gp;
@@ -112,6 +119,7 @@ __global__ __launch_bounds__(256) void group_corr_kernel(const uint16_t* __restr
     const float sv = to_f32<ACT>(scale[si]);
     const float ov = offset ? to_f32<ACT>(offset[si]) : 0.f;
     c = ov - Magic<ACT>::bias * sv;
+    if (sv == 0.f) atomicOr(&zflag[col / 512], 1u);   // the main tile's strip width
   }
   uint16_t hi, lo;
   split_bf16(c, hi, lo);
@@ -130,126 +138,180 @@ constexpr int WD_EROW = (64 + 4) * 4;              // epilogue staging row (fp32
 static_assert(32 * WD_EROW <= 16384, "epilogue staging must fit a wave's 16 KiB region");
 
 // x1 slab (128 rows x 128 K) -> LDS: 32 DMA instructions of 1 KiB (4 rows);
-// wave w issues 4w + j: rows 4*(4w + j) + lane/16. LDS rows are 256 bytes; the
-// 16-byte chunk j of row r sits at position j ^ (r & 15), so the A-fragment
-// reads of 16 lanes (16 rows, one K chunk) hit 16 distinct bank groups.
-// off[j] is the lane's element offset of instruction j from the tile's first
-// row (row and swizzled chunk); k0 advances it by slab.
-__device__ __forceinline__ void wd_dma_a(const uint16_t* xblk, const uint32_t (&off)[4], uint32_t k0,
-                                         uint8_t* buf) {
-  const int wave = threadIdx.x >> 6;
+// wave w issues 4w + j: rows 16w + 4j + lane/16. LDS rows are 256 bytes; the
+// 16-byte chunk of row r at position p holds logical chunk p ^ (r & 15), so
+// the A-fragment reads of 16 lanes (16 rows, one K chunk) hit 16 distinct
+// bank groups. With r & 15 = lane/16 + 4j the lane's source chunk is
+// c0 ^ 4j, c0 = (lane & 15) ^ (lane / 16), and its byte offset is
+// (v0 ^ 64j) + 8jk with v0 = (16w + lane/16) * 2k + 16 c0 (2k is a multiple
+// of 256, so the XOR only touches the chunk bits). The buffer resource
+// starts at the slab and ends after the tile's last row: rows past m read 0.
+__device__ __forceinline__ void wd_dma_a(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf) {
+  const int wave = wave_id();
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds((glb_void*)(xblk + (off[j] + k0)),
-                                     (lds_void*)(buf + (4 * wave + j) * 4 * WD_LROW), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (4 * wave + j) * 4 * WD_LROW), 16,
+                                             (v0 ^ (64u * j)) + 8u * j * k, 0, 0, 0);
 }
 
 // Weight slab for the tile's 512 columns (64 bytes per column in GFX950_B
-// order): 32 DMA instructions of 1 KiB (16 columns); wave w issues chunks
-// 4w + j, lane l the 16 bytes of column 16*chunk + l/4, block l%4; bsrc[j] is
-// the lane's byte offset from the tile's first column (clamped to the padded
-// width; columns past n are computed but never stored).
-__device__ __forceinline__ void wd_dma_b(const uint8_t* xslab, const int32_t (&bsrc)[4], uint8_t* buf) {
-  const int wave = threadIdx.x >> 6;
+// order) in 32 chunks of 16 columns (1 KiB), one DMA instruction each: wave
+// w issues chunks 4w + j. Inside a chunk, 16-byte slot p holds column p / 4,
+// K block b = (p % 4) ^ (p / 16), i.e. slot 4c + (b ^ (c / 4)) for column c:
+// with the per-step dword rotation of wd_slab, every 64-lane 4-byte read of
+// the weight fragments then hits 64 distinct banks. Lane l fetches slot l:
+// byte v0 + 1024 j of the tile's slab row, v0 = 4096 w + 64 (l / 4) +
+// 16 ((l % 4) ^ (l / 16)). The resource ends at the padded width: columns
+// past it read 0 (never stored).
+__device__ __forceinline__ uint32_t wd_b_v0(int wave, int lane) {
+  return 4096u * wave + 64u * (lane >> 2) + 16u * ((lane & 3) ^ (lane >> 4));
+}
+
+__device__ __forceinline__ void wd_dma_b(__amdgpu_buffer_rsrc_t rb, uint32_t v0, uint8_t* buf) {
+  // (the instruction's immediate offset would also move the LDS address, so
+  // the 1 KiB step goes into the per-lane offset)
+  uint8_t* dst = buf + wave_id() * 4096;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds((glb_void*)(xslab + bsrc[j]),
-                                     (lds_void*)(buf + (4 * wave + j) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + 1024 * j), 16, v0 + 1024u * j, 0, 0, 0);
 }
 
 // One 128-deep slab accumulated into acc: acc[i][f] += sum over the slab of
-// x1 * (q + bias), the MFMAs accumulating in place. Per K step c: the eight
-// A-fragment reads, the four weight fragments unpacked, 32 MFMAs.
-template <int ACT>
+// x1 * (q + bias), the MFMAs accumulating in place. The slab runs as four
+// 32-deep K steps; a step is four passes (column tile f) of eight MFMAs (row
+// tile i). The instruction order is fixed by hand (a scheduling barrier
+// after every MFMA slot) so that each operand is held once and every load
+// and unpack hides behind MFMAs:
+//  - pass f of step c unpacks one weight fragment in five pieces between its
+//    MFMAs: pass 0 fragment 3 of step c, pass f > 0 fragment f - 1 of step
+//    c + 1 (the registers of a fragment are free once its pass is done);
+//  - the packed dwords are read a step ahead: tiles 0..2 at the step start,
+//    tile 3 in pass 1 (after pass 0 consumed the previous one);
+//  - pass 3 refills A fragment i for step c + 1 right after its last MFMA;
+//  - FIRST (the slab starts a quantization group): accumulator (i, f) is
+//    rescaled by ratio[f] = old scale / new scale one MFMA slot before its
+//    first MFMA of the slab.
+// MASKED: per-lane masks mk / mc zero the weight operand of columns whose
+// group scale is zero (otherwise the unpack constants apply).
+template <int ACT, bool FIRST, bool MASKED>
 __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf,
-                                        const uint32_t (&mk)[4], const uint32_t (&mg)[4],
-                                        f32x4 (&acc)[8][4]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t b[4][4];
+                                        const uint32_t (&mk)[4], const uint32_t (&mc)[4],
+                                        const float (&ratio)[4], f32x4 (&acc)[8][4]) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  // Step c gives lane group g = lane / 16 the 8 K values of dword
+  // d = (c + g) % 4 of its 32-deep block (A chunk 4g + d), a rotation that
+  // makes the weight reads conflict-free; each group still covers its block
+  // once over the four steps.
+  const int g = lane >> 4, cl = lane & 15;
+  const uint8_t* arow = abuf + cl * WD_LROW;
+  const uint8_t* brow = wbuf + wave * 4096 + 16 * (4 * cl + (g ^ (cl >> 2)));
+  auto a_at = [&](int i, int c) {
+    return *reinterpret_cast<const u32x4*>(arow + i * 16 * WD_LROW + (((4 * g + ((c + g) & 3)) ^ cl) * 16));
+  };
+  auto b_at = [&](int f, int c) {
+    return *reinterpret_cast<const uint32_t*>(brow + f * 1024 + 4 * ((c + g) & 3));
+  };
+  auto rescale = [&](int i, int f) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(
-        wbuf + (wave * 64 + 16 * f + (lane & 15)) * 64 + (lane >> 4) * 16);
-    b[f][0] = v.x;
-    b[f][1] = v.y;
-    b[f][2] = v.z;
-    b[f][3] = v.w;
-  }
-  const uint8_t* arow = abuf + (lane & 15) * WD_LROW;
+    for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
+  };
+  uint32_t w4;
+  // piece p (0..4) of unpacking dword w of column tile f into out
+  auto unpack_piece = [&](int p, uint32_t w, int f, u32x4& out) {
+    const uint32_t m = MASKED ? mk[f] : NIBBLE_MASK;
+    const uint32_t cc = MASKED ? mc[f] : Magic<ACT>::xbits;
+    if (p == 0) w4 = w >> 4;
+    if (p == 1) out.x = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C040C00u), m, cc);
+    if (p == 2) out.y = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C050C01u), m, cc);
+    if (p == 3) out.z = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C060C02u), m, cc);
+    if (p == 4) out.w = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C070C03u), m, cc);
+  };
+
+  uint32_t rw[4];
+  u32x4 av[8], bf[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) rw[f] = b_at(f, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) av[i] = a_at(i, 0);
+#pragma unroll
+  for (int f = 0; f < 3; ++f)
+#pragma unroll
+    for (int p = 0; p < 5; ++p) unpack_piece(p, rw[f], f, bf[f]);
+#pragma unroll
+  for (int f = 0; f < 3; ++f) rw[f] = b_at(f, 1);
+  if (FIRST) rescale(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int pos = ((4 * (lane >> 4) + c) ^ (lane & 15)) * 16;
-    u32x4 av[8];
+    if (c > 0 && c + 1 < 4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) av[i] = *reinterpret_cast<const u32x4*>(arow + i * 16 * WD_LROW + pos);
-    u32x4 bf[4];
+      for (int f = 0; f < 3; ++f) rw[f] = b_at(f, c + 1);
+    }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bf[f] = unpack8(b[f][c], mk[f], mg[f]);
+    for (int f = 0; f < 4; ++f) {
+      // the fragment this pass unpacks: tile 3 of this step, or tile f - 1
+      // of the next one
+      const int uf = f == 0 ? 3 : f - 1;
+      const bool unpacking = f == 0 || c + 1 < 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int f = 0; f < 4; ++f) acc[i][f] = mfma16<ACT>(av[i], bf[f], acc[i][f]);
+      for (int i = 0; i < 8; ++i) {
+        acc[i][f] = mfma16<ACT>(av[i], bf[f], acc[i][f]);
+        if (FIRST && c == 0) {
+          if (i < 7) rescale(i + 1, f);
+          else if (f < 3) rescale(0, f + 1);
+        }
+        if (unpacking && i < 5) unpack_piece(i, rw[uf], uf, bf[uf]);
+        if (f == 1 && i == 5 && c + 1 < 4) rw[3] = b_at(3, c + 1);
+        if (f == 3 && c + 1 < 4) av[i] = a_at(i, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 }
 
-template <int ACT>
-__global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_m, int64_t tiles_n) {
-  // Four LDS objects (two x1 slabs, two weight slabs): the compiler then sees
-  // that the DMA filling one buffer does not alias reads of the other.
-  __shared__ __attribute__((aligned(16))) uint8_t abuf0[WD_ABUF];
-  __shared__ __attribute__((aligned(16))) uint8_t abuf1[WD_ABUF];
-  __shared__ __attribute__((aligned(16))) uint8_t wbuf0[WD_BBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t wbuf1[WD_BBUF];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-
-  // XCD-aware tile order: consecutive workgroups land on different XCDs, so
-  // give each XCD a contiguous range of tiles, walked two tile-rows at a time.
-  const int64_t T = tiles_m * tiles_n;
-  int64_t id = blockIdx.x;
-  if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
-  const int64_t band = id / (2 * tiles_n);
-  const int64_t rem = id % (2 * tiles_n);
-  int64_t tm = band * 2 + (rem & 1);
-  int64_t tn = rem >> 1;
-  if (band * 2 + 1 >= tiles_m && (tiles_m & 1)) {  // last odd band: one tile-row
-    tm = band * 2;
-    tn = rem;
-  }
-  const int64_t m0 = tm * WD_BM;
-  const int64_t n0 = tn * WD_BN;
+// The tile's K loop, rank-1 remainder and epilogue. EVERY: every slab starts
+// a quantization group (group = 128), so each slab rescales inside its MFMA
+// stream; otherwise the rescale runs before the first slab of a group.
+template <int ACT, bool EVERY, bool MASKED>
+__device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t n0, uint8_t* abuf0,
+                                          uint8_t* abuf1, uint8_t* wbuf0, uint8_t* wbuf1) {
+  const int t = threadIdx.x, lane = t & 63, wave = wave_id();
   const int64_t ncol0 = n0 + wave * 64;             // the wave's first column
   const int slabs = (int)(a.k / WD_KS);
   const uint32_t k = (uint32_t)a.k;
 
-  // ---- DMA sources ----
-  const uint16_t* xblk = a.x1 + m0 * a.k;
+  // ---- DMA sources: one base offset per lane and operand; the buffer
+  //      resources are rebuilt per slab in scalar registers ----
   const int rows_left = (int)(a.m - m0 < WD_BM ? a.m - m0 : WD_BM);
-  uint32_t aoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (4 * wave + j) * 4 + (lane >> 4);
-    const int cj = (lane & 15) ^ (row & 15);
-    const int r = row < rows_left ? row : rows_left - 1;   // rows past m: never stored
-    aoff[j] = (uint32_t)r * k + 8 * cj;
-  }
-  const uint8_t* xw = a.x2 + n0 * 64;
+  const uint32_t a_v0 = (uint32_t)(16 * wave + (lane >> 4)) * 2u * k +
+                        16u * (uint32_t)((lane & 15) ^ (lane >> 4));
+  const uint32_t b_v0 = wd_b_v0(wave, lane);
   const int64_t slab_bytes = a.np * 64;
-  int32_t bsrc[4];
+  auto rsrc_a = [&](int sl) {
+    return buf_rsrc(a.x1 + m0 * a.k + (int64_t)sl * WD_KS,
+                    (uint32_t)(rows_left * 2 * a.k - (int64_t)sl * 2 * WD_KS));
+  };
+  auto rsrc_b = [&](int sl) {
+    return buf_rsrc(a.x2 + sl * slab_bytes + n0 * 64, (uint32_t)((a.np - n0) * 64));
+  };
+  // Scales: lane's column of tile f is ncol0 + 16 f + lane % 16; a column
+  // past n reads scale 0 (its weight operand is then zeroed and it is never
+  // stored). Raw 16-bit scales are kept two to a register.
+  const __amdgpu_buffer_rsrc_t rscale = buf_rsrc(a.scale, a.s_bytes);
+  auto load_scales = [&](int64_t g, uint32_t (&dst)[2]) {
+    uint32_t v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int64_t col = n0 + 16 * (4 * wave + j) + (lane >> 2);
-    col = col < a.np ? col : a.np - 1;
-    bsrc[j] = (int32_t)((col - n0) * 64 + (lane & 3) * 16);
-  }
-  // scale offsets of the wave's 4 column tiles (clamped; columns past n get scale 0)
-  uint32_t soff[4];
-  float cmask[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int64_t col = ncol0 + 16 * f + (lane & 15);
-    soff[f] = (uint32_t)((col < a.n ? col : a.n - 1) * a.s_col);
-    cmask[f] = col < a.n ? 1.f : 0.f;
-  }
+    for (int f = 0; f < 4; ++f) {
+      const int64_t col = ncol0 + 16 * f + (lane & 15);
+      v[f] = __builtin_amdgcn_raw_buffer_load_b16(
+          rscale, col < a.n ? (uint32_t)(col * a.s_col * 2) : BUF_OOB, (uint32_t)(g * a.s_row * 2), 0);
+    }
+    dst[0] = v[0] | (v[1] << 16);
+    dst[1] = v[2] | (v[3] << 16);
+  };
+  auto scale_of = [](const uint32_t (&sc)[2], int f) -> uint16_t {
+    return (uint16_t)(sc[f >> 1] >> (16 * (f & 1)));
+  };
   const int spg = (int)(a.group / WD_KS);              // slabs per group (>= 1)
 
   f32x4 acc[8][4];
@@ -258,14 +320,13 @@ __global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[i][f] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  wd_dma_a(xblk, aoff, 0, abuf0);
-  wd_dma_b(xw, bsrc, wbuf0);
+  wd_dma_a(rsrc_a(0), a_v0, k, abuf0);
+  wd_dma_b(rsrc_b(0), b_v0, wbuf0);
   // raw scales of the current group and of the next one; the next group's
   // are loaded one step ahead, before that step's DMA, and used only after
   // the step's barrier, so waiting for them never waits for the DMA.
-  uint16_t scur[4], snxt[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) scur[f] = a.scale[soff[f]];
+  uint32_t scur[2], snxt[2];
+  load_scales(0, scur);
   __syncthreads();
 
   // acc holds the running sum in units of the current group's scale cs:
@@ -273,43 +334,43 @@ __global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_
   // MFMAs add that group's x1 * (q + bias) to acc, and cs = s. A zero scale
   // zeroes the column's weight operand and leaves acc and cs unchanged.
   float cs[4] = {0.f, 0.f, 0.f, 0.f};
-  uint32_t mk[4], mg[4];
+  float ratio[4];
+  uint32_t mk[4], mc[4];                               // MASKED: per-lane unpack masks
   int gpos = 0;                                        // slab index within its group
-  const uint16_t* srow_next = a.scale + a.s_row;       // scale row of the next group
+  int64_t gnext = 1;                                   // the next group
   auto step = [&](int s, const uint8_t* acur, uint8_t* anxt, const uint8_t* wcur, uint8_t* wnxt) {
     const bool more = s + 1 < slabs;
-    if (more && gpos == spg - 1) {                     // next slab starts a group
-#pragma unroll
-      for (int f = 0; f < 4; ++f) snxt[f] = srow_next[soff[f]];
-      srow_next += a.s_row;
-    }
+    if (more && gpos == spg - 1) load_scales(gnext++, snxt);   // next slab starts a group
     if (more) {
-      wd_dma_a(xblk, aoff, (uint32_t)(s + 1) * WD_KS, anxt);
-      wd_dma_b(xw + (s + 1) * slab_bytes, bsrc, wnxt);
+      wd_dma_a(rsrc_a(s + 1), a_v0, k, anxt);
+      wd_dma_b(rsrc_b(s + 1), b_v0, wnxt);
     }
     if (gpos == 0) {                                   // group start
-      float ratio[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const float sg = to_f32<ACT>(scur[f]) * cmask[f];
+        const float sg = to_f32<ACT>(scale_of(scur, f));
         const bool z = sg == 0.f;
-        ratio[f] = (z || cs[f] == 0.f) ? 1.f : cs[f] / sg;
+        ratio[f] = (z || cs[f] == 0.f) ? 1.f : cs[f] * __builtin_amdgcn_rcpf(sg);   // ~2 ulp
         cs[f] = z ? cs[f] : sg;
-        mk[f] = z ? 0u : 0x000F000Fu;
-        mg[f] = z ? 0u : Magic<ACT>::bits;
+        if (MASKED) {
+          mk[f] = z ? 0u : NIBBLE_MASK;
+          mc[f] = z ? 0u : Magic<ACT>::xbits;
+        }
       }
+      if (!EVERY) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+          for (int f = 0; f < 4; ++f)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
+            for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
+      }
     }
-    wd_slab<ACT>(acur, wcur, mk, mg, acc);
+    wd_slab<ACT, EVERY, MASKED>(acur, wcur, mk, mc, ratio, acc);
     if (++gpos == spg) {
       gpos = 0;
-#pragma unroll
-      for (int f = 0; f < 4; ++f) scur[f] = snxt[f];
+      scur[0] = snxt[0];
+      scur[1] = snxt[1];
     }
     __syncthreads();
   };
@@ -419,6 +480,41 @@ __global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_
   }
 }
 
+template <int ACT, bool EVERY>
+__global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_m, int64_t tiles_n) {
+  // Four LDS objects (two x1 slabs, two weight slabs): the compiler then sees
+  // that the DMA filling one buffer does not alias reads of the other.
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[WD_ABUF];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[WD_ABUF];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf0[WD_BBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf1[WD_BBUF];
+  const int t = threadIdx.x, lane = t & 63, wave = wave_id();
+
+  // XCD-aware tile order: consecutive workgroups land on different XCDs, so
+  // give each XCD a contiguous range of tiles, walked two tile-rows at a time.
+  const int64_t T = tiles_m * tiles_n;
+  int64_t id = blockIdx.x;
+  if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
+  const int64_t band = id / (2 * tiles_n);
+  const int64_t rem = id % (2 * tiles_n);
+  int64_t tm = band * 2 + (rem & 1);
+  int64_t tn = rem >> 1;
+  if (band * 2 + 1 >= tiles_m && (tiles_m & 1)) {  // last odd band: one tile-row
+    tm = band * 2;
+    tn = rem;
+  }
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // tile origin (and the buffer resources built from it) in scalar registers
+  const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)tm) * WD_BM;
+  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((int)tn) * WD_BN;
+  // A tile with a zero group scale somewhere in its columns (flagged by the
+  // correction pre-pass) or with columns past n runs the masked variant;
+  // the branch is taken once, outside the K loop.
+  const bool masked = n0 + WD_BN > a.n || a.zflag[n0 / WD_BN] != 0;
+  if (masked) wide_body<ACT, EVERY, true>(a, m0, n0, abuf0, abuf1, wbuf0, wbuf1);
+  else wide_body<ACT, EVERY, false>(a, m0, n0, abuf0, abuf1, wbuf0, wbuf1);
+}
+
 template <int ACT>
 hipError_t launch_wide_t(const WqProblem& p, float* partial, uint16_t* rs, uint16_t* corr,
                          hipStream_t s) {
@@ -441,18 +537,22 @@ hipError_t launch_wide_t(const WqProblem& p, float* partial, uint16_t* rs, uint1
   a.s_col = p.s_col;
   a.groups = (p.k + a.group - 1) / a.group;
   a.gp = 32 * ((a.groups + 31) / 32);
+  a.s_bytes = (uint32_t)(((a.groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
+  const int nstrips = (int)((a.np + WD_BN - 1) / WD_BN);
+  a.zflag = reinterpret_cast<uint32_t*>(corr + a.np * 2 * a.gp);
   group_rowsum_kernel<ACT><<<dim3((unsigned)p.m), 256, (size_t)(p.k / 8) * sizeof(float), s>>>(
-      a.x1, p.k, a.group, a.groups, a.gp, rs);
+      a.x1, p.k, a.group, a.groups, a.gp, rs, a.zflag, nstrips);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t cells = a.np * a.gp;
   group_corr_kernel<ACT><<<dim3((unsigned)((cells + 255) / 256)), 256, 0, s>>>(
       a.scale, static_cast<const uint16_t*>(p.offset), p.n, a.np, a.groups, a.gp, p.s_row,
-      p.s_col, corr);
+      p.s_col, corr, a.zflag);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tm = (p.m + WD_BM - 1) / WD_BM, tn = (p.n + WD_BN - 1) / WD_BN;
-  gemm_b_wide<ACT><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(a, tm, tn);
+  if (a.group == WD_KS) gemm_b_wide<ACT, true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(a, tm, tn);
+  else gemm_b_wide<ACT, false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(a, tm, tn);
   return hipGetLastError();
 }
 
@@ -471,11 +571,12 @@ size_t fast_rowsum_bytes(int64_t m, int64_t k) {
   const int64_t gp = 32 * ((groups + 31) / 32);
   return ((size_t)(m * 2 * gp * 2) + 255) & ~(size_t)255;
 }
+// ... followed by the zero-scale flags of the 512-column strips
 size_t fast_corr_bytes(int64_t n, int64_t k) {
   const int64_t groups = (k + 127) / 128;
   const int64_t gp = 32 * ((groups + 31) / 32);
   const int64_t np = 16 * ((n + 15) / 16);
-  return ((size_t)(np * 2 * gp * 2) + 255) & ~(size_t)255;
+  return ((size_t)(np * 2 * gp * 2 + (np + WD_BN - 1) / WD_BN * 4) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint16_t* corr,

@@ -157,6 +157,10 @@ FAST = [  # m, k, n, granularity, group, offset, bias, act: the large-m GFX950_B
     (512, 1024, 256, "group", 256, (-0.5, 0.5), 0.1, torch.float16),
     (33, 128, 18, "channel2d", 0, None, 0.1, torch.bfloat16),
     (520, 2048, 300, "group", 128, "none", None, torch.bfloat16),
+    # whole 512-column strips (the unmasked tile), next to a ragged one
+    (256, 512, 1024, "group", 128, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (384, 1024, 1536, "group", 256, (-0.5, 0.5), None, torch.float16),
+    (200, 640, 1100, "channel", 0, (-0.5, 0.5), 0.1, torch.bfloat16),
 ]
 
 
@@ -197,6 +201,21 @@ def test_decode_kernel_shapes(shape):
     check_wq(c, y, nrm)
     y2, n2 = wq_on_gpu(c, inplace=True)
     assert torch.equal(y, y2) and torch.equal(nrm, n2)
+
+
+@pytest.mark.parametrize("G", [128, 256])
+def test_fast_zero_scale_in_one_strip(G):
+    # zero group scales inside one 512-column strip only: that strip's tiles
+    # zero the weight operand, the other strips run unmasked
+    m, k, n = 160, 512, 1536
+    c = workloads.wq_case(f"fast_zero_scale_g{G}", m, k, n, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=G, scale_range=(0.002, 0.02),
+                          offset_range=(-1.0, 1.0), bias_std=0.1, seed=13 + G)
+    c.scale[1, 600:610] = 0
+    c.scale[:, 700] = 0
+    note(f"wq fast tile zero-scale strip g={G}")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
 
 
 def test_decode_zero_scale_columns():
