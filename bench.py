@@ -9,9 +9,12 @@ torch's current stream:
   3. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
   4. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
   5. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
-Every operator is timed with HIP events around its launch(es). The headline
-``value`` is the W4A16 dequant-GEMM + AddRmsNorm throughput of row 2 in
-TFLOP/s (2*M*N*K per call). A separate decode section times the HBM-bound
+Every operator is timed with HIP events around its launch(es); the library
+also times its contraction kernels (the prefill MFMA tile, the MX GEMM, the
+decode weight stream) with event pairs on their own stream (wq_profile_*).
+The headline ``value`` is the W4A16 dequant-GEMM + AddRmsNorm throughput of
+row 2 in TFLOP/s (2*M*N*K per call, all of its launches); ``roofline`` rates
+its MFMA tile alone against the bf16 MFMA peak. A separate decode section times the HBM-bound
 W4A16 decode shapes (m in {1, 8, 16}, k 4096, n 11008) rotating 24 weight
 copies so that the 256 MB last-level cache cannot hold them.
 
@@ -34,6 +37,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (the E4M3 x E2M1 MX rate)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+# rows whose call launches one contraction kernel that the library times
+CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "mx_matmul_inplace_add": "mx_gemm_tile"}
 COPY_BYTES = 256 << 20         # calibration copy (--only copy)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
 
@@ -51,9 +56,10 @@ def source_hash() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per prefill call from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel's reading),
-    or None when the summary is missing or was taken on other sources."""
+    """HBM bytes per launch of the prefill MFMA tile (gemm_b_wide) from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled
+    by a copy kernel's reading), or None when the summary is missing or was
+    taken on other sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
             text = fh.read()
@@ -67,7 +73,7 @@ def measured_traffic():
     if vals.get("source_hash") != source_hash():
         return None
     try:
-        return int(vals["traffic_bytes_per_call"])
+        return int(vals["gemm_b_wide_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -186,12 +192,22 @@ def main():
         step(None)
     torch.cuda.synchronize()
     rec = {r[0]: [] for r in rows}
+    # the library times its contraction kernels (one launch per wq / mx call)
+    # with event pairs on the stream they run on, inside the timed region
+    contraction_rows = [r[0] for r in rows if r[0] in CONTRACTION_ROWS]
+    wq.wq_profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(rec)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    kernel_times = wq.wq_profile_read()
+    wq.wq_profile_enable(False)
     ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
+    kernel_ms = {}
+    if contraction_rows and len(kernel_times) == args.steps * len(contraction_rows):
+        for j, name in enumerate(contraction_rows):
+            kernel_ms[name] = statistics.mean(kernel_times[j::len(contraction_rows)])
 
     out_rows = {}
     for name, _, flop, nbytes, bound in rows:
@@ -202,6 +218,11 @@ def main():
         if flop:
             d["TFLOP/s"] = round(flop / ms / 1e9, 2)
             d["flop"] = flop
+        if name in kernel_ms:
+            km = kernel_ms[name]
+            d["kernel"] = CONTRACTION_ROWS[name]
+            d["kernel_ms"] = round(km, 5)
+            d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
         peak = PEAK_BF16_TFLOPS if name == "wq_matmul_add_rmsnorm" else PEAK_FP8_TFLOPS
         d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
                                   else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
@@ -243,12 +264,28 @@ def main():
                 evs.append((a, b))
             torch.cuda.synchronize()
             ts = sorted(a.elapsed_time(b) for a, b in evs)
+            # the weight-stream kernel alone, in a loop of its own (the extra
+            # event records would otherwise sit inside the per-call timing)
+            wq.wq_profile_enable(True)
+            for i in range(args.decode_iters):
+                call(i)
+            torch.cuda.synchronize()
+            ktimes = wq.wq_profile_read()
+            wq.wq_profile_enable(False)
             med = statistics.median(ts)
             nbytes = (xb[0].numel() + 2 * sd.numel() * 2 + m * dk * 2 + 3 * m * dn * 2 + 2 * dn * 2)
             decode[f"m{m}"] = {"us": round(med * 1e3, 3), "us_p10": round(ts[len(ts) // 10] * 1e3, 3),
                                "us_p90": round(ts[(9 * len(ts)) // 10] * 1e3, 3),
                                "GB/s": round(nbytes / med / 1e6, 1), "bytes": nbytes,
                                "frac_of_hbm_peak": round(nbytes / med / 1e6 / PEAK_HBM_GBS, 4)}
+            if ktimes:
+                kmed = statistics.median(ktimes)
+                # the weight stream alone: packed weights, scales, offsets, x1,
+                # residual, bias, y and its sum-of-squares partials
+                kbytes = xb[0].numel() + 2 * sd.numel() * 2 + m * dk * 2 + 2 * m * dn * 2 + dn * 2
+                decode[f"m{m}"].update({"kernel": "gemm_decode", "kernel_us": round(kmed * 1e3, 3),
+                                        "kernel_GB/s": round(kbytes / kmed / 1e6, 1),
+                                        "kernel_bytes": kbytes})
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     cpu = None
@@ -302,11 +339,12 @@ def main():
         "decode": decode,
         "cpu_baseline": cpu,
     }
-    if head:
-        line["roofline"] = {"bound": "mfma", "achieved": head["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(head["TFLOP/s"] / PEAK_BF16_TFLOPS, 4),
+    if head and "kernel_TFLOP/s" in head:
+        ach = head["kernel_TFLOP/s"]
+        line["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                             "traffic": measured_traffic(),
-                            "kernel": "wq_matmul_add_rmsnorm (all launches of one call)"}
+                            "kernel": head["kernel"], "kernel_ms": head["kernel_ms"]}
     print(json.dumps(line), flush=True)
 
 

@@ -41,6 +41,7 @@ EXPORTS = (
     "wq_dynamic_quant",
     "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
     "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
+    "wq_profile_enable", "wq_profile_read",
 )
 
 _lib = None
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                           P, P, P, D, P, P, P, S, P]),
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
+            "wq_profile_enable": (I, [I]),
+            "wq_profile_read": (I, [P, I64, ctypes.POINTER(I64)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -123,6 +126,20 @@ def wq_dynamic_quant(x, x_dtype, rows, cols, smooth, y_dtype, block_k, transpose
     st = lib().wq_dynamic_quant(_ptr(x), x_dtype, rows, cols, _ptr(smooth), y_dtype, block_k,
                                 int(transpose_y), _ptr(y), _ptr(scale), _stream(stream))
     return _check(st, "wq_dynamic_quant", check)
+
+
+def wq_profile_enable(enable: bool, check=True) -> int:
+    return _check(lib().wq_profile_enable(int(enable)), "wq_profile_enable", check)
+
+
+def wq_profile_read(capacity: int = 4096, check=True):
+    """Per-launch contraction-kernel times (ms, launch order) recorded since
+    the last enable / read."""
+    buf = (ctypes.c_float * max(capacity, 1))()
+    n = ctypes.c_int64(0)
+    _check(lib().wq_profile_read(ctypes.addressof(buf), capacity, ctypes.byref(n)),
+           "wq_profile_read", check)
+    return [buf[i] for i in range(min(n.value, capacity))]
 
 
 def wq_matmul_add_rmsnorm_workspace_size(m: int, k: int, n: int) -> int:

@@ -271,12 +271,16 @@ hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s) {
   // the tiled kernel addresses y through a buffer resource (32-bit offsets)
   if (p.m % MF_BM == 0 && p.n % MF_BN == 0 && p.k % MF_BK == 0 && p.m * p.n * 4 < (int64_t(1) << 31)) {
     const int64_t tm = p.m / MF_BM, tn = p.n / MF_BN;
+    prof_begin(s);
     mx_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
                                                          Np, tm, tn);
+    prof_end(s);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((p.n + MX_BN - 1) / MX_BN), (unsigned)((p.m + MX_BM - 1) / MX_BM));
+  prof_begin(s);
   mx_gemm_kernel<<<grid, 256, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n, Np);
+  prof_end(s);
   return hipGetLastError();
 }
 

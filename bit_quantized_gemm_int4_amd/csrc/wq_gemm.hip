@@ -270,6 +270,7 @@ __global__ __launch_bounds__(256) void rmsnorm_finish(const uint16_t* __restrict
 template <int ACT>
 hipError_t launch_generic(const WqProblem& p, const GemmArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((p.m + GB_M - 1) / GB_M), (unsigned)((p.n + GB_N - 1) / GB_N));
+  prof_begin(s);
   if (p.w_bits == 4) {
     if (p.layout == WQ_LAYOUT_GFX950_B) gemm_generic<ACT, W_I4_B><<<grid, 256, 0, s>>>(a);
     else gemm_generic<ACT, W_I4_ND><<<grid, 256, 0, s>>>(a);
@@ -277,6 +278,7 @@ hipError_t launch_generic(const WqProblem& p, const GemmArgs& a, hipStream_t s) 
     if (p.transpose_x2) gemm_generic<ACT, W_I8_T><<<grid, 256, 0, s>>>(a);
     else gemm_generic<ACT, W_I8_ND><<<grid, 256, 0, s>>>(a);
   }
+  prof_end(s);
   return hipGetLastError();
 }
 

@@ -268,7 +268,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 
 template <int ACT, int CTW>
 void launch_ct(const DecodeArgs& a, unsigned grid, hipStream_t s) {
+  prof_begin(s);
   gemm_decode<ACT, CTW, 2><<<dim3(grid), 1024, 0, s>>>(a);
+  prof_end(s);
 }
 
 template <int ACT>

@@ -385,6 +385,27 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][f][r] *= cs[f];
 
+  // Residual rows for the epilogue, prefetched a quarter (32 rows) ahead so
+  // their HBM latency hides behind the remainder MFMAs and the previous
+  // quarter: lane (lr, lc) of quarter qt, pass st reads row 32 qt + 8 st + lr,
+  // columns ncol0 + lc .. + 7. Rows past m and lanes outside the 16-byte path
+  // read zeros (the latter use the element path below).
+  const int lr = lane >> 3, lc = (lane & 7) * 8;       // row within 8, first column
+  const int64_t col = ncol0 + lc;
+  const bool vec = (a.n & 7) == 0 && col + 8 <= a.n;
+  const int rows_here = (int)(a.m - m0 < WD_BM ? a.m - m0 : WD_BM);
+  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual + m0 * a.n, (uint32_t)(rows_here * a.n * 2));
+  auto load_res = [&](int qt, u32x4 (&rr)[4]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int rl = 32 * qt + 8 * st + lr;
+      rr[st] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rres, vec && rl < rows_here ? (uint32_t)((rl * a.n + col) * 2) : BUF_OOB, 0, 0));
+    }
+  };
+  u32x4 res_cur[4];
+  load_res(0, res_cur);
+
   // ---- rank-1 remainder: acc += sum_g rowsum_g(x) * corr_g over the group
   //      axis, three bf16 MFMA products per 32 groups ----
   for (int64_t g0 = 0; g0 < a.gp; g0 += 32) {
@@ -419,14 +440,13 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
   //      with 16-byte loads/stores, and the row's sum of y^2 over each
   //      32-column half of the wave's columns ----
   uint8_t* stage = (wave < 2 ? abuf0 : wave < 4 ? abuf1 : wave < 6 ? wbuf0 : wbuf1) + (wave & 1) * 16384;
-  const int lr = lane >> 3, lc = (lane & 7) * 8;       // row within 8, first column
-  const int64_t col = ncol0 + lc;
-  const bool vec = (a.n & 7) == 0 && col + 8 <= a.n;
   float bv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) bv[e] = (a.bias && col + e < a.n) ? to_f32<ACT>(a.bias[col + e]) : 0.f;
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
+    u32x4 res_nxt[4];
+    if (qt + 1 < 4) load_res(qt + 1, res_nxt);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -437,7 +457,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
           *reinterpret_cast<float*>(stage + row * WD_EROW + (16 * f + (lane & 15)) * 4) = acc[2 * qt + i][f][r];
         }
     __syncthreads();
-#pragma unroll 2
+#pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int rl = 8 * st + lr;                                // 0..31
       const int64_t row = m0 + 32 * qt + rl;
@@ -449,7 +469,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
       if (row < a.m) {
         const int64_t idx = row * a.n + col;
         if (vec) {
-          const u32x4 rv = *reinterpret_cast<const u32x4*>(a.residual + idx);
+          const u32x4 rv = res_cur[st];
           const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
           uint32_t yw[4];
 #pragma unroll
@@ -477,6 +497,10 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
       if ((lane & 3) == 0 && row < a.m && c32 < a.n) a.partial[row * ((a.n + 31) / 32) + c32 / 32] = ss;
     }
     __syncthreads();
+    if (qt + 1 < 4) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) res_cur[st] = res_nxt[st];
+    }
   }
 }
 
@@ -551,8 +575,10 @@ hipError_t launch_wide_t(const WqProblem& p, float* partial, uint16_t* rs, uint1
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tm = (p.m + WD_BM - 1) / WD_BM, tn = (p.n + WD_BN - 1) / WD_BN;
+  prof_begin(s);
   if (a.group == WD_KS) gemm_b_wide<ACT, true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(a, tm, tn);
   else gemm_b_wide<ACT, false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(a, tm, tn);
+  prof_end(s);
   return hipGetLastError();
 }
 

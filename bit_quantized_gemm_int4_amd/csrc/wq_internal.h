@@ -72,4 +72,8 @@ struct MxProblem {
 
 hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s);
 
+// Profiling hook (wq_profile.cpp): event pair around a contraction kernel.
+void prof_begin(hipStream_t s);
+void prof_end(hipStream_t s);
+
 }  // namespace wq

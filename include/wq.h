@@ -218,6 +218,26 @@ wq_status mx_quant_matmul_inplace_add(
     int64_t group_size, float* y, void* workspace, size_t workspace_size,
     hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Profiling of the contraction kernels (a measurement aid, not part of any
+ * operator): while enabled, each wq_matmul_add_rmsnorm and
+ * mx_quant_matmul_inplace_add call records a pair of HIP events on its
+ * stream around its contraction kernel (the MFMA tile, the decode weight
+ * stream or the generic tile; not the pre-passes or the RMSNorm finish).
+ *
+ * wq_profile_enable(1) creates the events on first use and clears the
+ * record; (0) stops recording. wq_profile_read waits for the recorded
+ * events, stores *launches = the number of timed launches since the last
+ * enable / read (at most 4096; later ones are not timed), writes the first
+ * min(capacity, *launches) kernel times in milliseconds, in launch order, to
+ * times_ms (host memory, caller-owned; may be null when capacity is 0), and
+ * clears the record. The record is process-wide; calls on several threads
+ * interleave in it.
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_LAUNCH if the runtime refuses an event.
+ * ---------------------------------------------------------------------- */
+wq_status wq_profile_enable(int enable);
+wq_status wq_profile_read(float* times_ms, int64_t capacity, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,6 +2,7 @@
 include/wq.h, and its host-side validation rejects bad arguments before any
 launch. No test here launches a kernel: each call breaks a rule that is
 checked on the host, and the fake device addresses are never dereferenced."""
+import ctypes
 import os
 import re
 
@@ -28,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -41,6 +42,14 @@ def test_version_and_status_strings():
         s = wq.lib().wq_status_string(code).decode()
         assert s.startswith("WQ_")
     assert wq.lib().wq_status_string(99).decode() == "unknown wq_status"
+
+
+def test_profile_read_without_a_record():
+    # nothing recorded yet: zero time, zero launches, no device call needed
+    assert wq.wq_profile_read() == []
+    assert wq.lib().wq_profile_read(None, 0, None) == wq.WQ_ERR_NULLPTR
+    n = ctypes.c_int64(0)
+    assert wq.lib().wq_profile_read(None, 4, ctypes.byref(n)) == wq.WQ_ERR_NULLPTR  # no buffer
 
 
 def test_size_queries():
@@ -70,6 +79,9 @@ def test_pack_validation():
     assert _pack(out=FAKE2 + 4) == wq.WQ_ERR_SHAPE                 # misaligned output
     assert _pack(out=FAKE + 64) == wq.WQ_ERR_ALIAS                 # overlaps the input
     assert _pack(k=0) == wq.WQ_OK and _pack(n=0) == wq.WQ_OK       # empty: no-op
+    # GFX950_B tiles use 32-bit byte offsets: n < 2^22, or k < 2^21 transposed
+    assert _pack(layout=wq.WQ_LAYOUT_GFX950_B, n=1 << 22) == wq.WQ_ERR_SHAPE
+    assert _pack(layout=wq.WQ_LAYOUT_GFX950_B, k=1 << 21, transpose=1) == wq.WQ_ERR_SHAPE
 
 
 def _quant(**kw):
@@ -95,6 +107,7 @@ def test_dynamic_quant_validation():
     assert _quant(scale=None) == wq.WQ_ERR_NULLPTR
     assert _quant(x=FAKE + 2) == wq.WQ_ERR_SHAPE
     assert _quant(rows=0) == wq.WQ_OK and _quant(cols=0) == wq.WQ_OK
+    assert _quant(cols=1 << 30) == wq.WQ_ERR_SHAPE                 # per-token row offsets
 
 
 def _wqmm(**kw):
