@@ -81,9 +81,10 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-iters", type=int, default=200)
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of rows to run (profiling)")
     return ap.parse_args()
@@ -213,7 +214,9 @@ def main():
     for name, _, flop, nbytes, bound in rows:
         times = [a.elapsed_time(b) for a, b in rec[name]]
         ms = statistics.median(times)
-        d = {"ms": round(ms, 5), "ms_mean": round(statistics.mean(times), 5),
+        ts = sorted(times)
+        d = {"ms": round(ms, 5), "ms_p10": round(ts[len(ts) // 10], 5),
+             "ms_p90": round(ts[(9 * len(ts)) // 10], 5), "ms_mean": round(statistics.mean(times), 5),
              "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
         if flop:
             d["TFLOP/s"] = round(flop / ms / 1e9, 2)
@@ -287,6 +290,47 @@ def main():
                                         "kernel_GB/s": round(kbytes / kmed / 1e6, 1),
                                         "kernel_bytes": kbytes})
 
+    # ---------------- achievable ceilings on this GPU (context, not targets) -------------
+    ceilings = None
+    if not args.no_ceilings and not only:
+        ceilings = {}
+        # vendor dense bf16 GEMM (hipBLASLt via torch.matmul) at the prefill shape
+        xa = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
+        wb = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
+        for _ in range(5):
+            torch.matmul(xa, wb)
+        evs = []
+        for _ in range(20):
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            torch.matmul(xa, wb)
+            b0.record(stream)
+            evs.append((a0, b0))
+        torch.cuda.synchronize()
+        mm_ms = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+        ceilings["dense_bf16_matmul"] = {"what": f"torch.matmul bf16 {M}x{K}x{N} (hipBLASLt)",
+                                         "ms": round(mm_ms, 5),
+                                         "TFLOP/s": round(2 * M * N * K / mm_ms / 1e9, 1)}
+        del xa, wb
+        # HBM: a device copy far larger than the 256 MB last-level cache
+        cb = 512 << 20
+        src = torch.empty(cb, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        evs = []
+        for _ in range(10):
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            dst.copy_(src)
+            b0.record(stream)
+            evs.append((a0, b0))
+        torch.cuda.synchronize()
+        cp_ms = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+        ceilings["hbm_copy"] = {"what": "device copy of 512 MiB (read + write)", "ms": round(cp_ms, 5),
+                                "GB/s": round(2 * cb / cp_ms / 1e6, 1)}
+        del src, dst
+
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     cpu = None
     if not args.no_cpu_baseline and want("wq_matmul_add_rmsnorm"):
@@ -338,6 +382,7 @@ def main():
         "rows": out_rows,
         "decode": decode,
         "cpu_baseline": cpu,
+        "ceilings": ceilings,
     }
     if head and "kernel_TFLOP/s" in head:
         ach = head["kernel_TFLOP/s"]

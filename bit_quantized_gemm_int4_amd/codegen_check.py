@@ -53,3 +53,31 @@ def partial_overlaps(asm_text: str) -> List[str]:
 
 def count_mfma(asm_text: str) -> int:
     return sum(1 for line in asm_text.splitlines() if line.strip().startswith("v_mfma"))
+
+
+def kernel_resources(asm_text: str) -> dict:
+    """Per-kernel resource figures from the code-object metadata of an
+    assembly listing: {kernel name: {"private_segment": bytes of scratch per
+    lane, "vgpr_spill": n, "sgpr_spill": n, "vgpr": n}}."""
+    import re
+    out = {}
+    cur = None
+    for line in asm_text.splitlines():
+        m = re.match(r"\s*\.amdhsa_kernel\s+(\S+)", line)
+        if m:
+            cur = m.group(1)
+            out.setdefault(cur, {})
+            continue
+        m = re.match(r"\s*\.amdhsa_private_segment_fixed_size\s+(\d+)", line)
+        if m and cur:
+            out[cur]["private_segment"] = int(m.group(1))
+        m = re.match(r"\s*-?\s*\.name:\s+(\S+)", line)
+        if m:
+            cur = m.group(1)
+            out.setdefault(cur, {})
+        for key, field in (("vgpr_spill", "vgpr_spill_count"), ("sgpr_spill", "sgpr_spill_count"),
+                           ("vgpr", "vgpr_count")):
+            m = re.match(r"\s*\.%s:\s+(\d+)" % field, line)
+            if m and cur:
+                out[cur][key] = int(m.group(1))
+    return out

@@ -335,7 +335,7 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
   hipError_t e;
   // partials are row-major: [row][tile], 32-column tiles (16 for decode)
   int64_t tiles = (p.n + 31) / 32;
-  if (fast_path_ok(p) && p.m <= 32) {
+  if (fast_path_ok(p) && decode_ok(p)) {
     tiles = decode_tiles(p.n);
     e = launch_decode(p, a.partial, s);
   } else if (fast_path_ok(p)) {

@@ -278,14 +278,19 @@ void launch_act(const DecodeArgs& a, int ctw, unsigned grid, hipStream_t s) {
   switch (ctw) {
     case 1: launch_ct<ACT, 1>(a, grid, s); break;
     case 2: launch_ct<ACT, 2>(a, grid, s); break;
-    case 3: launch_ct<ACT, 3>(a, grid, s); break;
-    default: launch_ct<ACT, 4>(a, grid, s); break;
+    default: launch_ct<ACT, 3>(a, grid, s); break;
   }
 }
 
 }  // namespace
 
 int64_t decode_tiles(int64_t n) { return (n + 15) / 16; }
+
+// The weight stream addresses the packed weight through one buffer resource
+// whose out-of-range offset is 2^31: the weight must stay below 2 GiB.
+bool decode_ok(const WqProblem& p) {
+  return p.m <= 32 && (p.k / 128) * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
+}
 
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   DecodeArgs a;
@@ -314,7 +319,8 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   const int64_t kbs = p.k / 128;
   a.kpw = (int32_t)((kbs + DC_WAVES - 1) / DC_WAVES);
   // column tiles per workgroup: keep the grid within one workgroup per CU
-  const int ctw = a.nct <= 256 ? 1 : a.nct <= 512 ? 2 : a.nct <= 768 ? 3 : 4;
+  // up to 768 tiles (n = 12288); wider layers take more workgroups of 3
+  const int ctw = a.nct <= 256 ? 1 : a.nct <= 512 ? 2 : 3;
   const unsigned grid = (unsigned)((a.nct + ctw - 1) / ctw);
   // one launch per 16 rows (m <= 32: at most two; the second finds the
   // weights in the last-level cache)

@@ -59,6 +59,7 @@ hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint
 // Weight-streaming kernel for m <= 32 on the same fast-path problems; writes
 // sums of y^2 per (row, 16-column tile), row-major: decode_tiles(n) per row.
 int64_t decode_tiles(int64_t n);
+bool decode_ok(const WqProblem& p);
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s);
 
 struct MxProblem {

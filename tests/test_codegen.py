@@ -1,11 +1,12 @@
-"""Static check of the gfx950 code the MFMA kernels compile to (no GPU needed):
-no MFMA destination may partially overlap one of its source operands."""
+"""Static checks of the gfx950 code the kernels compile to (no GPU needed): no
+MFMA destination may partially overlap one of its source operands, and no
+kernel spills registers or uses scratch memory."""
 import shutil
 
 import pytest
 
 from bit_quantized_gemm_int4_amd import build as wqbuild
-from bit_quantized_gemm_int4_amd.codegen_check import count_mfma, partial_overlaps
+from bit_quantized_gemm_int4_amd.codegen_check import count_mfma, kernel_resources, partial_overlaps
 
 
 def test_checker_flags_partial_overlaps():
@@ -31,3 +32,18 @@ def test_mfma_operands_never_partially_overlap(src):
     asm = wqbuild.device_asm(src)
     assert count_mfma(asm) > 0
     assert partial_overlaps(asm) == []
+
+
+@pytest.mark.skipif(shutil.which(wqbuild.HIPCC) is None and not __import__("os").path.exists(wqbuild.HIPCC),
+                    reason="hipcc not available")
+@pytest.mark.parametrize("src", [s for s in wqbuild.SOURCES if s.endswith(".hip")])
+def test_no_spills_no_scratch(src):
+    import os
+    os.makedirs(wqbuild.BUILD_DIR, exist_ok=True)
+    res = kernel_resources(wqbuild.device_asm(src))
+    kernels = {k: v for k, v in res.items() if "private_segment" in v}
+    assert kernels, src
+    for name, v in kernels.items():
+        # SGPR spills go to VGPR lanes, not memory; VGPR spills would need scratch
+        assert v["private_segment"] == 0, (name, v)
+        assert v.get("vgpr_spill", 0) == 0, (name, v)
