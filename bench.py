@@ -9,6 +9,8 @@ torch's current stream:
   3. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
   4. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
   5. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
+  6. wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 3's output)
+                           x INT8 weight (4096, 8192), per-token x per-channel
 Every operator is timed with HIP events around its launch(es); the library
 also times its contraction kernels (the prefill MFMA tile, the MX GEMM, the
 decode weight stream) with event pairs on their own stream (wq_profile_*).
@@ -36,9 +38,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (the E4M3 x E2M1 MX rate)
+PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rows whose call launches one contraction kernel that the library times
-CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "mx_matmul_inplace_add": "mx_gemm_tile"}
+CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "mx_matmul_inplace_add": "mx_gemm_tile",
+                    "quant_matmul_inplace_add_int8": "i8_gemm_tile"}
 COPY_BYTES = 256 << 20         # calibration copy (--only copy)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
 
@@ -139,6 +143,9 @@ def main():
     s2 = mxc.x2_scale.to(dev)
     ymx = mxc.y.to(dev)
     del mxc
+    i8c = workloads.int8_gemm(MM, MK, MN)
+    w8t, w8s, y8 = i8c.w.to(dev), i8c.w_scale.to(dev), i8c.y.to(dev)
+    del i8c
     torch.cuda.synchronize()
 
     def op_pack():
@@ -159,6 +166,10 @@ def main():
         wq.mx_quant_matmul_inplace_add(x1q, x2mx, wq.WQ_LAYOUT_GFX950_B, s1, s2, MM, MK, MN, 1, 0,
                                        wq.MX_GROUP_SIZE, ymx)
 
+    def op_i8():
+        # the A8W8 chain's GEMM on the per-token INT8 output of op_quant_tok
+        wq.wq_quant_matmul_inplace_add(q8, w8t, q8s, w8s, MM, MK, MN, y8)
+
     # algorithmic work per call (inputs + outputs as passed; packed weights)
     rows = [
         ("pack", op_pack, 0, K * N * 4 + x2.numel(), "hbm"),
@@ -168,6 +179,8 @@ def main():
         ("dynamic_quant_mx", op_quant_mx, 0, MM * MK * 2 + MK * 2 + MM * MK + s1.numel(), "hbm"),
         ("mx_matmul_inplace_add", op_mx, 2 * MM * MN * MK,
          x1q.numel() + x2mx.numel() + s1.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
+        ("quant_matmul_inplace_add_int8", op_i8, 2 * MM * MN * MK,
+         MM * MK + MN * MK + MM * 4 + MN * 4 + 2 * MM * MN * 4, "mfma"),
     ]
     rows = [r for r in rows if want(r[0])]
     if "copy" in only:
@@ -226,7 +239,8 @@ def main():
             d["kernel"] = CONTRACTION_ROWS[name]
             d["kernel_ms"] = round(km, 5)
             d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
-        peak = PEAK_BF16_TFLOPS if name == "wq_matmul_add_rmsnorm" else PEAK_FP8_TFLOPS
+        peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS,
+                "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS}.get(name, PEAK_FP8_TFLOPS)
         d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
                                   else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
         out_rows[name] = d

@@ -41,6 +41,7 @@ EXPORTS = (
     "wq_dynamic_quant",
     "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
     "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
+    "wq_quant_matmul_inplace_add",
     "wq_profile_enable", "wq_profile_read",
 )
 
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
                                           P, P, P, D, P, P, P, S, P]),
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
+            "wq_quant_matmul_inplace_add": (I, [P, P, P, P, I64, I64, I64, P, P]),
             "wq_profile_enable": (I, [I]),
             "wq_profile_read": (I, [P, I64, ctypes.POINTER(I64)]),
         }
@@ -126,6 +128,13 @@ def wq_dynamic_quant(x, x_dtype, rows, cols, smooth, y_dtype, block_k, transpose
     st = lib().wq_dynamic_quant(_ptr(x), x_dtype, rows, cols, _ptr(smooth), y_dtype, block_k,
                                 int(transpose_y), _ptr(y), _ptr(scale), _stream(stream))
     return _check(st, "wq_dynamic_quant", check)
+
+
+def wq_quant_matmul_inplace_add(x1, x2, x1_scale, x2_scale, m, k, n, y, stream=None,
+                                check=True) -> int:
+    st = lib().wq_quant_matmul_inplace_add(_ptr(x1), _ptr(x2), _ptr(x1_scale), _ptr(x2_scale), m, k,
+                                           n, _ptr(y), _stream(stream))
+    return _check(st, "wq_quant_matmul_inplace_add", check)
 
 
 def wq_profile_enable(enable: bool, check=True) -> int:
@@ -237,4 +246,14 @@ def mx_matmul_inplace_add(x1_t: torch.Tensor, x2_packed: torch.Tensor, x1_scale:
     """y += the MX block-32 product; x1_t is (k, m) E4M3, x2 GFX950_B E2M1."""
     mx_quant_matmul_inplace_add(x1_t, x2_packed, WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n,
                                 1, 0, group_size, y, None, 0, stream)
+    return y
+
+
+def quant_matmul_inplace_add(x1: torch.Tensor, x2_t: torch.Tensor, x1_scale: torch.Tensor,
+                             x2_scale: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y += (x1 @ x2_t.T) * x1_scale[:, None] * x2_scale[None, :] with INT8
+    x1 (m, k), x2_t (n, k), float32 scales and y (m, n) updated in place."""
+    m, k = x1.shape
+    n = x2_t.shape[0]
+    wq_quant_matmul_inplace_add(x1, x2_t, x1_scale, x2_scale, m, k, n, y, stream)
     return y

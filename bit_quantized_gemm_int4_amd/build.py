@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_profile.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
-           "wq_gemm_decode.hip", "mx_gemm.hip"]
+           "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -35,12 +35,15 @@ FLAGS = [
 # multiplies, so its MFMAs keep accumulators in ordinary VGPRs (no AGPR
 # copies). Its accumulators are long-lived and updated in place; the decode
 # kernel, whose per-block partial sums are short-lived, keeps them in AGPRs.
-FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              # the INT8 epilogue rounds each float step on its own, as its
+              # reading of the formula fixes: no fused multiply-add
+              "i8_gemm.hip": ["-ffp-contract=off"]}
 
 
 # Sources with MFMA kernels: their device assembly is checked for MFMA
 # destinations that partially overlap a source operand (codegen_check).
-MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "mx_gemm.hip"]
+MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip"]
 
 
 def _compile(src: str) -> str:

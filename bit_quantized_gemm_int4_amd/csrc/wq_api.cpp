@@ -244,4 +244,26 @@ wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout 
   return from_hip(wq::launch_mx_matmul(p, stream));
 }
 
+// ---------------------------------------------------------------------------
+wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const float* x1_scale,
+                                      const float* x2_scale, int64_t m, int64_t k, int64_t n,
+                                      float* y, hipStream_t stream) {
+  if (m < 0 || n < 0 || m > kMaxRows || n > kMaxKN) return WQ_ERR_SHAPE;
+  // k rows of 16-byte chunks; sums of |x| <= 128 products stay inside int32
+  if (k < 1 || k > kMaxKN || (k % 16)) return WQ_ERR_SHAPE;
+  if (m == 0 || n == 0) return WQ_OK;
+  if (!x1 || !x2 || !x1_scale || !x2_scale || !y) return WQ_ERR_NULLPTR;
+  if (!aligned16(x1) || !aligned16(x2) || (reinterpret_cast<uintptr_t>(y) & 3) ||
+      (reinterpret_cast<uintptr_t>(x1_scale) & 3) || (reinterpret_cast<uintptr_t>(x2_scale) & 3))
+    return WQ_ERR_SHAPE;
+  const size_t ybytes = (size_t)(m * n) * 4;
+  if (overlap(y, ybytes, x1, (size_t)(m * k)) || overlap(y, ybytes, x2, (size_t)(n * k)) ||
+      overlap(y, ybytes, x1_scale, (size_t)m * 4) || overlap(y, ybytes, x2_scale, (size_t)n * 4))
+    return WQ_ERR_ALIAS;
+  if ((m + 255) / 256 * ((n + 255) / 256) > 2147483647LL) return WQ_ERR_SHAPE;
+  wq::I8Problem p{static_cast<const int8_t*>(x1), static_cast<const int8_t*>(x2), x1_scale, x2_scale,
+                  y, m, k, n};
+  return from_hip(wq::launch_i8_matmul(p, stream));
+}
+
 }  // extern "C"

@@ -73,6 +73,17 @@ struct MxProblem {
 
 hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s);
 
+struct I8Problem {
+  const int8_t* x1;      // (m, k)
+  const int8_t* x2t;     // (n, k)
+  const float* s1;       // (m)
+  const float* s2;       // (n)
+  float* y;              // (m, n)
+  int64_t m, k, n;
+};
+
+hipError_t launch_i8_matmul(const I8Problem& p, hipStream_t s);
+
 // Profiling hook (wq_profile.cpp): event pair around a contraction kernel.
 void prof_begin(hipStream_t s);
 void prof_end(hipStream_t s);

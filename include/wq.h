@@ -219,6 +219,31 @@ wq_status mx_quant_matmul_inplace_add(
     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * INT8 quantized matmul with in-place add (aclnnQuantBatchMatmulInplaceAdd
+ * page, Formula, read for INT8 operands with one K group, i.e. groupSizeK =
+ * K, a per-token scale for x1 and a per-channel scale for x2):
+ *
+ *   y[m,n] = (sum_k x1[m,k] * x2[n,k]) * (x1_scale[m] * x2_scale[n]) + y[m,n]
+ *
+ * x1: int8 (m, k) row-major (the per-token output of wq_dynamic_quant with
+ *     y_dtype INT8); x1_scale: float32 (m) (its scale output).
+ * x2: int8 stored (n, k) row-major (transposed: each output column's k
+ *     values contiguous); x2_scale: float32 (n).
+ * y:  float32 (m, n) row-major, read and written in place.
+ * The sum over k is exact (int32); then, in float32 with round-to-nearest-
+ * even at each step: s = x1_scale[m] * x2_scale[n], t = float(sum) * s,
+ * y = y + t. All pointers are device memory owned by the caller; x1 and x2
+ * 16-byte aligned, the scales and y 4-byte aligned; y must not overlap an
+ * input. No workspace. m == 0 or n == 0 is an empty no-op.
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (m < 0, n outside [0, 65535], k
+ * outside [1, 65535] or not a multiple of 16, misaligned pointers);
+ * WQ_ERR_ALIAS (y overlapping an input).
+ * ---------------------------------------------------------------------- */
+wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const float* x1_scale,
+                                      const float* x2_scale, int64_t m, int64_t k, int64_t n,
+                                      float* y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Profiling of the contraction kernels (a measurement aid, not part of any
  * operator): while enabled, each wq_matmul_add_rmsnorm and
  * mx_quant_matmul_inplace_add call records a pair of HIP events on its

@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -188,3 +188,25 @@ def test_mx_matmul_validation():
     assert _mx(y=FAKE2 + 4) == wq.WQ_ERR_SHAPE
     assert _mx(y=FAKE2 + 16) == wq.WQ_ERR_ALIAS                      # y over x2
     assert _mx(m=0) == wq.WQ_OK and _mx(k=0) == wq.WQ_OK
+
+
+def _qmm(**kw):
+    a = dict(x1=FAKE, x2=FAKE2, s1=FAKE3, s2=FAKE3 + 0x4000, m=32, k=64, n=48, y=FAKE + 0x40000000,
+             stream=0)
+    a.update(kw)
+    return wq.lib().wq_quant_matmul_inplace_add(a["x1"], a["x2"], a["s1"], a["s2"], a["m"], a["k"],
+                                                a["n"], a["y"], a["stream"])
+
+
+def test_int8_matmul_validation():
+    assert _qmm(k=0) == wq.WQ_ERR_SHAPE
+    assert _qmm(k=40) == wq.WQ_ERR_SHAPE                   # k % 16
+    assert _qmm(k=65536) == wq.WQ_ERR_SHAPE
+    assert _qmm(n=65536) == wq.WQ_ERR_SHAPE
+    assert _qmm(m=-1) == wq.WQ_ERR_SHAPE
+    assert _qmm(x1=None) == wq.WQ_ERR_NULLPTR
+    assert _qmm(s2=None) == wq.WQ_ERR_NULLPTR
+    assert _qmm(x2=FAKE2 + 8) == wq.WQ_ERR_SHAPE           # 16-byte operand rows
+    assert _qmm(y=FAKE + 0x40000002) == wq.WQ_ERR_SHAPE    # float alignment
+    assert _qmm(y=FAKE + 64) == wq.WQ_ERR_ALIAS            # y over x1
+    assert _qmm(m=0) == wq.WQ_OK and _qmm(n=0) == wq.WQ_OK

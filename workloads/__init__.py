@@ -194,3 +194,22 @@ def mx(m: int = 4096, k: int = 8192, n: int = 4096, seed: int = 0,
     sc = torch.from_numpy(g[4].integers(120, 127, size=(kb, n), dtype=np.uint8))
     y = torch.from_numpy(g[5].standard_normal((m, n)).astype(np.float32))
     return MXCase(x, smooth, w, codes, sc, y)
+
+
+@dataclass
+class I8Case:
+    w: torch.Tensor          # int8 (n, k): weight, stored transposed (K contiguous)
+    w_scale: torch.Tensor    # float32 (n), per channel
+    y: torch.Tensor          # float32 (m, n)
+
+
+def int8_gemm(m: int = 4096, k: int = 8192, n: int = 4096, seed: int = 0) -> I8Case:
+    """The INT8 consumer of the per-token quant output of ``mx``'s x: weight
+    int8 uniform in [-127, 127] stored (n, k); per-channel scales
+    U[0.001, 0.01] fp32; y ~ N(0,1) fp32 (m, n). x1 is the per-token INT8
+    quantization of ``mx(m, k, n).x * smooth`` (made on the device)."""
+    g = streams(seed + 1, 3)
+    w = torch.from_numpy(g[0].integers(-127, 128, size=(n, k), dtype=np.int8))
+    ws = torch.from_numpy(g[1].uniform(0.001, 0.01, size=(n,)).astype(np.float32))
+    y = torch.from_numpy(g[2].standard_normal((m, n)).astype(np.float32))
+    return I8Case(w, ws, y)
