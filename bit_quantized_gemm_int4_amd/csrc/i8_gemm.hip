@@ -8,44 +8,71 @@
 // s = fl(scale1 * scale2), t = fl(fl(acc) * s), y = fl(y + t).
 //
 // Tile: 256 (m) x 256 (n) per workgroup of 8 waves, each wave 64 x 128 (4 x 8
-// MFMA tiles), two waves per SIMD. Per 128-deep K step the workgroup moves
-// 32 KiB of x1 and 32 KiB of x2 into LDS by buffer->LDS DMA, double-buffered;
-// both operands are K-contiguous rows, so every MFMA operand is one 16-byte
-// LDS read and nothing is unpacked. The accumulators need no VALU work inside
-// the K loop and live wherever the compiler puts them.
+// MFMA tiles), two waves per SIMD. K advances 64 bytes per step; each step's
+// operands (16 KiB of x1 and 16 KiB of x2) come into LDS by buffer->LDS DMA
+// into a ring of four stages, issued about two and a half steps ahead so the
+// fetch latency hides behind the MFMAs of the steps between. Both operands are K-contiguous rows, so
+// every MFMA operand is one 16-byte LDS read and nothing is unpacked; each
+// step's operands are read into registers during the second half of the
+// previous step's MFMAs.
 #include "wq_device.h"
 #include "wq_internal.h"
 
 namespace wq {
 namespace {
 
-constexpr int I8_BM = 256, I8_BN = 256, I8_BK = 128;
-constexpr int I8_SLAB = 256 * I8_BK;   // one operand's LDS stage: 32 KiB
+constexpr int I8_BM = 256, I8_BN = 256, I8_BK = 64;
+constexpr int I8_STAGE = 256 * I8_BK;   // one operand's LDS stage: 16 KiB
 
-// LDS rows are 128 bytes (one K step of one row / column), 16-byte chunks.
-// Chunk c of row r sits at position c ^ ((r >> 1) & 7): two rows share a
+// LDS rows are 64 bytes (one step of one row / column), four 16-byte chunks.
+// Chunk c of row r sits at position c ^ ((r >> 2) & 3): four rows share a
 // 256-byte bank row, so the 16 rows of one MFMA operand read (one chunk) land
 // in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int i8_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int i8_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// One operand stage (256 rows x 128 K bytes) by 32 DMA instructions of 1 KiB
-// (8 rows); wave w issues 4w + j, lane l fills row 8 (4w + j) + l / 8 at
-// position l % 8, fetching logical chunk (l % 8) ^ ((row >> 1) & 7). Rows
-// past `rows` and chunks past k read zeros (offset BUF_OOB): they add nothing.
-__device__ __forceinline__ void i8_dma(__amdgpu_buffer_rsrc_t rs, int rows, int64_t k, int64_t k0,
-                                       uint8_t* buf) {
+// Per-lane DMA addressing of one operand: 256 rows x 64 K bytes per stage by
+// 16 DMA instructions of 1 KiB (16 rows); wave w issues 2w + j, lane l fills
+// row 16 (2w + j) + l / 4 at position l % 4, fetching logical chunk
+// (l % 4) ^ ((row >> 2) & 3). `base` is the byte offset of that chunk at K 0
+// (BUF_OOB for rows past the operand), `klim` the step origins k0 < klim for
+// which the chunk lies inside K; outside, the lane reads zeros.
+struct I8Dma {
+  uint32_t base[2];
+  int klim[2];
+};
+
+__device__ __forceinline__ I8Dma i8_dma_setup(int rows, int64_t k) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
+  I8Dma d;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 8 * (4 * wave + j) + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    const int64_t kk = k0 + 16 * c;
-    const uint32_t off = row < rows && kk < k ? (uint32_t)(row * k + kk) : BUF_OOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (4 * wave + j) * 1024), 16, off, 0, 0, 0);
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wave + j) + (lane >> 2);
+    const int c = i8_pos(row, lane & 3);
+    d.base[j] = row < rows ? (uint32_t)(row * k + 16 * c) : BUF_OOB;
+    d.klim[j] = (int)k - 16 * c;
   }
+  return d;
+}
+
+// DMA instruction j (0 or 1) of this wave for one operand stage starting at
+// K offset k0.
+__device__ __forceinline__ void i8_dma(__amdgpu_buffer_rsrc_t rs, const I8Dma& d, int j, int k0, uint8_t* buf) {
+  const uint32_t off = k0 < d.klim[j] ? d.base[j] + (uint32_t)k0 : BUF_OOB;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (2 * wave_id() + j) * 1024), 16, off, 0, 0, 0);
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A workgroup barrier that orders LDS accesses only: the caller has already
+// waited for what must be complete (its own DMA and LDS reads), so the
+// buffer->LDS DMA of later stages stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 __global__ __launch_bounds__(512, 1) void i8_gemm_tile(const int8_t* __restrict__ x1,
                                                        const int8_t* __restrict__ x2t,
@@ -53,8 +80,8 @@ __global__ __launch_bounds__(512, 1) void i8_gemm_tile(const int8_t* __restrict_
                                                        const float* __restrict__ s2,
                                                        float* __restrict__ y, int64_t M, int64_t K,
                                                        int64_t N, int64_t tiles_m, int64_t tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t a0[I8_SLAB], a1[I8_SLAB];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[I8_SLAB], b1[I8_SLAB];
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[I8_STAGE], a1[I8_STAGE], a2[I8_STAGE], a3[I8_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[I8_STAGE], b1[I8_STAGE], b2[I8_STAGE], b3[I8_STAGE];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave & 3, wn = wave >> 2;       // 64-row and 128-column blocks of the tile
 
@@ -70,7 +97,10 @@ __global__ __launch_bounds__(512, 1) void i8_gemm_tile(const int8_t* __restrict_
   // tile-relative offsets stay below 2^31: 256 rows of at most 65535 bytes
   const __amdgpu_buffer_rsrc_t ra = buf_rsrc(x1 + m0 * K, (uint32_t)(rows_a * K));
   const __amdgpu_buffer_rsrc_t rb = buf_rsrc(x2t + n0 * K, (uint32_t)(rows_b * K));
-  const int steps = (int)((K + I8_BK - 1) / I8_BK);
+  const I8Dma da = i8_dma_setup(rows_a, K), db = i8_dma_setup(rows_b, K);
+  // steps rounded up to a multiple of the ring length; steps past K read
+  // zero stages and add nothing
+  const int steps = (int)((K + 4 * I8_BK - 1) / (4 * I8_BK)) * 4;
 
   i32x4 acc[4][8];
 #pragma unroll
@@ -78,47 +108,82 @@ __global__ __launch_bounds__(512, 1) void i8_gemm_tile(const int8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = (i32x4){0, 0, 0, 0};
 
-  i8_dma(ra, rows_a, K, 0, a0);
-  i8_dma(rb, rows_b, K, 0, b0);
-  wait_vm<0>();
-  __syncthreads();
-
   // lane roles of the 16x16x64 MFMA: operand row / column l % 16, lane group
-  // g = l / 16 takes 16 K bytes; substep h of a step covers K 64h .. 64h + 63,
-  // so group g reads logical chunk 4h + g of its row. A and B use the same
-  // assignment, so every K index of the step is multiplied exactly once.
+  // g = l / 16 takes 16 K bytes, logical chunk g of its row. A and B use the
+  // same assignment, so every K index of the step is multiplied exactly once.
+  // The rows a lane reads differ by multiples of 16, so its chunk position is
+  // the same for all of them.
   const int g = lane >> 4, r16 = lane & 15;
-  auto step = [&](int s, const uint8_t* acur, uint8_t* anxt, const uint8_t* bcur, uint8_t* bnxt) {
-    if (s + 1 < steps) {
-      i8_dma(ra, rows_a, K, (int64_t)(s + 1) * I8_BK, anxt);
-      i8_dma(rb, rows_b, K, (int64_t)(s + 1) * I8_BK, bnxt);
+  const int lds_off = r16 * I8_BK + 16 * i8_pos(r16, g);
+  // operand t of a step: t = 0 is A block 0, 1..8 B blocks 0..7, 9..11 A
+  // blocks 1..3 (the order the next step's MFMAs consume them)
+  auto read_op = [&](int t, const uint8_t* abuf, const uint8_t* bbuf, i32x4 (&av)[4], i32x4 (&bv)[8]) {
+    if (t == 0 || t >= 9) {
+      const int i = t == 0 ? 0 : t - 8;
+      av[i] = *reinterpret_cast<const i32x4*>(abuf + (64 * wm + 16 * i) * I8_BK + lds_off);
+    } else {
+      const int j = t - 1;
+      bv[j] = *reinterpret_cast<const i32x4*>(bbuf + (128 * wn + 16 * j) * I8_BK + lds_off);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      i32x4 av[4], bv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wm + 16 * i + r16;
-        av[i] = *reinterpret_cast<const i32x4*>(acur + r * I8_BK + 16 * i8_pos(r, 4 * h + g));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 128 * wn + 16 * j + r16;
-        bv[j] = *reinterpret_cast<const i32x4*>(bcur + r * I8_BK + 16 * i8_pos(r, 4 * h + g));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-    wait_vm<0>();            // this wave's DMA into the next buffers has landed
-    __syncthreads();
   };
-  for (int s = 0; s < steps; s += 2) {
-    step(s, a0, a1, b0, b1);
-    if (s + 1 < steps) step(s + 1, a1, a0, b1, b0);
+  auto mfma = [&](int i, int j, const i32x4 (&av)[4], const i32x4 (&bv)[8]) {
+    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: stages 0..2 in flight; stage 0 landed everywhere; its operands
+  // in registers
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    uint8_t* ab = st == 0 ? a0 : st == 1 ? a1 : a2;
+    uint8_t* bb = st == 0 ? b0 : st == 1 ? b1 : b2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      i8_dma(ra, da, j, st * I8_BK, ab);
+      i8_dma(rb, db, j, st * I8_BK, bb);
+    }
   }
+  wait_vm<8>();                      // this wave's stage 0 (in-order completion)
+  lds_barrier();
+  i32x4 pa[4], pb[8], qa[4], qb[8];
+#pragma unroll
+  for (int t = 0; t < 12; ++t) read_op(t, a0, b0, pa, pb);
+
+  // step s: the operands of stage s are in registers (cur); stage s + 3's
+  // buffers were last read before the previous barrier. The first half of the
+  // MFMAs carries the DMA of stage s + 3 (one instruction per slot, so no wave
+  // stalls on a full memory queue with MFMAs waiting behind it); then wait for
+  // this wave's DMA of stage s + 1 (stages s + 1 .. s + 3 are in flight, four
+  // instructions each, completing in order); the barrier makes stage s + 1
+  // visible; the second half carries the twelve reads of stage s + 1's
+  // operands (nxt). Every slot is fixed by a scheduling barrier.
+  auto step = [&](int s, uint8_t* adma, uint8_t* bdma, const uint8_t* anxt, const uint8_t* bnxt,
+                  const i32x4 (&ca)[4], const i32x4 (&cb)[8], i32x4 (&na)[4], i32x4 (&nb)[8]) {
+    const int kd = (s + 3) * I8_BK;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      mfma(t >> 3, t & 7, ca, cb);
+      if (t == 1) i8_dma(ra, da, 0, kd, adma);
+      if (t == 3) i8_dma(rb, db, 0, kd, bdma);
+      if (t == 5) i8_dma(ra, da, 1, kd, adma);
+      if (t == 7) i8_dma(rb, db, 1, kd, bdma);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<8>();
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      mfma(2 + (t >> 3), t & 7, ca, cb);
+      if (t < 12) read_op(t, anxt, bnxt, na, nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int s = 0; s < steps; s += 4) {
+    step(s, a3, b3, a1, b1, pa, pb, qa, qb);
+    step(s + 1, a0, b0, a2, b2, qa, qb, pa, pb);
+    step(s + 2, a1, b1, a3, b3, pa, pb, qa, qb);
+    step(s + 3, a2, b2, a0, b0, qa, qb, pa, pb);
+  }
+  wait_vm<0>();                      // the DMA of the stages past the end
 
   // epilogue: lane holds rows 4 g + r (r = 0..3) of column r16 in each 16x16
   // tile; y, the row scales and the column scales through buffer resources

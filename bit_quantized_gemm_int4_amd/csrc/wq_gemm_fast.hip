@@ -146,12 +146,15 @@ static_assert(32 * WD_EROW <= 16384, "epilogue staging must fit a wave's 16 KiB 
 // (v0 ^ 64j) + 8jk with v0 = (16w + lane/16) * 2k + 16 c0 (2k is a multiple
 // of 256, so the XOR only touches the chunk bits). The buffer resource
 // starts at the slab and ends after the tile's last row: rows past m read 0.
+__device__ __forceinline__ void wd_dma_a1(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf,
+                                          int j) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (4 * wave_id() + j) * 4 * WD_LROW), 16,
+                                           (v0 ^ (64u * j)) + 8u * j * k, 0, 0, 0);
+}
+
 __device__ __forceinline__ void wd_dma_a(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf) {
-  const int wave = wave_id();
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (4 * wave + j) * 4 * WD_LROW), 16,
-                                             (v0 ^ (64u * j)) + 8u * j * k, 0, 0, 0);
+  for (int j = 0; j < 4; ++j) wd_dma_a1(ra, v0, k, buf, j);
 }
 
 // Weight slab for the tile's 512 columns (64 bytes per column in GFX950_B
@@ -167,13 +170,16 @@ __device__ __forceinline__ uint32_t wd_b_v0(int wave, int lane) {
   return 4096u * wave + 64u * (lane >> 2) + 16u * ((lane & 3) ^ (lane >> 4));
 }
 
-__device__ __forceinline__ void wd_dma_b(__amdgpu_buffer_rsrc_t rb, uint32_t v0, uint8_t* buf) {
+__device__ __forceinline__ void wd_dma_b1(__amdgpu_buffer_rsrc_t rb, uint32_t v0, uint8_t* buf, int j) {
   // (the instruction's immediate offset would also move the LDS address, so
   // the 1 KiB step goes into the per-lane offset)
-  uint8_t* dst = buf + wave_id() * 4096;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(buf + wave_id() * 4096 + 1024 * j), 16,
+                                           v0 + 1024u * j, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wd_dma_b(__amdgpu_buffer_rsrc_t rb, uint32_t v0, uint8_t* buf) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + 1024 * j), 16, v0 + 1024u * j, 0, 0, 0);
+  for (int j = 0; j < 4; ++j) wd_dma_b1(rb, v0, buf, j);
 }
 
 // One 128-deep slab accumulated into acc: acc[i][f] += sum over the slab of
@@ -190,13 +196,16 @@ __device__ __forceinline__ void wd_dma_b(__amdgpu_buffer_rsrc_t rb, uint32_t v0,
 //  - pass 3 refills A fragment i for step c + 1 right after its last MFMA;
 //  - FIRST (the slab starts a quantization group): accumulator (i, f) is
 //    rescaled by ratio[f] = old scale / new scale one MFMA slot before its
-//    first MFMA of the slab.
+//    first MFMA of the slab;
+//  - dma(n), n = 0..7, issues the n-th DMA instruction of the next slab in
+//    slots 5 and 7 of the passes of step 0: spread between MFMAs, no wave
+//    stalls on a full memory queue with its MFMAs waiting behind the loads.
 // MASKED: per-lane masks mk / mc zero the weight operand of columns whose
 // group scale is zero (otherwise the unpack constants apply).
-template <int ACT, bool FIRST, bool MASKED>
+template <int ACT, bool FIRST, bool MASKED, typename Dma>
 __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf,
                                         const uint32_t (&mk)[4], const uint32_t (&mc)[4],
-                                        const float (&ratio)[4], f32x4 (&acc)[8][4]) {
+                                        const float (&ratio)[4], f32x4 (&acc)[8][4], const Dma& dma) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   // Step c gives lane group g = lane / 16 the 8 K values of dword
   // d = (c + g) % 4 of its 32-deep block (A chunk 4g + d), a rotation that
@@ -263,6 +272,7 @@ __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf
         if (unpacking && i < 5) unpack_piece(i, rw[uf], uf, bf[uf]);
         if (f == 1 && i == 5 && c + 1 < 4) rw[3] = b_at(3, c + 1);
         if (f == 3 && c + 1 < 4) av[i] = a_at(i, c + 1);
+        if (c == 0 && (i == 5 || i == 7)) dma(2 * f + (i == 7));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -287,12 +297,15 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
                         16u * (uint32_t)((lane & 15) ^ (lane >> 4));
   const uint32_t b_v0 = wd_b_v0(wave, lane);
   const int64_t slab_bytes = a.np * 64;
+  // (the slab after the last one gets empty resources: its DMA, issued
+  // unconditionally inside the last slab's MFMA stream, reads zeros and
+  // touches no memory)
   auto rsrc_a = [&](int sl) {
     return buf_rsrc(a.x1 + m0 * a.k + (int64_t)sl * WD_KS,
-                    (uint32_t)(rows_left * 2 * a.k - (int64_t)sl * 2 * WD_KS));
+                    sl < slabs ? (uint32_t)(rows_left * 2 * a.k - (int64_t)sl * 2 * WD_KS) : 0u);
   };
   auto rsrc_b = [&](int sl) {
-    return buf_rsrc(a.x2 + sl * slab_bytes + n0 * 64, (uint32_t)((a.np - n0) * 64));
+    return buf_rsrc(a.x2 + sl * slab_bytes + n0 * 64, sl < slabs ? (uint32_t)((a.np - n0) * 64) : 0u);
   };
   // Scales: lane's column of tile f is ncol0 + 16 f + lane % 16; a column
   // past n reads scale 0 (its weight operand is then zeroed and it is never
@@ -341,10 +354,11 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
   auto step = [&](int s, const uint8_t* acur, uint8_t* anxt, const uint8_t* wcur, uint8_t* wnxt) {
     const bool more = s + 1 < slabs;
     if (more && gpos == spg - 1) load_scales(gnext++, snxt);   // next slab starts a group
-    if (more) {
-      wd_dma_a(rsrc_a(s + 1), a_v0, k, anxt);
-      wd_dma_b(rsrc_b(s + 1), b_v0, wnxt);
-    }
+    const __amdgpu_buffer_rsrc_t ra_n = rsrc_a(s + 1), rb_n = rsrc_b(s + 1);
+    auto dma = [&](int n) {
+      if (n < 4) wd_dma_a1(ra_n, a_v0, k, anxt, n);
+      else wd_dma_b1(rb_n, b_v0, wnxt, n - 4);
+    };
     if (gpos == 0) {                                   // group start
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -366,7 +380,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
             for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
       }
     }
-    wd_slab<ACT, EVERY, MASKED>(acur, wcur, mk, mc, ratio, acc);
+    wd_slab<ACT, EVERY, MASKED>(acur, wcur, mk, mc, ratio, acc, dma);
     if (++gpos == spg) {
       gpos = 0;
       scur[0] = snxt[0];
