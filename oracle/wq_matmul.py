@@ -61,3 +61,31 @@ def wq_matmul_add_rmsnorm(x1, w, scale, offset, group_size, bias, residual,
     ms = np.mean(y * y, axis=1, keepdims=True)
     norm_out = y / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64).reshape(1, n)
     return mm, y, norm_out
+
+
+def weight_quant_matmul(x1, w, scale, offset, group_size, bias):
+    """The Formula's first line alone, ``mm = x1 @ (x2 * antiquantScale +
+    antiquantOffset) + bias`` (AllReduce the identity on one device): the
+    standalone weight-quantized matmul that the page's deprecation note names
+    as the replacement's first half. Returns float64 (rows, n)."""
+    q = np.asarray(w)
+    k, n = q.shape
+    x = np.asarray(x1, dtype=np.float64).reshape(-1, k)
+    mm = x @ dequantize_weight(q, scale, offset, group_size)
+    if bias is not None:
+        mm = mm + np.asarray(bias, dtype=np.float64).reshape(1, n)
+    return mm
+
+
+def add_rms_norm(x, residual, gamma, eps: float):
+    """The Formula's second and third lines alone (the replacement's second
+    half, AddRmsNorm): ``y = x + residual`` and ``normOut = y / RMS(y) *
+    gamma`` with ``RMS(y) = sqrt(mean of y^2 over the last dimension +
+    epsilon)``. ``x`` and ``residual`` are (rows, d) (or anything reshaping to
+    it), gamma (d). Returns (y, norm_out) as float64 (rows, d)."""
+    g = np.asarray(gamma, dtype=np.float64).reshape(-1)
+    d = g.size
+    y = (np.asarray(x, dtype=np.float64).reshape(-1, d)
+         + np.asarray(residual, dtype=np.float64).reshape(-1, d))
+    rms = np.sqrt(np.sum(y * y, axis=1, keepdims=True) / d + eps)
+    return y, y / rms * g.reshape(1, d)
