@@ -42,6 +42,7 @@ EXPORTS = (
     "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
     "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
     "wq_quant_matmul_inplace_add",
+    "wq_weight_quant_matmul_workspace_size", "wq_weight_quant_matmul", "wq_add_rms_norm",
     "wq_profile_enable", "wq_profile_read",
 )
 
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
             "wq_quant_matmul_inplace_add": (I, [P, P, P, P, I64, I64, I64, P, P]),
+            "wq_weight_quant_matmul_workspace_size": (S, [I64, I64, I64]),
+            "wq_weight_quant_matmul": (I, [P, I64, I64, I, P, I64, I, I, I, P, I64, I64, P, I64,
+                                           P, P, P, S, P]),
+            "wq_add_rms_norm": (I, [P, P, P, I64, I64, I, D, P, P, P]),
             "wq_profile_enable": (I, [I]),
             "wq_profile_read": (I, [P, I64, ctypes.POINTER(I64)]),
         }
@@ -167,6 +172,27 @@ def wq_matmul_add_rmsnorm(x1, m, k, act_dtype, x2, n, w_dtype, x2_layout, transp
     return _check(st, "wq_matmul_add_rmsnorm", check)
 
 
+def wq_weight_quant_matmul_workspace_size(m: int, k: int, n: int) -> int:
+    return lib().wq_weight_quant_matmul_workspace_size(m, k, n)
+
+
+def wq_weight_quant_matmul(x1, m, k, act_dtype, x2, n, w_dtype, x2_layout, transpose_x2,
+                           scale, scale_rows, scale_cols, offset, group_size, bias, out,
+                           workspace, workspace_size, stream=None, check=True) -> int:
+    st = lib().wq_weight_quant_matmul(
+        _ptr(x1), m, k, act_dtype, _ptr(x2), n, w_dtype, x2_layout, int(transpose_x2),
+        _ptr(scale), scale_rows, scale_cols, _ptr(offset), group_size, _ptr(bias), _ptr(out),
+        _ptr(workspace), workspace_size, _stream(stream))
+    return _check(st, "wq_weight_quant_matmul", check)
+
+
+def wq_add_rms_norm(x, residual, gamma, rows, cols, dtype, epsilon, y, norm_out, stream=None,
+                    check=True) -> int:
+    st = lib().wq_add_rms_norm(_ptr(x), _ptr(residual), _ptr(gamma), rows, cols, dtype,
+                               float(epsilon), _ptr(y), _ptr(norm_out), _stream(stream))
+    return _check(st, "wq_add_rms_norm", check)
+
+
 def mx_quant_matmul_inplace_add_workspace_size(m: int, k: int, n: int) -> int:
     return lib().mx_quant_matmul_inplace_add_workspace_size(m, k, n)
 
@@ -257,3 +283,40 @@ def quant_matmul_inplace_add(x1: torch.Tensor, x2_t: torch.Tensor, x1_scale: tor
     n = x2_t.shape[0]
     wq_quant_matmul_inplace_add(x1, x2_t, x1_scale, x2_scale, m, k, n, y, stream)
     return y
+
+
+def weight_quant_matmul(x1: torch.Tensor, x2: torch.Tensor, k: int, n: int, w_dtype: int,
+                        scale: torch.Tensor, offset: Optional[torch.Tensor], group_size: int,
+                        bias: Optional[torch.Tensor], layout: int = WQ_LAYOUT_GFX950_B,
+                        transpose_x2: bool = False, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out = x1 @ (x2 * scale + offset) + bias, (m, n) in x1's dtype."""
+    m = x1.numel() // k
+    if scale.dim() == 2:
+        s_rows, s_cols = scale.shape
+    else:
+        s_rows, s_cols = 1, scale.numel()
+    if out is None:
+        out = torch.empty((m, n), dtype=x1.dtype, device=x1.device)
+    ws = wq_weight_quant_matmul_workspace_size(m, k, n)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=x1.device)
+    wq_weight_quant_matmul(x1, m, k, act_code(x1.dtype), x2, n, w_dtype, layout, transpose_x2,
+                           scale, s_rows, s_cols, offset, group_size, bias, out, workspace,
+                           workspace.numel(), stream)
+    return out
+
+
+def add_rms_norm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                 y: Optional[torch.Tensor] = None, norm_out: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Returns (y, norm_out): y = x + residual, norm_out = y / RMS(y) * gamma
+    over the last dimension."""
+    cols = gamma.numel()
+    rows = x.numel() // cols
+    if y is None:
+        y = torch.empty_like(x)
+    if norm_out is None:
+        norm_out = torch.empty_like(x)
+    wq_add_rms_norm(x, residual, gamma, rows, cols, act_code(x.dtype), eps, y, norm_out, stream)
+    return y, norm_out

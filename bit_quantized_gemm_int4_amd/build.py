@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_profile.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
-           "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip"]
+           "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip", "add_rmsnorm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -113,14 +113,14 @@ size_t wq_matmul_add_rmsnorm_workspace_size(int64_t m, int64_t k, int64_t n) {
   return wq::wq_workspace_bytes(m, k, n);
 }
 
-wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
-                                const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
-                                int transpose_x2, const void* antiquant_scale, int64_t scale_rows,
-                                int64_t scale_cols, const void* antiquant_offset,
-                                int64_t antiquant_group_size, const void* bias,
-                                const void* residual, const void* gamma, double epsilon, void* y,
-                                void* norm_out, void* workspace, size_t workspace_size,
-                                hipStream_t stream) {
+namespace {
+
+// Checks shared by the fused operator and the standalone matmul (the pages'
+// Constraints): dtypes, layouts, sizes and the scale granularity. Fills the
+// problem's dequant indexing.
+wq_status check_wq_common(int64_t m, int64_t k, wq_dtype act_dtype, int64_t n, wq_dtype w_dtype,
+                          wq_layout x2_layout, int transpose_x2, int64_t scale_rows,
+                          int64_t scale_cols, int64_t antiquant_group_size, wq::WqProblem& p) {
   // dtypes: x2 int8 or int4; every other input shares one dtype (Constraints)
   if (!is_act(act_dtype)) return WQ_ERR_DTYPE;
   if (w_dtype != WQ_INT4 && w_dtype != WQ_INT8) return WQ_ERR_DTYPE;
@@ -132,11 +132,9 @@ wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype a
   if (k < 1 || k > kMaxKN) return WQ_ERR_SHAPE;
   if (n < 0 || n > kMaxKN) return WQ_ERR_SHAPE;
   if (w_dtype == WQ_INT4 && x2_layout == WQ_LAYOUT_ND && (n % 2)) return WQ_ERR_SHAPE;
-  if (!std::isfinite(epsilon) || epsilon < 0) return WQ_ERR_SHAPE;
   // quantization granularity (Constraints): per tensor (1), per channel
   // (1, n) / (n), per group (ceil(k/G), n) with G in [32, k-1], G % 32 == 0.
   const int64_t G = antiquant_group_size;
-  wq::WqProblem p{};
   if (G != 0) {
     if (G < 32 || G % 32 != 0 || G > k - 1) return WQ_ERR_GROUP;
     if (scale_rows != (k + G - 1) / G || scale_cols != n) return WQ_ERR_GROUP;
@@ -154,6 +152,31 @@ wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype a
   } else {
     return WQ_ERR_GROUP;
   }
+  p.m = m;
+  p.k = k;
+  p.n = n;
+  p.bf16 = act_dtype == WQ_BF16;
+  p.w_bits = w_dtype == WQ_INT4 ? 4 : 8;
+  p.layout = x2_layout;
+  p.transpose_x2 = transpose_x2 != 0;
+  return WQ_OK;
+}
+
+}  // namespace
+
+wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
+                                const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
+                                int transpose_x2, const void* antiquant_scale, int64_t scale_rows,
+                                int64_t scale_cols, const void* antiquant_offset,
+                                int64_t antiquant_group_size, const void* bias,
+                                const void* residual, const void* gamma, double epsilon, void* y,
+                                void* norm_out, void* workspace, size_t workspace_size,
+                                hipStream_t stream) {
+  wq::WqProblem p{};
+  const wq_status st = check_wq_common(m, k, act_dtype, n, w_dtype, x2_layout, transpose_x2,
+                                       scale_rows, scale_cols, antiquant_group_size, p);
+  if (st != WQ_OK) return st;
+  if (!std::isfinite(epsilon) || epsilon < 0) return WQ_ERR_SHAPE;
   if (m == 0 || n == 0) return WQ_OK;                  // empty tensors (Constraints)
   if (!x1 || !x2 || !antiquant_scale || !residual || !gamma || !y || !norm_out)
     return WQ_ERR_NULLPTR;
@@ -191,15 +214,79 @@ wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype a
   p.norm_out = norm_out;
   p.workspace = workspace;
   p.workspace_size = workspace_size;
-  p.m = m;
-  p.k = k;
-  p.n = n;
-  p.bf16 = act_dtype == WQ_BF16;
-  p.w_bits = w_dtype == WQ_INT4 ? 4 : 8;
-  p.layout = x2_layout;
-  p.transpose_x2 = transpose_x2 != 0;
   p.eps = (float)epsilon;
   return from_hip(wq::launch_wq_matmul_add_rmsnorm(p, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t wq_weight_quant_matmul_workspace_size(int64_t m, int64_t k, int64_t n) {
+  if (m < 0 || k < 0 || n < 0) return 0;
+  return wq::wq_workspace_bytes(m, k, n);
+}
+
+wq_status wq_weight_quant_matmul(const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
+                                 const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
+                                 int transpose_x2, const void* antiquant_scale, int64_t scale_rows,
+                                 int64_t scale_cols, const void* antiquant_offset,
+                                 int64_t antiquant_group_size, const void* bias, void* out,
+                                 void* workspace, size_t workspace_size, hipStream_t stream) {
+  wq::WqProblem p{};
+  const wq_status st = check_wq_common(m, k, act_dtype, n, w_dtype, x2_layout, transpose_x2,
+                                       scale_rows, scale_cols, antiquant_group_size, p);
+  if (st != WQ_OK) return st;
+  if (m == 0 || n == 0) return WQ_OK;
+  if (!x1 || !x2 || !antiquant_scale || !out) return WQ_ERR_NULLPTR;
+  const size_t need = wq::wq_workspace_bytes(m, k, n);
+  if (!workspace || workspace_size < need) return WQ_ERR_WORKSPACE;
+  const void* ptrs[] = {x1, x2, antiquant_scale, antiquant_offset, bias, out, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return WQ_ERR_SHAPE;
+  const size_t mn2 = (size_t)(m * n) * 2;
+  const size_t wbytes = w_dtype == WQ_INT8 ? (size_t)(k * n)
+                                            : wq_pack_int4_bytes(k, n, x2_layout);
+  const size_t sbytes = (size_t)(scale_rows * scale_cols) * 2;
+  if (overlap(out, mn2, x1, (size_t)(m * k) * 2) || overlap(out, mn2, x2, wbytes) ||
+      overlap(out, mn2, antiquant_scale, sbytes) || overlap(out, mn2, antiquant_offset, sbytes) ||
+      overlap(out, mn2, bias, (size_t)n * 2) || overlap(out, mn2, workspace, need))
+    return WQ_ERR_ALIAS;
+  p.x1 = x1;
+  p.x2 = x2;
+  p.scale = antiquant_scale;
+  p.offset = antiquant_offset;
+  p.bias = bias;
+  p.residual = nullptr;             // read as zeros by every path
+  p.gamma = nullptr;
+  p.y = out;
+  p.norm_out = nullptr;             // no norm pass
+  p.workspace = workspace;
+  p.workspace_size = workspace_size;
+  p.eps = 0.f;
+  return from_hip(wq::launch_wq_matmul_add_rmsnorm(p, stream));
+}
+
+// ---------------------------------------------------------------------------
+wq_status wq_add_rms_norm(const void* x, const void* residual, const void* gamma, int64_t rows,
+                          int64_t cols, wq_dtype dtype, double epsilon, void* y, void* norm_out,
+                          hipStream_t stream) {
+  if (!is_act(dtype)) return WQ_ERR_DTYPE;
+  if (rows < 0 || rows > kMaxRows || cols < 1 || cols > kMaxKN) return WQ_ERR_SHAPE;
+  if (!std::isfinite(epsilon) || epsilon < 0) return WQ_ERR_SHAPE;
+  if (rows == 0) return WQ_OK;
+  if (!x || !residual || !gamma || !y || !norm_out) return WQ_ERR_NULLPTR;
+  const void* ptrs[] = {x, residual, gamma, y, norm_out};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return WQ_ERR_SHAPE;
+  const size_t b = (size_t)(rows * cols) * 2, gb = (size_t)cols * 2;
+  // y: exactly x or residual (in place), or apart from both; norm_out apart
+  // from everything
+  if ((y != x && overlap(y, b, x, b)) || (y != residual && overlap(y, b, residual, b)) ||
+      overlap(y, b, gamma, gb))
+    return WQ_ERR_ALIAS;
+  if (overlap(norm_out, b, x, b) || overlap(norm_out, b, residual, b) ||
+      overlap(norm_out, b, gamma, gb) || overlap(norm_out, b, y, b))
+    return WQ_ERR_ALIAS;
+  return from_hip(wq::launch_add_rmsnorm(x, residual, gamma, rows, cols, dtype == WQ_BF16,
+                                         (float)epsilon, y, norm_out, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -40,8 +40,9 @@ struct GemmArgs {
   int64_t group, s_row, s_col;
 };
 
-// Epilogue for one 16x16 MFMA tile held by a wave: y = acc + bias + residual,
-// stored rounded; returns the float32 y values (0 outside the matrix).
+// Epilogue for one 16x16 MFMA tile held by a wave: y = acc + bias + residual
+// (no residual: zero), stored rounded; returns the float32 y values (0
+// outside the matrix).
 template <int ACT>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x4& acc, int64_t row0,
                                               int64_t col, float yv[4]) {
@@ -54,7 +55,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const f32x4& ac
     float v = 0.f;
     if (cin && row < a.m) {
       const int64_t idx = row * a.n + col;
-      v = acc[i] + b + to_f32<ACT>(a.residual[idx]);
+      v = acc[i] + b + (a.residual ? to_f32<ACT>(a.residual[idx]) : 0.f);
       a.y[idx] = from_f32<ACT>(v);
     }
     yv[i] = v;
@@ -348,6 +349,7 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
     e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
   }
   if (e != hipSuccess) return e;
+  if (!p.norm_out) return hipSuccess;                 // the standalone matmul: no norm
   return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, 1, tiles, s)
                 : launch_finish<ACT_F16>(p, a, tiles, 1, tiles, s);
 }

@@ -202,8 +202,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const bool pair = (a.n & 1) == 0 && c1ok;       // y rows start 4-byte aligned
   const int64_t idx = orow * a.n + col0;
   // Unconditional buffer loads (an invalid element reads zero; no bias is a
-  // zero-size buffer), so nothing forces a wait before the stream is issued.
-  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual, (uint32_t)(a.m * a.n * 2));
+  // zero-size buffer, as is no residual), so nothing forces a wait before the
+  // stream is issued.
+  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual ? a.residual : a.x1, a.residual ? (uint32_t)(a.m * a.n * 2) : 0u);
   const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias ? a.bias : a.residual, a.bias ? (uint32_t)(a.n * 2) : 0u);
   const uint32_t r0 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c0ok ? (uint32_t)(idx * 2) : BUF_OOB, 0, 0);
   const uint32_t r1 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c1ok ? (uint32_t)(idx * 2 + 2) : BUF_OOB, 0, 0);

@@ -408,7 +408,9 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
   const int64_t col = ncol0 + lc;
   const bool vec = (a.n & 7) == 0 && col + 8 <= a.n;
   const int rows_here = (int)(a.m - m0 < WD_BM ? a.m - m0 : WD_BM);
-  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual + m0 * a.n, (uint32_t)(rows_here * a.n * 2));
+  // (no residual: an empty resource, every lane reads zeros)
+  const __amdgpu_buffer_rsrc_t rres = a.residual ? buf_rsrc(a.residual + m0 * a.n, (uint32_t)(rows_here * a.n * 2))
+                                                 : buf_rsrc(a.x1, 0u);
   auto load_res = [&](int qt, u32x4 (&rr)[4]) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -499,7 +501,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             if (col + e < a.n) {
-              const float yv = v[e] + bv[e] + to_f32<ACT>(a.residual[idx + e]);
+              const float yv = v[e] + bv[e] + (a.residual ? to_f32<ACT>(a.residual[idx + e]) : 0.f);
               ss = fmaf(yv, yv, ss);
               a.y[idx + e] = from_f32<ACT>(yv);
             }

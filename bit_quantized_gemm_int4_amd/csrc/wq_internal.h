@@ -28,10 +28,10 @@ struct WqProblem {
   const void* scale;
   const void* offset;   // may be null
   const void* bias;     // may be null
-  const void* residual;
+  const void* residual;  // null: zero (the standalone matmul)
   const void* gamma;
   void* y;
-  void* norm_out;
+  void* norm_out;       // null: no norm pass (the standalone matmul)
   void* workspace;
   size_t workspace_size;
   int64_t m, k, n;
@@ -47,6 +47,11 @@ struct WqProblem {
 };
 
 size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n);
+
+// AddRmsNorm on (rows, d) act-dtype rows: y = x + residual, normOut =
+// y * rstd * gamma (add_rmsnorm.hip).
+hipError_t launch_add_rmsnorm(const void* x, const void* residual, const void* gamma, int64_t rows,
+                              int64_t d, bool bf16, float eps, void* y, void* norm_out, hipStream_t s);
 hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s);
 
 // Fast GFX950_B INT4 path (group a multiple of 128, or per channel/tensor).

@@ -8,6 +8,8 @@
  *   wq_matmul_add_rmsnorm         aclnnWeightQuantMatmulAllReduceAddRmsNorm
  *                                 (single device: the AllReduce is the identity)
  *   mx_quant_matmul_inplace_add   aclnnQuantBatchMatmulInplaceAdd (mx)
+ *   wq_weight_quant_matmul        \ the unfused chain that the fused operator's
+ *   wq_add_rms_norm               / page names as its replacement
  *
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major
@@ -185,6 +187,55 @@ wq_status wq_matmul_add_rmsnorm(
     const void* bias, const void* residual, const void* gamma,
     double epsilon, void* y, void* norm_out,
     void* workspace, size_t workspace_size, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weight-quantized matmul alone (the first half of the unfused chain).
+ * aclnnWeightQuantMatmulAllReduceAddRmsNorm page: the deprecation note names
+ * a weight-quantized matmul (with AllReduce) followed by AddRmsNorm as the
+ * replacement; this is the Formula's first line on one device:
+ *     out = x1 @ (x2 * antiquantScale + antiquantOffset) + bias
+ * Every argument but the outputs means what it means for
+ * wq_matmul_add_rmsnorm (dtypes, layouts, scale shapes and group rules,
+ * limits, alignment); residual, gamma, epsilon and norm_out are absent.
+ *
+ * out         device (m, n) act_dtype, rounded once from the float32 sum; may
+ *             not overlap x1, x2, the scales, bias or the workspace.
+ * workspace   device, >= wq_weight_quant_matmul_workspace_size(m, k, n)
+ *             bytes, no initial contents needed.
+ * Errors: as wq_matmul_add_rmsnorm (WQ_ERR_ALIAS for an overlapping out).
+ * ---------------------------------------------------------------------- */
+size_t wq_weight_quant_matmul_workspace_size(int64_t m, int64_t k, int64_t n);
+wq_status wq_weight_quant_matmul(
+    const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
+    const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
+    int transpose_x2,
+    const void* antiquant_scale, int64_t scale_rows, int64_t scale_cols,
+    const void* antiquant_offset, int64_t antiquant_group_size,
+    const void* bias, void* out,
+    void* workspace, size_t workspace_size, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * AddRmsNorm (the second half of the unfused chain).
+ * aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula, last two lines:
+ *     y = x + residual
+ *     normOut = y / RMS(y) * gamma,  RMS(y) = sqrt(mean over the row of y^2 + epsilon)
+ *
+ * x, residual device (rows, cols) dtype (WQ_F16 or WQ_BF16); rows in
+ *             [0, 2^31 - 1] (0: nothing to do), cols in [1, 65535].
+ * gamma       device (cols) dtype.
+ * epsilon     finite, >= 0.
+ * y           device (rows, cols) dtype; may equal x or residual (in place)
+ *             but not overlap them otherwise.
+ * norm_out    device (rows, cols) dtype; may not overlap any other argument.
+ * Every pointer 16-byte aligned. The sum of squares uses the float32 y (one
+ * float32 addition of the two inputs); y is rounded to dtype once and
+ * normOut = y_rounded * rstd * gamma is rounded once, as in the fused
+ * operator.
+ * Errors: WQ_ERR_NULLPTR, WQ_ERR_SHAPE, WQ_ERR_DTYPE, WQ_ERR_ALIAS.
+ * ---------------------------------------------------------------------- */
+wq_status wq_add_rms_norm(const void* x, const void* residual, const void* gamma,
+                          int64_t rows, int64_t cols, wq_dtype dtype, double epsilon,
+                          void* y, void* norm_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * MX block-32 quantized matmul with in-place add.

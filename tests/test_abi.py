@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -210,3 +210,63 @@ def test_int8_matmul_validation():
     assert _qmm(y=FAKE + 0x40000002) == wq.WQ_ERR_SHAPE    # float alignment
     assert _qmm(y=FAKE + 64) == wq.WQ_ERR_ALIAS            # y over x1
     assert _qmm(m=0) == wq.WQ_OK and _qmm(n=0) == wq.WQ_OK
+
+
+def _wqbmm(**kw):
+    # the standalone matmul on the fused call's defaults (no residual, gamma,
+    # epsilon or norm_out); out where the fused call has y
+    m, k, n = kw.pop("m", 64), kw.pop("k", 256), kw.pop("n", 128)
+    a = dict(x1=FAKE, act=wq.WQ_BF16, x2=FAKE + 0x10000, w=wq.WQ_INT4,
+             layout=wq.WQ_LAYOUT_GFX950_B, tx2=0, scale=FAKE + 0x20000, srows=8, scols=n,
+             offset=None, group=32, bias=None, out=FAKE + 0x50000, ws=FAKE2,
+             ws_size=wq.wq_weight_quant_matmul_workspace_size(m, k, n))
+    a.update(kw)
+    return wq.lib().wq_weight_quant_matmul(
+        a["x1"], m, k, a["act"], a["x2"], n, a["w"], a["layout"], a["tx2"], a["scale"],
+        a["srows"], a["scols"], a["offset"], a["group"], a["bias"], a["out"], a["ws"],
+        a["ws_size"], 0)
+
+
+def test_weight_quant_matmul_validation():
+    assert wq.wq_weight_quant_matmul_workspace_size(64, 256, 128) == \
+        wq.wq_matmul_add_rmsnorm_workspace_size(64, 256, 128)
+    assert _wqbmm(act=wq.WQ_F32) == wq.WQ_ERR_DTYPE
+    assert _wqbmm(tx2=1) == wq.WQ_ERR_UNSUPPORTED
+    assert _wqbmm(k=0) == wq.WQ_ERR_SHAPE
+    assert _wqbmm(n=65536) == wq.WQ_ERR_SHAPE
+    assert _wqbmm(group=48, srows=6) == wq.WQ_ERR_GROUP
+    assert _wqbmm(m=0) == wq.WQ_OK
+    assert _wqbmm(out=None) == wq.WQ_ERR_NULLPTR
+    assert _wqbmm(ws=None) == wq.WQ_ERR_WORKSPACE
+    assert _wqbmm(out=FAKE + 0x50008) == wq.WQ_ERR_SHAPE             # misaligned
+    assert _wqbmm(out=FAKE + 0x10000) == wq.WQ_ERR_ALIAS             # out over x2
+    assert _wqbmm(out=FAKE2 + 0x100) == wq.WQ_ERR_ALIAS              # out over the workspace
+
+
+def _arn(**kw):
+    # five disjoint regions (each row block is 64 x 1024 x 2 = 0x20000 bytes)
+    a = dict(x=FAKE, res=FAKE + 0x100000, gamma=FAKE + 0x200000, rows=64, cols=1024,
+             dt=wq.WQ_BF16, eps=1e-6, y=FAKE + 0x300000, norm=FAKE + 0x400000)
+    a.update(kw)
+    return wq.lib().wq_add_rms_norm(a["x"], a["res"], a["gamma"], a["rows"], a["cols"], a["dt"],
+                                    a["eps"], a["y"], a["norm"], 0)
+
+
+def test_add_rms_norm_validation():
+    assert _arn(dt=wq.WQ_INT8) == wq.WQ_ERR_DTYPE
+    assert _arn(cols=0) == wq.WQ_ERR_SHAPE
+    assert _arn(cols=65536) == wq.WQ_ERR_SHAPE
+    assert _arn(rows=-1) == wq.WQ_ERR_SHAPE
+    assert _arn(eps=-1.0) == wq.WQ_ERR_SHAPE
+    assert _arn(eps=float("inf")) == wq.WQ_ERR_SHAPE
+    assert _arn(rows=0) == wq.WQ_OK
+    assert _arn(gamma=None) == wq.WQ_ERR_NULLPTR
+    assert _arn(x=FAKE + 2) == wq.WQ_ERR_SHAPE                       # misaligned
+    assert _arn(y=FAKE + 0x10) == wq.WQ_ERR_ALIAS                    # y partly over x
+    assert _arn(norm=FAKE + 0x100000) == wq.WQ_ERR_ALIAS             # norm_out == residual
+    assert _arn(norm=FAKE + 0x300000) == wq.WQ_ERR_ALIAS             # norm_out == y
+    assert _arn(norm=FAKE + 0x200000 - 0x10) == wq.WQ_ERR_ALIAS      # norm_out over gamma
+    assert _arn(y=FAKE + 0x200000 - 0x10) == wq.WQ_ERR_ALIAS         # y over gamma
+    # in place is allowed: y == x or y == residual pass every host check (not
+    # called here: a valid call would launch)
+

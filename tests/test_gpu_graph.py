@@ -219,3 +219,33 @@ def test_inplace_accumulators_replay():
         torch.cuda.synchronize()
         assert torch.equal(y_i8, seq[r + 1][0]), f"int8 replay {r}"
         assert torch.equal(y_mx, seq[r + 1][1]), f"mx replay {r}"
+
+
+def test_unfused_chain_replays():
+    note("graph: standalone matmul -> add_rms_norm (decode m=4)")
+    c = workloads.decode(4)
+    m, k, n = c.mkn
+    x1 = c.x1.to(DEV).reshape(m, k)
+    x2 = wq.pack_int4(c.w.to(DEV), B)
+    sc, off, bias = c.scale.to(DEV), c.offset.to(DEV), c.bias.to(DEV)
+    res, gam = c.residual.to(DEV).reshape(m, n), c.gamma.to(DEV)
+    mm = torch.empty((m, n), dtype=x1.dtype, device=DEV)
+    y, nrm = torch.empty_like(mm), torch.empty_like(mm)
+    ws = torch.empty(wq.wq_weight_quant_matmul_workspace_size(m, k, n), dtype=torch.uint8, device=DEV)
+
+    def fn():
+        wq.weight_quant_matmul(x1, x2, k, n, wq.WQ_INT4, sc, off, c.group_size, bias, out=mm,
+                               workspace=ws)
+        wq.add_rms_norm(mm, res, gam, c.eps, y=y, norm_out=nrm)
+    fn()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (mm, y, nrm)]
+    g = _capture(fn)
+    for r in range(3):
+        for t in (mm, y, nrm):
+            t.fill_(float("nan"))
+        _eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((mm, y, nrm), want):
+            assert torch.equal(a, b), f"replay {r}"
