@@ -6,10 +6,13 @@ torch's current stream:
   1. wq_pack_int4          prefill weight (8192, 8192) int32 -> GFX950_B
   2. wq_matmul_add_rmsnorm prefill W4A16 group 128 + AddRmsNorm, bf16,
                            x1 (4, 1024, 8192), x2 (8192, 8192)
-  3. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
-  4. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
-  5. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
-  6. wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 3's output)
+  3. wq_weight_quant_matmul   the unfused chain on row 2's inputs: the
+  4. wq_add_rms_norm          standalone matmul (4096, 8192) bf16, then
+                              AddRmsNorm of it with the residual
+  5. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
+  6. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
+  7. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
+  8. wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 5's output)
                            x INT8 weight (4096, 8192), per-token x per-channel
 Every operator is timed with HIP events around its launch(es); the library
 also times its contraction kernels (the prefill MFMA tile, the MX GEMM, the
@@ -41,7 +44,8 @@ PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (the E4M3 x E2M1 MX rate)
 PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rows whose call launches one contraction kernel that the library times
-CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "mx_matmul_inplace_add": "mx_gemm_tile",
+CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "weight_quant_matmul": "gemm_b_wide",
+                    "mx_matmul_inplace_add": "mx_gemm_tile",
                     "quant_matmul_inplace_add_int8": "i8_gemm_tile"}
 COPY_BYTES = 256 << 20         # calibration copy (--only copy)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
@@ -156,6 +160,18 @@ def main():
                                  scale, s_rows, s_cols, offset, pf.group_size, bias, residual,
                                  gamma, pf.eps, y, norm, ws, ws_n)
 
+    # the unfused chain on the same inputs: standalone matmul, then AddRmsNorm
+    mm_out = torch.empty((M, N), dtype=x1.dtype, device=dev)
+    y2, norm2 = torch.empty_like(mm_out), torch.empty_like(mm_out)
+
+    def op_wqbmm():
+        wq.wq_weight_quant_matmul(x1, M, K, wq.WQ_BF16, x2, N, wq.WQ_INT4, wq.WQ_LAYOUT_GFX950_B, 0,
+                                  scale, s_rows, s_cols, offset, pf.group_size, bias, mm_out, ws,
+                                  ws_n)
+
+    def op_arn():
+        wq.wq_add_rms_norm(mm_out, residual, gamma, M, N, wq.WQ_BF16, pf.eps, y2, norm2)
+
     def op_quant_tok():
         wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_INT8, 0, 0, q8, q8s)
 
@@ -175,6 +191,9 @@ def main():
         ("pack", op_pack, 0, K * N * 4 + x2.numel(), "hbm"),
         ("wq_matmul_add_rmsnorm", op_wq, 2 * M * N * K,
          x1.numel() * 2 + x2.numel() + 2 * scale.numel() * 2 + N * 2 * 2 + 3 * M * N * 2, "mfma"),
+        ("weight_quant_matmul", op_wqbmm, 2 * M * N * K,
+         x1.numel() * 2 + x2.numel() + 2 * scale.numel() * 2 + N * 2 + M * N * 2, "mfma"),
+        ("add_rms_norm", op_arn, 0, 4 * M * N * 2 + N * 2, "hbm"),
         ("dynamic_quant_int8", op_quant_tok, 0, MM * MK * 2 + MK * 2 + MM * MK + MM * 4, "hbm"),
         ("dynamic_quant_mx", op_quant_mx, 0, MM * MK * 2 + MK * 2 + MM * MK + s1.numel(), "hbm"),
         ("mx_matmul_inplace_add", op_mx, 2 * MM * MN * MK,
@@ -239,7 +258,7 @@ def main():
             d["kernel"] = CONTRACTION_ROWS[name]
             d["kernel_ms"] = round(km, 5)
             d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
-        peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS,
+        peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS, "weight_quant_matmul": PEAK_BF16_TFLOPS,
                 "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS}.get(name, PEAK_FP8_TFLOPS)
         d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
                                   else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
@@ -357,6 +376,43 @@ def main():
                                          "ms": round(mm_ms, 5),
                                          "TFLOP/s": round(2 * M * N * K / mm_ms / 1e9, 1)}
         del xa, wb
+
+        def vendor_ceiling(name, what, flop, make):
+            # a vendor GEMM through torch (hipBLASLt); reported, not required
+            try:
+                fn = make()
+                for _ in range(5):
+                    fn()
+                evs = []
+                for _ in range(20):
+                    a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a0.record(stream)
+                    fn()
+                    b0.record(stream)
+                    evs.append((a0, b0))
+                torch.cuda.synchronize()
+                t = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+                ceilings[name] = {"what": what, "ms": round(t, 5), "TFLOP/s": round(flop / t / 1e9, 1)}
+            except Exception as e:               # not offered by this torch build
+                ceilings[name] = {"what": what, "unavailable": str(e).splitlines()[0][:160]}
+
+        # dense INT8 (int32 out) and FP8 E4M3 (bf16 out) at the INT8 / MX rows' shape
+        def make_i8():
+            a8 = torch.randint(-127, 128, (MM, MK), dtype=torch.int8, device=dev)
+            b8 = torch.randint(-127, 128, (MN, MK), dtype=torch.int8, device=dev).t()
+            return lambda: torch._int_mm(a8, b8)
+
+        def make_f8():
+            af = torch.randn(MM, MK, device=dev).to(torch.float8_e4m3fn)
+            bf = torch.randn(MN, MK, device=dev).to(torch.float8_e4m3fn).t()
+            one = torch.ones((), dtype=torch.float32, device=dev)
+            return lambda: torch._scaled_mm(af, bf, one, one, out_dtype=torch.bfloat16)
+
+        vendor_ceiling("dense_int8_matmul", f"torch._int_mm int8 {MM}x{MK}x{MN} (hipBLASLt)",
+                       2 * MM * MN * MK, make_i8)
+        vendor_ceiling("dense_fp8_matmul", f"torch._scaled_mm e4m3 {MM}x{MK}x{MN} (hipBLASLt)",
+                       2 * MM * MN * MK, make_f8)
+        torch.cuda.empty_cache()
         # HBM: a device copy far larger than the 256 MB last-level cache
         cb = 512 << 20
         src = torch.empty(cb, dtype=torch.uint8, device=dev).fill_(3)
