@@ -71,3 +71,29 @@ def mx_quant_matmul_inplace_add(x1_t_codes, x2_codes, scale1, scale2, y):
         block_sum = a[:, sl] @ b[sl, :]
         out += block_sum * (s1[:, j:j + 1] * s2[j:j + 1, :])
     return out
+
+
+def mxfp4_quant_matmul_inplace_add(x1_codes, x2_codes, scale1, scale2, y):
+    """The same Formula (mx quantization) with both operands MXFP4:
+    x1_codes (M, K) E2M1 codes (0..15), stored row-major (not transposed: the
+    layout in which the block-32 dynamic quant writes E2M1 activations, K
+    contiguous); x2_codes (K, N) E2M1 codes; scale1 (M, ceil(K/32)) and
+    scale2 (ceil(K/32), N) E8M0 codes; y (M, N). Returns the updated y as
+    float64. Every slice sum is exact in float64 (products are multiples of
+    2^-2 below 2^6), so only the accumulation over slices and into y rounds."""
+    a = e2m1_decode(np.asarray(x1_codes))               # (M, K)
+    b = e2m1_decode(np.asarray(x2_codes))               # (K, N)
+    s1 = e8m0_decode(scale1)
+    s2 = e8m0_decode(scale2)
+    m, k = a.shape
+    if b.shape[0] != k:
+        raise ValueError("x1 is (M, K) and x2 is (K, N)")
+    n = b.shape[1]
+    k_loops = -(-k // 32)
+    if s1.shape != (m, k_loops) or s2.shape != (k_loops, n):
+        raise ValueError("scale shapes must be (M, ceil(K/32)) and (ceil(K/32), N)")
+    out = np.array(y, dtype=np.float64, copy=True)
+    for j in range(k_loops):
+        sl = slice(32 * j, min(k, 32 * j + 32))
+        out += (a[:, sl] @ b[sl, :]) * (s1[:, j:j + 1] * s2[j:j + 1, :])
+    return out

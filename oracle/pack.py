@@ -98,3 +98,29 @@ def unpack_int4_gfx950b(packed, k: int, n: int, signed: bool = True) -> np.ndarr
     full = t.transpose(0, 2, 3, 4, 1).reshape(kp, np_)
     out = full[:k, :n]
     return np.where(out >= 8, out - 16, out) if signed else out
+
+
+def pack_float_e2m1(w, layout: str = "gfx950b", transpose: bool = False) -> np.ndarray:
+    """FLOAT -> tightly packed FLOAT4_E2M1 (aclnnConvertWeightToINT4Pack page:
+    on the newer chips the pack also takes FLOAT weights and writes packed
+    E2M1). ``w`` is (k, n) float32 (or (n, k) with ``transpose``).
+
+    Reading: each value goes to the nearest E2M1 value, ties to even, the sign
+    of zero kept; magnitudes beyond 6 (the largest E2M1) saturate to +-6.
+    NaN is outside the contract. The codes are then packed exactly as INT4
+    codes are (``layout`` "nd": (k, n/2) bytes, even column low; "gfx950b")."""
+    from .formats import E2M1_MAX, e2m1_encode
+    v = np.asarray(w, dtype=np.float64)
+    if np.any(np.isnan(v)):
+        raise ValueError("NaN has no E2M1 code")
+    if transpose:
+        v = v.T
+    k, n = v.shape
+    codes = e2m1_encode(np.clip(v, -E2M1_MAX, E2M1_MAX)).astype(np.int64)
+    if layout == "nd":
+        if n % 2:
+            raise ValueError("the packed axis must have even length")
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    if layout == "gfx950b":
+        return pack_codes_gfx950b(codes, k, n)
+    raise ValueError(layout)
