@@ -14,6 +14,9 @@ torch's current stream:
   7. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
   8. wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 5's output)
                            x INT8 weight (4096, 8192), per-token x per-channel
+  9. wq_dynamic_quant      MX E2M1 (row-major) + E8M0 of the same x
+ 10. mx_fp4_quant_matmul_inplace_add  y (4096, 4096) fp32 += E2M1 (row 9's
+                           output) x row 7's E2M1 weight, at the FP4 rate
 Every operator is timed with HIP events around its launch(es); the library
 also times its contraction kernels (the prefill MFMA tile, the MX GEMM, the
 decode weight stream) with event pairs on their own stream (wq_profile_*).
@@ -42,11 +45,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (the E4M3 x E2M1 MX rate)
 PEAK_INT8_TOPS = 5033.2        # MI355X dense int8 MFMA
+PEAK_FP4_TFLOPS = 10066.3      # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rows whose call launches one contraction kernel that the library times
 CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "weight_quant_matmul": "gemm_b_wide",
                     "mx_matmul_inplace_add": "mx_gemm_tile",
-                    "quant_matmul_inplace_add_int8": "i8_gemm_tile"}
+                    "quant_matmul_inplace_add_int8": "i8_gemm_tile",
+                    "mxfp4_matmul_inplace_add": "mx4_gemm_tile"}
 COPY_BYTES = 256 << 20         # calibration copy (--only copy)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
 
@@ -147,6 +152,11 @@ def main():
     s2 = mxc.x2_scale.to(dev)
     ymx = mxc.y.to(dev)
     del mxc
+    x1f4 = torch.empty((MM, MK // 2), dtype=torch.uint8, device=dev)
+    s1f4 = torch.empty((MM, MK // 32), dtype=torch.uint8, device=dev)
+    yf4 = ymx.clone()
+    ws4_n = wq.mx_fp4_quant_matmul_inplace_add_workspace_size(MM, MK, MN)
+    ws4 = torch.empty(ws4_n, dtype=torch.uint8, device=dev)
     i8c = workloads.int8_gemm(MM, MK, MN)
     w8t, w8s, y8 = i8c.w.to(dev), i8c.w_scale.to(dev), i8c.y.to(dev)
     del i8c
@@ -182,6 +192,13 @@ def main():
         wq.mx_quant_matmul_inplace_add(x1q, x2mx, wq.WQ_LAYOUT_GFX950_B, s1, s2, MM, MK, MN, 1, 0,
                                        wq.MX_GROUP_SIZE, ymx)
 
+    def op_quant_f4():
+        wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_FP4_E2M1, 32, 0, x1f4, s1f4)
+
+    def op_f4():
+        wq.mx_fp4_quant_matmul_inplace_add(x1f4, x2mx, wq.WQ_LAYOUT_GFX950_B, s1f4, s2, MM, MK, MN,
+                                           wq.MX_GROUP_SIZE, yf4, ws4, ws4_n)
+
     def op_i8():
         # the A8W8 chain's GEMM on the per-token INT8 output of op_quant_tok
         wq.wq_quant_matmul_inplace_add(q8, w8t, q8s, w8s, MM, MK, MN, y8)
@@ -200,6 +217,9 @@ def main():
          x1q.numel() + x2mx.numel() + s1.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
         ("quant_matmul_inplace_add_int8", op_i8, 2 * MM * MN * MK,
          MM * MK + MN * MK + MM * 4 + MN * 4 + 2 * MM * MN * 4, "mfma"),
+        ("dynamic_quant_mx_e2m1", op_quant_f4, 0, MM * MK * 2 + MK * 2 + MM * MK // 2 + s1f4.numel(), "hbm"),
+        ("mxfp4_matmul_inplace_add", op_f4, 2 * MM * MN * MK,
+         x1f4.numel() + x2mx.numel() + s1f4.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
     ]
     rows = [r for r in rows if want(r[0])]
     if "copy" in only:
@@ -259,7 +279,8 @@ def main():
             d["kernel_ms"] = round(km, 5)
             d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
         peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS, "weight_quant_matmul": PEAK_BF16_TFLOPS,
-                "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS}.get(name, PEAK_FP8_TFLOPS)
+                "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS,
+                "mxfp4_matmul_inplace_add": PEAK_FP4_TFLOPS}.get(name, PEAK_FP8_TFLOPS)
         d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
                                   else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
         out_rows[name] = d

@@ -37,11 +37,12 @@ MX_GROUP_SIZE = 32 | (1 << 16) | (1 << 32)
 
 EXPORTS = (
     "wq_status_string", "wq_abi_version",
-    "wq_pack_int4_bytes", "wq_pack_int4",
+    "wq_pack_int4_bytes", "wq_pack_int4", "wq_pack_fp4",
     "wq_dynamic_quant",
     "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
     "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
     "wq_quant_matmul_inplace_add",
+    "mx_fp4_quant_matmul_inplace_add_workspace_size", "mx_fp4_quant_matmul_inplace_add",
     "wq_weight_quant_matmul_workspace_size", "wq_weight_quant_matmul", "wq_add_rms_norm",
     "wq_profile_enable", "wq_profile_read",
 )
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "wq_abi_version": (I, []),
             "wq_pack_int4_bytes": (S, [I64, I64, I]),
             "wq_pack_int4": (I, [P, I64, I64, I, I, P, P]),
+            "wq_pack_fp4": (I, [P, I64, I64, I, I, P, P]),
             "wq_dynamic_quant": (I, [P, I, I64, I64, P, I, I64, I, P, P, P]),
             "wq_matmul_add_rmsnorm_workspace_size": (S, [I64, I64, I64]),
             "wq_matmul_add_rmsnorm": (I, [P, I64, I64, I, P, I64, I, I, I, P, I64, I64, P, I64,
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
             "wq_quant_matmul_inplace_add": (I, [P, P, P, P, I64, I64, I64, P, P]),
+            "mx_fp4_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
+            "mx_fp4_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I64, P, P, S, P]),
             "wq_weight_quant_matmul_workspace_size": (S, [I64, I64, I64]),
             "wq_weight_quant_matmul": (I, [P, I64, I64, I, P, I64, I, I, I, P, I64, I64, P, I64,
                                            P, P, P, S, P]),
@@ -92,10 +96,14 @@ def lib() -> ctypes.CDLL:
 
 
 def _ptr(t) -> Optional[int]:
+    """A tensor's address for the C ABI, which reads every tensor as dense
+    row-major memory: a strided view is refused, not reinterpreted."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError("libwq takes contiguous tensors (call .contiguous() first)")
     return t.data_ptr()
 
 
@@ -170,6 +178,23 @@ def wq_matmul_add_rmsnorm(x1, m, k, act_dtype, x2, n, w_dtype, x2_layout, transp
         _ptr(residual), _ptr(gamma), float(epsilon), _ptr(y), _ptr(norm_out),
         _ptr(workspace), workspace_size, _stream(stream))
     return _check(st, "wq_matmul_add_rmsnorm", check)
+
+
+def wq_pack_fp4(weight, k, n, transpose, layout, out, stream=None, check=True) -> int:
+    st = lib().wq_pack_fp4(_ptr(weight), k, n, int(transpose), layout, _ptr(out), _stream(stream))
+    return _check(st, "wq_pack_fp4", check)
+
+
+def mx_fp4_quant_matmul_inplace_add_workspace_size(m: int, k: int, n: int) -> int:
+    return lib().mx_fp4_quant_matmul_inplace_add_workspace_size(m, k, n)
+
+
+def mx_fp4_quant_matmul_inplace_add(x1, x2, x2_layout, x1_scale, x2_scale, m, k, n, group_size, y,
+                                    workspace, workspace_size, stream=None, check=True) -> int:
+    st = lib().mx_fp4_quant_matmul_inplace_add(
+        _ptr(x1), _ptr(x2), x2_layout, _ptr(x1_scale), _ptr(x2_scale), m, k, n, group_size, _ptr(y),
+        _ptr(workspace), workspace_size, _stream(stream))
+    return _check(st, "mx_fp4_quant_matmul_inplace_add", check)
 
 
 def wq_weight_quant_matmul_workspace_size(m: int, k: int, n: int) -> int:
@@ -320,3 +345,31 @@ def add_rms_norm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, e
         norm_out = torch.empty_like(x)
     wq_add_rms_norm(x, residual, gamma, rows, cols, act_code(x.dtype), eps, y, norm_out, stream)
     return y, norm_out
+
+
+def pack_fp4(weight: torch.Tensor, layout: int = WQ_LAYOUT_GFX950_B, transpose: bool = False,
+             stream=None) -> torch.Tensor:
+    """FLOAT -> packed E2M1 codes; ``weight`` float32 (k, n), or (n, k) with
+    ``transpose``."""
+    if transpose:
+        n, k = weight.shape
+    else:
+        k, n = weight.shape
+    out = torch.empty(wq_pack_int4_bytes(k, n, layout), dtype=torch.uint8, device=weight.device)
+    wq_pack_fp4(weight, k, n, transpose, layout, out, stream)
+    return out
+
+
+def mxfp4_matmul_inplace_add(x1: torch.Tensor, x2_packed: torch.Tensor, x1_scale: torch.Tensor,
+                             x2_scale: torch.Tensor, y: torch.Tensor, m: int, k: int, n: int,
+                             group_size: int = MX_GROUP_SIZE, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """y += the MXFP4 x MXFP4 block-32 product; x1 (m, k/2) packed E2M1,
+    x2 GFX950_B E2M1."""
+    ws = mx_fp4_quant_matmul_inplace_add_workspace_size(m, k, n)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=y.device)
+    mx_fp4_quant_matmul_inplace_add(x1, x2_packed, WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n,
+                                    group_size, y, workspace, workspace.numel(), stream)
+    return y
+

@@ -18,7 +18,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_profile.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
-           "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip", "add_rmsnorm.hip"]
+           "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip", "add_rmsnorm.hip",
+           "mx4_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -43,7 +44,8 @@ FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 
 # Sources with MFMA kernels: their device assembly is checked for MFMA
 # destinations that partially overlap a source operand (codegen_check).
-MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip"]
+MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip",
+                "mx4_gemm.hip"]
 
 
 def _compile(src: str) -> str:

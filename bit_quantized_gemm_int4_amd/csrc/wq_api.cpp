@@ -57,8 +57,11 @@ size_t wq_pack_int4_bytes(int64_t k, int64_t n, wq_layout layout) {
   return 0;
 }
 
-wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n, int transpose,
-                       wq_layout layout, void* out, hipStream_t stream) {
+namespace {
+
+// Both packs: the same sizes, limits and layouts (32-bit inputs either way).
+wq_status pack_checked(const void* weight, int64_t k, int64_t n, int transpose, wq_layout layout,
+                       void* out, hipStream_t stream, bool fp4) {
   if (layout != WQ_LAYOUT_ND && layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
   if (k < 0 || n < 0) return WQ_ERR_SHAPE;
   if (layout == WQ_LAYOUT_ND && (n % 2)) return WQ_ERR_SHAPE;
@@ -70,8 +73,20 @@ wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n, int transpos
   if (!weight || !out) return WQ_ERR_NULLPTR;
   if (!aligned16(out)) return WQ_ERR_SHAPE;
   if (overlap(weight, (size_t)(k * n) * 4, out, wq_pack_int4_bytes(k, n, layout))) return WQ_ERR_ALIAS;
-  return from_hip(wq::launch_pack_int4(weight, k, n, transpose != 0, layout,
-                                       static_cast<uint8_t*>(out), stream));
+  return from_hip(wq::launch_pack_int4(static_cast<const int32_t*>(weight), k, n, transpose != 0,
+                                       layout, static_cast<uint8_t*>(out), stream, fp4));
+}
+
+}  // namespace
+
+wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n, int transpose,
+                       wq_layout layout, void* out, hipStream_t stream) {
+  return pack_checked(weight, k, n, transpose, layout, out, stream, false);
+}
+
+wq_status wq_pack_fp4(const float* weight, int64_t k, int64_t n, int transpose, wq_layout layout,
+                      void* out, hipStream_t stream) {
+  return pack_checked(weight, k, n, transpose, layout, out, stream, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -351,6 +366,48 @@ wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const floa
   wq::I8Problem p{static_cast<const int8_t*>(x1), static_cast<const int8_t*>(x2), x1_scale, x2_scale,
                   y, m, k, n};
   return from_hip(wq::launch_i8_matmul(p, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t mx_fp4_quant_matmul_inplace_add_workspace_size(int64_t m, int64_t k, int64_t n) {
+  if (m < 0 || k < 0 || n < 0) return 0;
+  return wq::mx4_workspace_bytes(m, k, n);
+}
+
+wq_status mx_fp4_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout x2_layout,
+                                          const uint8_t* x1_scale, const uint8_t* x2_scale,
+                                          int64_t m, int64_t k, int64_t n, int64_t group_size,
+                                          float* y, void* workspace, size_t workspace_size,
+                                          hipStream_t stream) {
+  if (x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
+  if (m < 0 || n < 0 || m > kMaxRows || n > kMaxKN) return WQ_ERR_SHAPE;
+  // whole 32-slices, so every x1 row is whole 16-byte chunks
+  if (k < 1 || k > kMaxKN || (k % 32)) return WQ_ERR_SHAPE;
+  // groupSize as for the mx mode: only (K, N, M) = (32, 1, 1), zero fields inferred
+  if (group_size < 0 || (group_size >> 48) != 0) return WQ_ERR_GROUP;
+  const int64_t gk = group_size & 0xFFFF, gn = (group_size >> 16) & 0xFFFF,
+                gm = (group_size >> 32) & 0xFFFF;
+  if ((gk != 0 && gk != 32) || (gn != 0 && gn != 1) || (gm != 0 && gm != 1)) return WQ_ERR_GROUP;
+  if (m == 0 || n == 0) return WQ_OK;
+  if (!x1 || !x2 || !x1_scale || !x2_scale || !y) return WQ_ERR_NULLPTR;
+  const size_t need = wq::mx4_workspace_bytes(m, k, n);
+  if (!workspace || workspace_size < need) return WQ_ERR_WORKSPACE;
+  if (!aligned16(x1) || !aligned16(x2) || !aligned16(y) || !aligned16(workspace)) return WQ_ERR_SHAPE;
+  // the weight and its per-step offsets stay below the 2 GiB buffer bound
+  const size_t wbytes = wq_pack_int4_bytes(k, n, WQ_LAYOUT_GFX950_B);
+  if (wbytes >= ((size_t)1 << 31)) return WQ_ERR_SHAPE;
+  if ((m + 255) / 256 * ((n + 255) / 256) > 2147483647LL) return WQ_ERR_SHAPE;
+  const size_t ybytes = (size_t)(m * n) * 4, x1bytes = (size_t)(m * (k / 2));
+  const int64_t kb = k / 32;
+  if (overlap(y, ybytes, x1, x1bytes) || overlap(y, ybytes, x2, wbytes) ||
+      overlap(y, ybytes, x1_scale, (size_t)(m * kb)) || overlap(y, ybytes, x2_scale, (size_t)(kb * n)) ||
+      overlap(y, ybytes, workspace, need) || overlap(workspace, need, x1, x1bytes) ||
+      overlap(workspace, need, x2, wbytes) || overlap(workspace, need, x1_scale, (size_t)(m * kb)) ||
+      overlap(workspace, need, x2_scale, (size_t)(kb * n)))
+    return WQ_ERR_ALIAS;
+  wq::Mx4Problem p{static_cast<const uint8_t*>(x1), static_cast<const uint8_t*>(x2), x1_scale, x2_scale,
+                   y, m, k, n, workspace};
+  return from_hip(wq::launch_mx4_matmul(p, stream));
 }
 
 }  // extern "C"

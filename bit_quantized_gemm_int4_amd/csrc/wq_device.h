@@ -123,6 +123,17 @@ typedef __attribute__((address_space(1))) void glb_void;
 // wave-uniform SGPR offset, so no 64-bit address arithmetic runs per load.
 // An offset at or past the resource's byte count reads zero; BUF_OOB is such
 // an offset for every resource of at most 2 GiB.
+// One float -> OCP E2M1 code, round to nearest even: count the rounding
+// thresholds passed (ties go to the even code: 0, 1.0, 2.0, 4.0); a
+// magnitude beyond 6 passes every threshold and saturates to 6; the sign bit
+// is kept (-0.0 -> code 8). NaN has no code (outside every caller's contract).
+__device__ __forceinline__ uint32_t e2m1(float v) {
+  const float a = fabsf(v);
+  uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
 constexpr uint32_t BUF_OOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {

@@ -10,8 +10,9 @@
 
 namespace wq {
 
+// fp4: the 32-bit inputs are floats, encoded to E2M1 codes (else int4 values)
 hipError_t launch_pack_int4(const int32_t* w, int64_t k, int64_t n, bool transpose,
-                            wq_layout layout, uint8_t* out, hipStream_t s);
+                            wq_layout layout, uint8_t* out, hipStream_t s, bool fp4);
 
 hipError_t launch_quant_per_token(const void* x, bool bf16, int64_t rows, int64_t cols,
                                   const void* smooth, wq_dtype y_dtype, void* y,
@@ -88,6 +89,21 @@ struct I8Problem {
 };
 
 hipError_t launch_i8_matmul(const I8Problem& p, hipStream_t s);
+
+// MXFP4 x MXFP4 with in-place add (mx4_gemm.hip). The workspace holds the
+// scales rearranged for the lanes (mx4_workspace_bytes).
+struct Mx4Problem {
+  const uint8_t* x1;     // E2M1 (m, k), two per byte along k
+  const uint8_t* x2;     // E2M1 in GFX950_B
+  const uint8_t* s1;     // E8M0 (m, ceil(k/32))
+  const uint8_t* s2;     // E8M0 (ceil(k/32), n)
+  float* y;              // (m, n)
+  int64_t m, k, n;
+  void* workspace;
+};
+
+size_t mx4_workspace_bytes(int64_t m, int64_t k, int64_t n);
+hipError_t launch_mx4_matmul(const Mx4Problem& p, hipStream_t s);
 
 // Profiling hook (wq_profile.cpp): event pair around a contraction kernel.
 void prof_begin(hipStream_t s);

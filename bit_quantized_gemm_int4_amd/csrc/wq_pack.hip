@@ -1,6 +1,9 @@
 // INT4 weight pack (aclnnConvertWeightToINT4Pack page, operator description):
 // one 4-bit value per int32 in, tightly packed nibbles out, in the ND layout
-// or the gfx950 MFMA-operand layout GFX950_B (byte formula in wq.h).
+// or the gfx950 MFMA-operand layout GFX950_B (byte formula in wq.h). The
+// same page packs FLOAT weights into FLOAT4_E2M1 on the newer chips: with FP4
+// each 32-bit input is a float, encoded to its E2M1 code (nearest, ties to
+// even, saturating at +-6) instead of taking its low nibble.
 //
 // GFX950_B is built in registers (each word's eight codes come from eight
 // coalesced loads or one 32-byte run) and leaves as one contiguous run per
@@ -18,7 +21,13 @@ constexpr int TK = 128;        // tile depth (K)
 constexpr int TN = 64;         // tile width (N)
 constexpr int LROW = TK + 4;   // LDS row (one column's codes), padded
 
-template <bool TRANSPOSED>
+// The 4-bit code of one 32-bit input word.
+template <bool FP4>
+__device__ __forceinline__ uint32_t code_of(uint32_t v) {
+  return FP4 ? e2m1(__uint_as_float(v)) : (v & 0xFu);
+}
+
+template <bool TRANSPOSED, bool FP4>
 __device__ __forceinline__ void stage_tile(const int32_t* __restrict__ w, int64_t K, int64_t N,
                                            int64_t k0, int64_t n0, uint8_t (*tile)[LROW]) {
   const int t = threadIdx.x;
@@ -30,7 +39,7 @@ __device__ __forceinline__ void stage_tile(const int32_t* __restrict__ w, int64_
     for (int kk = t >> 6; kk < TK; kk += 4) {
       const int64_t k = k0 + kk;
       const int v = (k < K && n < N) ? w[k * N + n] : 0;
-      tile[nn][kk] = (uint8_t)(v & 0xF);
+      tile[nn][kk] = (uint8_t)code_of<FP4>((uint32_t)v);
     }
   } else {
     // weight stored (N, K): 128 consecutive threads read one 512-byte row piece
@@ -40,7 +49,7 @@ __device__ __forceinline__ void stage_tile(const int32_t* __restrict__ w, int64_
     for (int nn = t >> 7; nn < TN; nn += 2) {
       const int64_t n = n0 + nn;
       const int v = (k < K && n < N) ? w[n * K + k] : 0;
-      tile[nn][kk] = (uint8_t)(v & 0xF);
+      tile[nn][kk] = (uint8_t)code_of<FP4>((uint32_t)v);
     }
   }
 }
@@ -60,15 +69,16 @@ constexpr int PB_N = 256;
 // a record quarter still hits one aligned quarter (with its words permuted).
 __device__ __forceinline__ int pb_slot(int c, int w) { return c * 16 + (w ^ ((c >> 2) & 15)); }
 
-// Eight codes (one per int32, low nibble) -> one word, the first code lowest.
+// Eight input words -> one word of their codes, the first code lowest.
+template <bool FP4>
 __device__ __forceinline__ uint32_t nibbles_of(const uint32_t (&v)[8]) {
-  uint32_t word = v[0] & 0xFu;
+  uint32_t word = code_of<FP4>(v[0]);
 #pragma unroll
-  for (int j = 1; j < 8; ++j) word |= (v[j] & 0xFu) << (4 * j);
+  for (int j = 1; j < 8; ++j) word |= code_of<FP4>(v[j]) << (4 * j);
   return word;
 }
 
-template <bool TRANSPOSED>
+template <bool TRANSPOSED, bool FP4>
 __global__ __launch_bounds__(1024) void pack_gfx950b_kernel(const int32_t* __restrict__ w,
                                                             int64_t K, int64_t N, int64_t Np,
                                                             uint8_t* __restrict__ out) {
@@ -93,7 +103,7 @@ __global__ __launch_bounds__(1024) void pack_gfx950b_kernel(const int32_t* __res
         v[j] = __builtin_amdgcn_raw_buffer_load_b32(
             rs, ok ? (uint32_t)(((kr + j) * N + col) * 4) : BUF_OOB, 0, 0);
       }
-      rec[pb_slot(col, wave)] = nibbles_of(v);
+      rec[pb_slot(col, wave)] = nibbles_of<FP4>(v);
     }
   } else {
     // weight (N, K): a column's 8 codes of one word are 32 contiguous bytes;
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(1024) void pack_gfx950b_kernel(const int32_t* __res
           v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? off + 4 * j : BUF_OOB, 0, 0);
         }
       }
-      rec[pb_slot(col, wd)] = nibbles_of(v);
+      rec[pb_slot(col, wd)] = nibbles_of<FP4>(v);
     }
   }
   __syncthreads();
@@ -136,13 +146,13 @@ __global__ __launch_bounds__(1024) void pack_gfx950b_kernel(const int32_t* __res
   *reinterpret_cast<u32x4*>(out + ((k0 / 128) * Np + n0) * 64 + 16 * t) = v;
 }
 
-template <bool TRANSPOSED>
+template <bool TRANSPOSED, bool FP4>
 __global__ __launch_bounds__(256) void pack_nd_kernel(const int32_t* __restrict__ w, int64_t K,
                                                       int64_t N, uint8_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[TN][LROW];
   const int64_t k0 = (int64_t)blockIdx.y * TK;
   const int64_t n0 = (int64_t)blockIdx.x * TN;
-  stage_tile<TRANSPOSED>(w, K, N, k0, n0, tile);
+  stage_tile<TRANSPOSED, FP4>(w, K, N, k0, n0, tile);
   __syncthreads();
   // thread -> packed row kk, 16 output bytes = columns n0 + half*32 .. +32
   const int t = threadIdx.x;
@@ -174,23 +184,29 @@ __global__ __launch_bounds__(256) void pack_nd_kernel(const int32_t* __restrict_
 }  // namespace
 
 hipError_t launch_pack_int4(const int32_t* w, int64_t k, int64_t n, bool transpose,
-                            wq_layout layout, uint8_t* out, hipStream_t s) {
+                            wq_layout layout, uint8_t* out, hipStream_t s, bool fp4) {
   if (layout == WQ_LAYOUT_GFX950_B) {
     const int64_t Kp = 128 * ((k + 127) / 128);
     const int64_t Np = 16 * ((n + 15) / 16);
     // tile-relative byte offsets stay below 2^31 (the buffer bound)
     if ((transpose ? (PB_N * k) : (128 * n)) >= (int64_t(1) << 29)) return hipErrorInvalidValue;
     dim3 grid((unsigned)((Np + PB_N - 1) / PB_N), (unsigned)(Kp / 128));
-    if (transpose)
-      pack_gfx950b_kernel<true><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
-    else
-      pack_gfx950b_kernel<false><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
+    if (fp4) {
+      if (transpose) pack_gfx950b_kernel<true, true><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
+      else pack_gfx950b_kernel<false, true><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
+    } else {
+      if (transpose) pack_gfx950b_kernel<true, false><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
+      else pack_gfx950b_kernel<false, false><<<grid, 1024, 0, s>>>(w, k, n, Np, out);
+    }
   } else {
     dim3 grid((unsigned)((n + TN - 1) / TN), (unsigned)((k + TK - 1) / TK));
-    if (transpose)
-      pack_nd_kernel<true><<<grid, 256, 0, s>>>(w, k, n, out);
-    else
-      pack_nd_kernel<false><<<grid, 256, 0, s>>>(w, k, n, out);
+    if (fp4) {
+      if (transpose) pack_nd_kernel<true, true><<<grid, 256, 0, s>>>(w, k, n, out);
+      else pack_nd_kernel<false, true><<<grid, 256, 0, s>>>(w, k, n, out);
+    } else {
+      if (transpose) pack_nd_kernel<true, false><<<grid, 256, 0, s>>>(w, k, n, out);
+      else pack_nd_kernel<false, false><<<grid, 256, 0, s>>>(w, k, n, out);
+    }
   }
   return hipGetLastError();
 }

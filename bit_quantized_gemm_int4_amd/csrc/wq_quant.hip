@@ -231,14 +231,6 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-// One float (|v| <= 6) -> E2M1 code, RNE: count the rounding thresholds
-// passed (ties go to the even code: 0, 1.0, 2.0, 4.0).
-__device__ __forceinline__ uint32_t e2m1(float v) {
-  const float a = fabsf(v);
-  uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return m | ((__float_as_uint(v) >> 28) & 0x8u);
-}
 
 template <int ACT, int FMT, bool TRANS, bool VEC, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_mx_kernel(

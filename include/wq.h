@@ -8,6 +8,8 @@
  *   wq_matmul_add_rmsnorm         aclnnWeightQuantMatmulAllReduceAddRmsNorm
  *                                 (single device: the AllReduce is the identity)
  *   mx_quant_matmul_inplace_add   aclnnQuantBatchMatmulInplaceAdd (mx)
+ *   mx_fp4_quant_matmul_inplace_add  the same, both operands MXFP4
+ *   wq_pack_fp4                   aclnnConvertWeightToINT4Pack (FLOAT -> E2M1)
  *   wq_weight_quant_matmul        \ the unfused chain that the fused operator's
  *   wq_add_rms_norm               / page names as its replacement
  *
@@ -102,6 +104,22 @@ wq_status wq_pack_int4(const int32_t* weight, int64_t k, int64_t n,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * FLOAT -> FLOAT4_E2M1 pack. aclnnConvertWeightToINT4Pack page, operator
+ * description: on the newer chips the pack also turns FLOAT weights into
+ * tightly packed FLOAT4_E2M1 data.
+ *
+ * weight     device float32, logical (k, n); stored as for wq_pack_int4.
+ * out        device, wq_pack_int4_bytes(k, n, layout) bytes: the E2M1 codes
+ *            in the INT4 code layout (WQ_LAYOUT_GFX950_B is the MX GEMMs' x2).
+ * Each value goes to its nearest E2M1 value, ties to even; magnitudes beyond
+ * 6 saturate to +-6; the sign of zero is kept (-0.0 -> code 8). NaN is
+ * outside the contract. Limits and errors as wq_pack_int4.
+ * ---------------------------------------------------------------------- */
+wq_status wq_pack_fp4(const float* weight, int64_t k, int64_t n, int transpose,
+                      wq_layout layout, void* out, hipStream_t stream);
+
+
+/* ------------------------------------------------------------------------
  * Dynamic quantization. aclnnDynamicQuant page, Formula: with optional
  * smooth scales, input = x * smooth; scale = row_max(|input|) / dtypeMax;
  * y = round(input / scale). Constraints section: an INT4 output needs an even
@@ -187,6 +205,41 @@ wq_status wq_matmul_add_rmsnorm(
     const void* bias, const void* residual, const void* gamma,
     double epsilon, void* y, void* norm_out,
     void* workspace, size_t workspace_size, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MXFP4 x MXFP4 quantized matmul with in-place add.
+ * aclnnQuantBatchMatmulInplaceAdd page, Formula (mx quantization), read with
+ * both operands FLOAT4_E2M1:
+ *     y[m,n] += sum_j (sum_{k in slice j} x1[m,k] * x2[k,n])
+ *                     * scale1[m,j] * scale2[j,n]
+ * with 32-long K slices, j < k/32. The scaled MFMA runs at the FP4 rate.
+ *
+ * x1          device E2M1 codes (m, k) row-major, two per byte along k, even
+ *             k in the low nibble (wq_dynamic_quant's block-32 E2M1 output;
+ *             transposeX1 = false).
+ * x2          device E2M1 codes, logical (k, n), in WQ_LAYOUT_GFX950_B
+ *             (wq_pack_fp4 or wq_pack_int4 of the codes); ND is
+ *             WQ_ERR_UNSUPPORTED.
+ * x1_scale    device E8M0 (m, k/32) = scale1[m][j].
+ * x2_scale    device E8M0 (k/32, n) = scale2[j][n].
+ * m in [0, 2^31 - 1], n in [0, 65535] (0: nothing to do); k in [32, 65535]
+ * and a multiple of 32 (else WQ_ERR_SHAPE).
+ * group_size  0 or 32 | 1 << 16 | 1 << 32, as for mx_quant_matmul_inplace_add.
+ * y           device float32 (m, n), read and written.
+ * workspace   device, >= mx_fp4_quant_matmul_inplace_add_workspace_size(m, k,
+ *             n) bytes (the scales rearranged for the matrix cores), no
+ *             initial contents needed.
+ * x1, x2, y and the workspace 16-byte aligned. Accumulation is float32 and
+ * starts from y; every slice sum is exact.
+ * Errors: WQ_ERR_NULLPTR, WQ_ERR_SHAPE, WQ_ERR_GROUP, WQ_ERR_WORKSPACE,
+ * WQ_ERR_UNSUPPORTED, WQ_ERR_ALIAS (y or the workspace overlapping an input).
+ * ---------------------------------------------------------------------- */
+size_t mx_fp4_quant_matmul_inplace_add_workspace_size(int64_t m, int64_t k, int64_t n);
+wq_status mx_fp4_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout x2_layout,
+                                          const uint8_t* x1_scale, const uint8_t* x2_scale,
+                                          int64_t m, int64_t k, int64_t n, int64_t group_size,
+                                          float* y, void* workspace, size_t workspace_size,
+                                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Weight-quantized matmul alone (the first half of the unfused chain).

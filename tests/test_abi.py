@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -270,3 +270,42 @@ def test_add_rms_norm_validation():
     # in place is allowed: y == x or y == residual pass every host check (not
     # called here: a valid call would launch)
 
+
+
+def test_pack_fp4_validation():
+    L = wq.lib()
+    assert L.wq_pack_fp4(FAKE, 256, 128, 0, 5, FAKE2, 0) == wq.WQ_ERR_UNSUPPORTED
+    assert L.wq_pack_fp4(FAKE, -1, 128, 0, wq.WQ_LAYOUT_GFX950_B, FAKE2, 0) == wq.WQ_ERR_SHAPE
+    assert L.wq_pack_fp4(FAKE, 256, 127, 0, wq.WQ_LAYOUT_ND, FAKE2, 0) == wq.WQ_ERR_SHAPE
+    assert L.wq_pack_fp4(None, 256, 128, 0, wq.WQ_LAYOUT_GFX950_B, FAKE2, 0) == wq.WQ_ERR_NULLPTR
+    assert L.wq_pack_fp4(FAKE, 256, 128, 0, wq.WQ_LAYOUT_GFX950_B, FAKE2 + 8, 0) == wq.WQ_ERR_SHAPE
+    assert L.wq_pack_fp4(FAKE, 256, 128, 0, wq.WQ_LAYOUT_GFX950_B, FAKE + 64, 0) == wq.WQ_ERR_ALIAS
+    assert L.wq_pack_fp4(FAKE, 0, 128, 0, wq.WQ_LAYOUT_GFX950_B, FAKE2, 0) == wq.WQ_OK
+
+
+def _mx4(**kw):
+    m, k, n = kw.pop("m", 256), kw.pop("k", 512), kw.pop("n", 256)
+    a = dict(x1=FAKE, x2=FAKE + 0x100000, layout=wq.WQ_LAYOUT_GFX950_B, s1=FAKE + 0x200000,
+             s2=FAKE + 0x300000, group=wq.MX_GROUP_SIZE, y=FAKE + 0x400000, ws=FAKE + 0x800000,
+             ws_size=wq.mx_fp4_quant_matmul_inplace_add_workspace_size(m, k, n))
+    a.update(kw)
+    return wq.lib().mx_fp4_quant_matmul_inplace_add(a["x1"], a["x2"], a["layout"], a["s1"], a["s2"], m, k,
+                                                    n, a["group"], a["y"], a["ws"], a["ws_size"], 0)
+
+
+def test_mx_fp4_matmul_validation():
+    # 2 m-tiles + 1 n-tile, 4 steps of 128, 1 KiB each
+    assert wq.mx_fp4_quant_matmul_inplace_add_workspace_size(300, 512, 200) == (2 + 1) * 4 * 1024
+    assert _mx4(layout=wq.WQ_LAYOUT_ND) == wq.WQ_ERR_UNSUPPORTED
+    assert _mx4(k=48) == wq.WQ_ERR_SHAPE                              # k % 32
+    assert _mx4(k=0) == wq.WQ_ERR_SHAPE
+    assert _mx4(n=65536) == wq.WQ_ERR_SHAPE
+    assert _mx4(group=64) == wq.WQ_ERR_GROUP
+    assert _mx4(group=0, ws=None) == wq.WQ_ERR_WORKSPACE                # 0 passes the group rule
+    assert _mx4(m=0) == wq.WQ_OK
+    assert _mx4(y=None) == wq.WQ_ERR_NULLPTR
+    assert _mx4(ws=None) == wq.WQ_ERR_WORKSPACE
+    assert _mx4(ws_size=1024) == wq.WQ_ERR_WORKSPACE
+    assert _mx4(x1=FAKE + 8) == wq.WQ_ERR_SHAPE                       # misaligned
+    assert _mx4(y=FAKE + 0x100000) == wq.WQ_ERR_ALIAS                 # y over x2
+    assert _mx4(ws=FAKE + 0x200000) == wq.WQ_ERR_ALIAS                # workspace over x1's scales
