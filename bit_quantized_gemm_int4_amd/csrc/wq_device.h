@@ -134,6 +134,19 @@ __device__ __forceinline__ uint32_t e2m1(float v) {
   return m | ((__float_as_uint(v) >> 28) & 0x8u);
 }
 
+// Eight floats -> eight E2M1 codes in one word, the first lowest: the
+// gfx950 converter (scale 1), which rounds as e2m1() does (nearest, ties to
+// even, saturating, sign kept; checked on every grid value, tie, signed zero
+// and infinity).
+__device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
 constexpr uint32_t BUF_OOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {

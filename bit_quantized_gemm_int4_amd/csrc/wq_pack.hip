@@ -72,10 +72,17 @@ __device__ __forceinline__ int pb_slot(int c, int w) { return c * 16 + (w ^ ((c 
 // Eight input words -> one word of their codes, the first code lowest.
 template <bool FP4>
 __device__ __forceinline__ uint32_t nibbles_of(const uint32_t (&v)[8]) {
-  uint32_t word = code_of<FP4>(v[0]);
+  if constexpr (FP4) {
+    float f[8];
 #pragma unroll
-  for (int j = 1; j < 8; ++j) word |= code_of<FP4>(v[j]) << (4 * j);
-  return word;
+    for (int j = 0; j < 8; ++j) f[j] = __uint_as_float(v[j]);
+    return e2m1x8(f);
+  } else {
+    uint32_t word = code_of<FP4>(v[0]);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) word |= code_of<FP4>(v[j]) << (4 * j);
+    return word;
+  }
 }
 
 template <bool TRANSPOSED, bool FP4>

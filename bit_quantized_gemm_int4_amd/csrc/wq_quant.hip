@@ -238,14 +238,20 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
     int64_t cols, uint8_t* __restrict__ y, uint8_t* __restrict__ scale) {
   constexpr int LR = 128 + 4;                    // LDS row (one column), bytes
   __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? 64 : 1][TRANS ? LR : 4];
+  // A thread takes 8 columns of 4 rows. Transposed output: 8 threads along a
+  // row, a 128-row x 64-column block (transposed through LDS). Row-major
+  // output: 64 threads along a row, a 16-row x 512-column block, so a
+  // wave's loads and stores each cover 512 consecutive columns of a row.
+  constexpr int TCOLS = TRANS ? 8 : 64;
+  constexpr int BR = 256 / TCOLS * 4, BC = TCOLS * 8;
   const int t = threadIdx.x;
-  const int rg = t >> 3, cc = t & 7;
-  const int64_t r0 = (int64_t)blockIdx.x * 128 + rg * 4;
-  const int64_t c0 = (int64_t)blockIdx.y * 64 + cc * 8;
+  const int rg = t / TCOLS, cc = t % TCOLS;
+  const int64_t r0 = (int64_t)blockIdx.x * BR + rg * 4;
+  const int64_t c0 = (int64_t)blockIdx.y * BC + cc * 8;
   const int64_t nb = (cols + 31) / 32;
-  // One resource over the workgroup's 128 rows; tile-relative byte offsets
+  // One resource over the workgroup's rows; block-relative byte offsets
   // stay below 2^31 for cols < 2^22. All loads are issued before any use.
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x + (int64_t)blockIdx.x * 128 * cols, 0x7FFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x + (int64_t)blockIdx.x * BR * cols, 0x7FFFFFFFu);
   const bool cin = c0 < cols;
   u32x4 raw[4];
 #pragma unroll
@@ -280,10 +286,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
       codes[r][0] = e4m3x2(s[0], s[1]) | (e4m3x2(s[2], s[3]) << 16);
       codes[r][1] = e4m3x2(s[4], s[5]) | (e4m3x2(s[6], s[7]) << 16);
     } else {
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= e2m1(s[i]) << (4 * i);
-      codes[r][0] = w;
+      codes[r][0] = e2m1x8(s);
       codes[r][1] = 0;
     }
   }
@@ -375,7 +378,9 @@ hipError_t launch_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols,
                            uint8_t* y, uint8_t* scale, hipStream_t s) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* sp = static_cast<const uint16_t*>(smooth);
-  dim3 grid((unsigned)((rows + 127) / 128), (unsigned)((cols + 63) / 64));
+  // blocks of 128 x 64 (transposed output) or 16 x 512 (row-major output)
+  dim3 grid = transpose_y ? dim3((unsigned)((rows + 127) / 128), (unsigned)((cols + 63) / 64))
+                          : dim3((unsigned)((rows + 15) / 16), (unsigned)((cols + 511) / 512));
   const bool vec = (cols & 7) == 0;
 #define WQ_MX_LAUNCH(A, F, T)                                                                     \
   do {                                                                                            \
