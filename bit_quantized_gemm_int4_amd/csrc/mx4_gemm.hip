@@ -18,9 +18,9 @@
 // one GFX950_B column record) per step. A step's x1 rows, weight records and
 // scales move by buffer->LDS DMA into a ring of four stages, issued about two
 // and a half steps ahead, one DMA instruction per MFMA slot. In LDS a 64-byte
-// row keeps 16-byte chunk c at position c ^ ((row >> 2) & 3), so every
-// 16-lane operand read hits 16 distinct bank groups. The accumulators start
-// as y, so the in-place add needs no extra pass over y.
+// row keeps 16-byte chunk c at position c ^ ((row >> 1) & 3), the INT8
+// tile's swizzle (the fastest of those timed for these reads). The
+// accumulators start as y, so the in-place add needs no extra pass over y.
 //
 // Scales: a pre-pass writes them in the order the lanes use them (the byte
 // select is one immediate for all lanes): per (m tile, step), one dword per
@@ -41,7 +41,7 @@ constexpr int F4_ROW = F4_BK / 2;                       // bytes per row per ste
 constexpr int F4_OPS = 256 * F4_ROW;                    // one operand's stage: 16 KiB
 constexpr int F4_SC = 2048;                             // a stage's scale dwords
 
-__device__ __forceinline__ int f4_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int f4_pos(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 __global__ __launch_bounds__(256) void mx4_scale_prep(const uint8_t* __restrict__ s1,
                                                       const uint8_t* __restrict__ s2,
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void mx4_scale_prep(const uint8_t* __restrict_
 // Per-lane DMA addressing of one operand stage: 256 rows x 64 bytes by 16
 // DMA instructions of 1 KiB (16 rows); wave w issues 2w + j, lane l fills
 // row 16 (2w + j) + l / 4 at position l % 4, fetching logical chunk
-// (l % 4) ^ ((row >> 2) & 3). `base` is the byte offset of that chunk at step
+// (l % 4) ^ ((row >> 1) & 3). `base` is the byte offset of that chunk at step
 // 0 (BUF_OOB for rows past the operand), `lim` bounds the step offset.
 struct F4Dma {
   uint32_t base[2];
