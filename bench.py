@@ -1,22 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the weight-quantized matmul hot path on one MI355X.
 
-One step runs every operator of the path once, each on its workload, on
-torch's current stream:
+One step runs the operators of the hot path once each, on their workloads,
+on torch's current stream:
   1. wq_pack_int4          prefill weight (8192, 8192) int32 -> GFX950_B
   2. wq_matmul_add_rmsnorm prefill W4A16 group 128 + AddRmsNorm, bf16,
                            x1 (4, 1024, 8192), x2 (8192, 8192)
-  3. wq_weight_quant_matmul   the unfused chain on row 2's inputs: the
-  4. wq_add_rms_norm          standalone matmul (4096, 8192) bf16, then
-                              AddRmsNorm of it with the residual
-  5. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
-  6. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
-  7. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
-  8. wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 5's output)
+  3. wq_dynamic_quant      per-token INT8 of x (4096, 8192) fp16 * smooth
+  4. wq_dynamic_quant      MX E4M3 (transposed) + E8M0 of the same x
+  5. mx_quant_matmul_inplace_add  y (4096, 4096) fp32 += E4M3 x E2M1, K 8192
+The operators built on the path run after the steps, in a loop of their
+own with the same warm-up and step counts, reported under ``extras``:
+  wq_weight_quant_matmul + wq_add_rms_norm   the unfused chain on row 2's
+                           inputs: matmul (4096, 8192) bf16, then AddRmsNorm
+  wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 3's output)
                            x INT8 weight (4096, 8192), per-token x per-channel
-  9. wq_dynamic_quant      MX E2M1 (row-major) + E8M0 of the same x
- 10. mx_fp4_quant_matmul_inplace_add  y (4096, 4096) fp32 += E2M1 (row 9's
-                           output) x row 7's E2M1 weight, at the FP4 rate
+  wq_dynamic_quant         MX E2M1 (row-major) + E8M0 of the same x
+  mx_fp4_quant_matmul_inplace_add  y (4096, 4096) fp32 += E2M1 x row 5's
+                           E2M1 weight, at the FP4 rate
 Every operator is timed with HIP events around its launch(es). A second
 pass of the same steps has the library time its contraction kernels (the
 prefill MFMA tile, the MX, INT8 and FP4 tiles, the decode weight stream)
@@ -205,6 +206,12 @@ def main():
         # the A8W8 chain's GEMM on the per-token INT8 output of op_quant_tok
         wq.wq_quant_matmul_inplace_add(q8, w8t, q8s, w8s, MM, MK, MN, y8)
 
+    # the INT8 GEMM and the FP4 GEMM read the quants' outputs: fill them once
+    # here so that every row runs on defined inputs whatever --only selects
+    op_quant_tok()
+    op_quant_f4()
+    torch.cuda.synchronize()
+
     # algorithmic work per call (inputs + outputs as passed; packed weights)
     rows = [
         ("pack", op_pack, 0, K * N * 4 + x2.numel(), "hbm"),
@@ -223,77 +230,87 @@ def main():
         ("mxfp4_matmul_inplace_add", op_f4, 2 * MM * MN * MK,
          x1f4.numel() + x2mx.numel() + s1f4.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
     ]
-    rows = [r for r in rows if want(r[0])]
+    # the step is the hot path's rows (pack, the fused W4A16 call, the two
+    # quants, the MX GEMM); the rows built on it (the unfused chain, the INT8
+    # and MXFP4 paths) run as extras in a loop of their own, so that their
+    # dense GEMMs do not heat the GPU under the step's rows
+    EXTRA = {"weight_quant_matmul", "add_rms_norm", "quant_matmul_inplace_add_int8",
+             "dynamic_quant_mx_e2m1", "mxfp4_matmul_inplace_add"}
+    core = [r for r in rows if want(r[0]) and r[0] not in EXTRA]
+    extras = [r for r in rows if want(r[0]) and r[0] in EXTRA]
     if "copy" in only:
         # Not part of the step: a plain device copy of known size, whose
         # FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures.
         cp_src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         cp_dst = torch.empty_like(cp_src)
-        rows.append(("copy", lambda: cp_dst.copy_(cp_src), 0, 2 * COPY_BYTES, "hbm"))
+        core.append(("copy", lambda: cp_dst.copy_(cp_src), 0, 2 * COPY_BYTES, "hbm"))
 
-    def step(record):
-        for name, fn, _, _, _ in rows:
-            if record is not None:
-                ev0 = torch.cuda.Event(enable_timing=True)
-                ev1 = torch.cuda.Event(enable_timing=True)
-                ev0.record(stream)
-                fn()
-                ev1.record(stream)
-                record[name].append((ev0, ev1))
-            else:
-                fn()
+    def run_rows(rows):
+        """Warm-up steps, then the timed steps (every call bracketed by
+        events on torch's stream, the library's own profiling off: its event
+        pairs would sit inside the multi-kernel calls and lengthen them), then
+        a second timed pass of the same steps in which the library times its
+        contraction kernels (one launch per contraction row and call) with
+        event pairs on the stream they run on. Returns (rows, ms per step)."""
+        def step(record):
+            for name, fn, _, _, _ in rows:
+                if record is not None:
+                    ev0 = torch.cuda.Event(enable_timing=True)
+                    ev1 = torch.cuda.Event(enable_timing=True)
+                    ev0.record(stream)
+                    fn()
+                    ev1.record(stream)
+                    record[name].append((ev0, ev1))
+                else:
+                    fn()
 
-    for _ in range(args.warmup):
-        step(None)
-    torch.cuda.synchronize()
-    rec = {r[0]: [] for r in rows}
-    # the timed steps: every call bracketed by events on torch's stream, with
-    # the library's own profiling off (its event pairs would sit inside the
-    # multi-kernel calls and lengthen them)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(rec)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / max(1, args.steps)
-    # a second timed pass of the same steps in which the library times its
-    # contraction kernels (one launch per contraction row and call) with event
-    # pairs on the stream they run on: the kernel times of `roofline`
-    contraction_rows = [r[0] for r in rows if r[0] in CONTRACTION_ROWS]
-    kernel_ms = {}
-    if contraction_rows:
-        wq.wq_profile_enable(True)
-        for _ in range(args.steps):
+        for _ in range(args.warmup):
             step(None)
         torch.cuda.synchronize()
-        kernel_times = wq.wq_profile_read()
-        wq.wq_profile_enable(False)
-        if len(kernel_times) == args.steps * len(contraction_rows):
-            for j, name in enumerate(contraction_rows):
-                kernel_ms[name] = statistics.mean(kernel_times[j::len(contraction_rows)])
+        rec = {r[0]: [] for r in rows}
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(rec)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        contraction_rows = [r[0] for r in rows if r[0] in CONTRACTION_ROWS]
+        kernel_ms = {}
+        if contraction_rows:
+            wq.wq_profile_enable(True)
+            for _ in range(args.steps):
+                step(None)
+            torch.cuda.synchronize()
+            kernel_times = wq.wq_profile_read()
+            wq.wq_profile_enable(False)
+            if len(kernel_times) == args.steps * len(contraction_rows):
+                for j, name in enumerate(contraction_rows):
+                    kernel_ms[name] = statistics.mean(kernel_times[j::len(contraction_rows)])
+        out = {}
+        for name, _, flop, nbytes, bound in rows:
+            times = [a.elapsed_time(b) for a, b in rec[name]]
+            ms = statistics.median(times)
+            ts = sorted(times)
+            d = {"ms": round(ms, 5), "ms_p10": round(ts[len(ts) // 10], 5),
+                 "ms_p90": round(ts[(9 * len(ts)) // 10], 5), "ms_mean": round(statistics.mean(times), 5),
+                 "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
+            if flop:
+                d["TFLOP/s"] = round(flop / ms / 1e9, 2)
+                d["flop"] = flop
+            if name in kernel_ms:
+                km = kernel_ms[name]
+                d["kernel"] = CONTRACTION_ROWS[name]
+                d["kernel_ms"] = round(km, 5)
+                d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
+            peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS, "weight_quant_matmul": PEAK_BF16_TFLOPS,
+                    "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS,
+                    "mxfp4_matmul_inplace_add": PEAK_FP4_TFLOPS}.get(name, PEAK_FP8_TFLOPS)
+            d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
+                                      else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
+            out[name] = d
+        return out, (t1 - t0) * 1e3 / max(1, args.steps)
 
-    out_rows = {}
-    for name, _, flop, nbytes, bound in rows:
-        times = [a.elapsed_time(b) for a, b in rec[name]]
-        ms = statistics.median(times)
-        ts = sorted(times)
-        d = {"ms": round(ms, 5), "ms_p10": round(ts[len(ts) // 10], 5),
-             "ms_p90": round(ts[(9 * len(ts)) // 10], 5), "ms_mean": round(statistics.mean(times), 5),
-             "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
-        if flop:
-            d["TFLOP/s"] = round(flop / ms / 1e9, 2)
-            d["flop"] = flop
-        if name in kernel_ms:
-            km = kernel_ms[name]
-            d["kernel"] = CONTRACTION_ROWS[name]
-            d["kernel_ms"] = round(km, 5)
-            d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
-        peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS, "weight_quant_matmul": PEAK_BF16_TFLOPS,
-                "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS,
-                "mxfp4_matmul_inplace_add": PEAK_FP4_TFLOPS}.get(name, PEAK_FP8_TFLOPS)
-        d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
-                                  else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)
-        out_rows[name] = d
+    out_rows, ms_per_step = run_rows(core) if core else ({}, 0.0)
+    out_extras, _ = run_rows(extras) if extras else ({}, 0.0)
 
     # ---------------- decode section (HBM-bound) ----------------
     decode = {}
@@ -509,9 +526,10 @@ def main():
         "config": {"workload": "prefill W4A16 group-128 dequant-GEMM + AddRmsNorm, "
                                "x1 bf16 (4,1024,8192), x2 int4 (8192,8192), offset zeros",
                    "m": M, "k": K, "n": N, "group_size": pf.group_size,
-                   "step": [r[0] for r in rows]},
+                   "step": [r[0] for r in core], "extras": [r[0] for r in extras]},
         "roofline": None,
         "rows": out_rows,
+        "extras": out_extras,
         "decode": decode,
         "cpu_baseline": cpu,
         "ceilings": ceilings,

@@ -229,3 +229,15 @@ def test_decode_zero_scale_columns():
     note("wq decode zero-scale groups and columns")
     y, nrm = wq_on_gpu(c)
     check_wq(c, y, nrm)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17, 19, 21, 24, 28, 31, 32])
+def test_decode_every_row_count(m):
+    # the decode kernel computes 16 rows per launch (absent rows read zeros),
+    # rows 17..32 in a second launch: every count of rows, against the oracle
+    c = workloads.wq_case(f"dec{m}", m, 1024, 640, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=128, offset_range=(-0.5, 0.5),
+                          bias_std=0.1, seed=100 + m)
+    note(f"wq decode rows m={m} 1024x640 g128")
+    y, n = wq_on_gpu(c)
+    check_wq(c, y, n)
