@@ -140,13 +140,16 @@ wq_status check_wq_common(int64_t m, int64_t k, wq_dtype act_dtype, int64_t n, w
   if (!is_act(act_dtype)) return WQ_ERR_DTYPE;
   if (w_dtype != WQ_INT4 && w_dtype != WQ_INT8) return WQ_ERR_DTYPE;
   if (x2_layout != WQ_LAYOUT_ND && x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
-  if (w_dtype == WQ_INT4 && transpose_x2) return WQ_ERR_UNSUPPORTED;   // pack the transpose
+  // a transposed GFX950_B weight is the same layout: the pack takes the transpose
+  if (w_dtype == WQ_INT4 && transpose_x2 && x2_layout != WQ_LAYOUT_ND) return WQ_ERR_UNSUPPORTED;
   if (w_dtype == WQ_INT8 && x2_layout != WQ_LAYOUT_ND) return WQ_ERR_UNSUPPORTED;
   // shapes: b*s in [0, 2^31-1] (0 = empty); k in [1, 65535]; n in [0, 65535]
   if (m < 0 || m > kMaxRows) return WQ_ERR_SHAPE;
   if (k < 1 || k > kMaxKN) return WQ_ERR_SHAPE;
   if (n < 0 || n > kMaxKN) return WQ_ERR_SHAPE;
-  if (w_dtype == WQ_INT4 && x2_layout == WQ_LAYOUT_ND && (n % 2)) return WQ_ERR_SHAPE;
+  // INT4 ND packs the last stored dimension: n, or k when transposed (n, k)
+  if (w_dtype == WQ_INT4 && x2_layout == WQ_LAYOUT_ND && ((transpose_x2 ? k : n) % 2))
+    return WQ_ERR_SHAPE;
   // quantization granularity (Constraints): per tensor (1), per channel
   // (1, n) / (n), per group (ceil(k/G), n) with G in [32, k-1], G % 32 == 0.
   const int64_t G = antiquant_group_size;

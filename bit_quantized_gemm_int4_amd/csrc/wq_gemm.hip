@@ -15,8 +15,8 @@
 //     multiple of 128 (or per channel / tensor): a weight stream;
 //   - gemm_b_wide (wq_gemm_fast.hip): the same weights at larger m, the
 //     MFMA-bound tile;
-//   - gemm_generic: any weight layout (INT4 ND / GFX950_B, INT8 ND /
-//     transposed), any group size, 64x64x32 tiles with both operands staged
+//   - gemm_generic: any weight layout (INT4 ND / ND transposed / GFX950_B,
+//     INT8 ND / transposed), any group size, 64x64x32 tiles with both operands staged
 //     in LDS; integer codes go to the MFMA and each group's scale and
 //     offset are applied to its float32 partial sums.
 #include "wq_device.h"
@@ -25,7 +25,7 @@
 namespace wq {
 namespace {
 
-enum WFmt { W_I4_ND = 0, W_I4_B = 1, W_I8_ND = 2, W_I8_T = 3 };
+enum WFmt { W_I4_ND = 0, W_I4_B = 1, W_I8_ND = 2, W_I8_T = 3, W_I4_T = 4 };
 
 struct GemmArgs {
   const uint16_t* x1;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
       *reinterpret_cast<u32x4*>(&As[r][kc]) = v;
     }
     // ---- B tile: integer codes as 16-bit floats, stored [n][k] ----
-    if constexpr (WF == W_I4_B || WF == W_I8_T) {
+    if constexpr (WF == W_I4_B || WF == W_I8_T || WF == W_I4_T) {
       // thread -> column t/4, 8 consecutive k
       const int c = t >> 2, kc = (t & 3) * 8;
       const int64_t col = n0 + c, kk = k0 + kc;
@@ -118,6 +118,15 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs a) {
               a.x2 + ((kk / 128) * a.np + col) * 64 + ((kk / 32) % 4) * 16 + (kk % 32) / 2);
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = ((int)(word << (28 - 4 * i))) >> 28;
+      } else if constexpr (WF == W_I4_T) {
+        // (n, k) with k packed two per byte, even k in the low nibble (k even)
+        const uint8_t* src = a.x2 + col * (a.k / 2) + kk / 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = (col < a.n && kk + 2 * i < a.k) ? (int)src[i] : 0;
+          q[2 * i] = ((int)(b << 28)) >> 28;
+          q[2 * i + 1] = ((int)(b << 24)) >> 28;
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -274,6 +283,7 @@ hipError_t launch_generic(const WqProblem& p, const GemmArgs& a, hipStream_t s) 
   prof_begin(s);
   if (p.w_bits == 4) {
     if (p.layout == WQ_LAYOUT_GFX950_B) gemm_generic<ACT, W_I4_B><<<grid, 256, 0, s>>>(a);
+    else if (p.transpose_x2) gemm_generic<ACT, W_I4_T><<<grid, 256, 0, s>>>(a);
     else gemm_generic<ACT, W_I4_ND><<<grid, 256, 0, s>>>(a);
   } else {
     if (p.transpose_x2) gemm_generic<ACT, W_I8_T><<<grid, 256, 0, s>>>(a);

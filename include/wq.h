@@ -172,9 +172,13 @@ wq_status wq_dynamic_quant(const void* x, wq_dtype x_dtype, int64_t rows,
  *
  * x1          device (m, k) of act_dtype (WQ_F16 or WQ_BF16), row-major.
  * x2          device weight. w_dtype WQ_INT4: packed by wq_pack_int4 in
- *             x2_layout (ND or GFX950_B), transpose_x2 must be 0 (pack the
- *             transpose instead). w_dtype WQ_INT8: layout ND, (k, n)
- *             row-major, or (n, k) row-major when transpose_x2 != 0.
+ *             x2_layout. ND: (k, n/2) bytes (n even), or, when transpose_x2
+ *             != 0, the transpose stored (n, k/2) bytes (k even), even k in
+ *             the low nibble (the Constraints section lets x2 be
+ *             transposed). GFX950_B: transpose_x2 must be 0 (the pack takes
+ *             the transpose and writes the same layout). w_dtype WQ_INT8:
+ *             layout ND, (k, n) row-major, or (n, k) row-major when
+ *             transpose_x2 != 0.
  * antiquant_scale   device act_dtype, (scale_rows, scale_cols):
  *             (1, 1) per tensor, (1, n) per channel, (ceil(k/G), n) per group.
  * antiquant_offset  device, same shape and dtype, or NULL (zero).

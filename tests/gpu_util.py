@@ -26,7 +26,13 @@ def wq_on_gpu(case, layout=wq.WQ_LAYOUT_GFX950_B, inplace=False, transpose_x2=Fa
     x1 = case.x1.to(DEV)
     if case.w_bits == 4:
         w = case.w.to(DEV)
-        x2 = wq.pack_int4(w, layout)
+        if transpose_x2:
+            # the transposed weight (n, k), packed along its last dimension:
+            # (n, k/2) bytes, even k in the low nibble
+            assert layout == wq.WQ_LAYOUT_ND
+            x2 = wq.pack_int4(w.t().contiguous(), layout)
+        else:
+            x2 = wq.pack_int4(w, layout)
         wdt = wq.WQ_INT4
     else:
         w8 = case.w.to(torch.int8)

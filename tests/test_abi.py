@@ -128,7 +128,8 @@ def test_wq_matmul_validation_dtypes_and_layouts():
     assert _wqmm(act=wq.WQ_F32) == wq.WQ_ERR_DTYPE
     assert _wqmm(w=wq.WQ_FP8_E4M3) == wq.WQ_ERR_DTYPE
     assert _wqmm(layout=5) == wq.WQ_ERR_UNSUPPORTED
-    assert _wqmm(tx2=1) == wq.WQ_ERR_UNSUPPORTED                    # int4: pack the transpose
+    assert _wqmm(tx2=1) == wq.WQ_ERR_UNSUPPORTED                    # GFX950_B: pack the transpose
+    assert _wqmm(tx2=1, layout=wq.WQ_LAYOUT_ND, k=255) == wq.WQ_ERR_SHAPE   # (n, k/2) needs k even
     assert _wqmm(w=wq.WQ_INT8) == wq.WQ_ERR_UNSUPPORTED             # int8 in GFX950_B
 
 

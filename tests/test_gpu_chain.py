@@ -77,6 +77,22 @@ def test_weight_quant_matmul(case):
     assert torch.equal(out.cpu(), y.cpu().reshape(m, n))
 
 
+@pytest.mark.parametrize("act", [torch.bfloat16, torch.float16])
+def test_weight_quant_matmul_int4_transposed(act):
+    # x2 given transposed: (n, k) INT4 codes packed along k, ND layout
+    c = workloads.wq_case("wqbmmT", 70, 640, 150, act=act, w_bits=4, granularity="group",
+                          group_size=64, offset_range=(-0.5, 0.5), bias_std=0.1, seed=77)
+    m, k, n = c.mkn
+    note(f"standalone wq matmul int4 transposed ND {m}x{k}x{n} {act}")
+    x2 = wq.pack_int4(c.w.to(DEV).t().contiguous(), ND)
+    assert x2.numel() == n * k // 2
+    d = lambda t: None if t is None else t.to(DEV)
+    out = wq.weight_quant_matmul(c.x1.to(DEV).reshape(m, k), x2, k, n, wq.WQ_INT4, d(c.scale),
+                                 d(c.offset), c.group_size, d(c.bias), layout=ND, transpose_x2=True)
+    torch.cuda.synchronize()
+    _check(out.cpu(), _oracle_mm(c), "int4 transposed")
+
+
 def test_weight_quant_matmul_w8():
     c = workloads.w8()
     note("standalone wq matmul w8 per-channel")

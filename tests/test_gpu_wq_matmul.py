@@ -77,6 +77,21 @@ def test_edge_shapes_int4(shape, layout):
     check_wq(c, y, nrm)
 
 
+@pytest.mark.parametrize("shape", SHAPES + [(300, 1024, 200, "group", 128, (-0.5, 0.5), 0.1,
+                                              torch.bfloat16)],
+                         ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}" for s in SHAPES] + ["300x1024x200"])
+def test_edge_shapes_int4_transposed(shape):
+    # x2 given transposed, (n, k) packed along k (ND only)
+    m, k, n, gran, g, off, bias, act = shape
+    if k % 2:
+        pytest.skip("the transposed ND weight packs pairs along k")
+    c = workloads.wq_case(f"edgeT{m}x{k}x{n}", m, k, n, act=act, w_bits=4, granularity=gran,
+                          group_size=g, offset_range=off, bias_std=bias, seed=3 * m + k + n)
+    note(f"wq edge int4 transposed ND {c.name} {gran} g={g}")
+    y, nrm = wq_on_gpu(c, ND, transpose_x2=True)
+    check_wq(c, y, nrm)
+
+
 @pytest.mark.parametrize("shape", SHAPES[:4], ids=[f"{s[0]}x{s[1]}x{s[2]}" for s in SHAPES[:4]])
 @pytest.mark.parametrize("transpose", [False, True])
 def test_edge_shapes_int8(shape, transpose):
