@@ -41,7 +41,7 @@ EXPORTS = (
     "wq_dynamic_quant",
     "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
     "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
-    "wq_quant_matmul_inplace_add",
+    "wq_quant_matmul_inplace_add", "wq_quant_matmul_inplace_add_w4",
     "mx_fp4_quant_matmul_inplace_add_workspace_size", "mx_fp4_quant_matmul_inplace_add",
     "wq_weight_quant_matmul_workspace_size", "wq_weight_quant_matmul", "wq_add_rms_norm",
     "wq_profile_enable", "wq_profile_read",
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
             "wq_quant_matmul_inplace_add": (I, [P, P, P, P, I64, I64, I64, P, P]),
+            "wq_quant_matmul_inplace_add_w4": (I, [P, P, I, P, P, I64, I64, I64, P, P]),
             "mx_fp4_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_fp4_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I64, P, P, S, P]),
             "wq_weight_quant_matmul_workspace_size": (S, [I64, I64, I64]),
@@ -148,6 +149,13 @@ def wq_quant_matmul_inplace_add(x1, x2, x1_scale, x2_scale, m, k, n, y, stream=N
     st = lib().wq_quant_matmul_inplace_add(_ptr(x1), _ptr(x2), _ptr(x1_scale), _ptr(x2_scale), m, k,
                                            n, _ptr(y), _stream(stream))
     return _check(st, "wq_quant_matmul_inplace_add", check)
+
+
+def wq_quant_matmul_inplace_add_w4(x1, x2, x2_layout, x1_scale, x2_scale, m, k, n, y, stream=None,
+                                   check=True) -> int:
+    st = lib().wq_quant_matmul_inplace_add_w4(_ptr(x1), _ptr(x2), x2_layout, _ptr(x1_scale),
+                                              _ptr(x2_scale), m, k, n, _ptr(y), _stream(stream))
+    return _check(st, "wq_quant_matmul_inplace_add_w4", check)
 
 
 def wq_profile_enable(enable: bool, check=True) -> int:
@@ -307,6 +315,18 @@ def quant_matmul_inplace_add(x1: torch.Tensor, x2_t: torch.Tensor, x1_scale: tor
     m, k = x1.shape
     n = x2_t.shape[0]
     wq_quant_matmul_inplace_add(x1, x2_t, x1_scale, x2_scale, m, k, n, y, stream)
+    return y
+
+
+def quant_matmul_inplace_add_w4(x1: torch.Tensor, x2_packed: torch.Tensor, n: int,
+                                x1_scale: torch.Tensor, x2_scale: torch.Tensor, y: torch.Tensor,
+                                stream=None) -> torch.Tensor:
+    """y += (x1 @ q) * x1_scale[:, None] * x2_scale[None, :] with INT8 x1
+    (m, k), INT4 codes q (k, n) packed in GFX950_B, float32 scales and y
+    (m, n) updated in place."""
+    m, k = x1.shape
+    wq_quant_matmul_inplace_add_w4(x1, x2_packed, WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n,
+                                   y, stream)
     return y
 
 

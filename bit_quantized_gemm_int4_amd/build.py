@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_profile.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
            "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip", "add_rmsnorm.hip",
-           "mx4_gemm.hip"]
+           "mx4_gemm.hip", "a8w4_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -39,13 +39,13 @@ FLAGS = [
 FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               # the INT8 epilogue rounds each float step on its own, as its
               # reading of the formula fixes: no fused multiply-add
-              "i8_gemm.hip": ["-ffp-contract=off"]}
+              "i8_gemm.hip": ["-ffp-contract=off"], "a8w4_gemm.hip": ["-ffp-contract=off"]}
 
 
 # Sources with MFMA kernels: their device assembly is checked for MFMA
 # destinations that partially overlap a source operand (codegen_check).
 MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip",
-                "mx4_gemm.hip"]
+                "mx4_gemm.hip", "a8w4_gemm.hip"]
 
 
 def _compile(src: str) -> str:

@@ -90,6 +90,18 @@ struct I8Problem {
 
 hipError_t launch_i8_matmul(const I8Problem& p, hipStream_t s);
 
+// INT8 x INT4 (GFX950_B) quantized matmul with in-place add (a8w4_gemm.hip).
+struct A8W4Problem {
+  const int8_t* x1;      // (m, k)
+  const uint8_t* x2;     // INT4 codes, logical (k, n), GFX950_B
+  const float* s1;       // (m)
+  const float* s2;       // (n)
+  float* y;              // (m, n)
+  int64_t m, k, n;
+};
+
+hipError_t launch_a8w4_matmul(const A8W4Problem& p, hipStream_t s);
+
 // MXFP4 x MXFP4 with in-place add (mx4_gemm.hip). The workspace holds the
 // scales rearranged for the lanes (mx4_workspace_bytes).
 struct Mx4Problem {

@@ -2,13 +2,15 @@
  * wq.h - C ABI of libwq: weight-quantized matmul + AddRmsNorm and its
  * companions, written for AMD Instinct MI355X (gfx950).
  *
- * Four operators, each following one operator page:
+ * The operators, each following one operator page:
  *   wq_pack_int4                  aclnnConvertWeightToINT4Pack
  *   wq_dynamic_quant              aclnnDynamicQuant (plus an MX block-32 mode)
  *   wq_matmul_add_rmsnorm         aclnnWeightQuantMatmulAllReduceAddRmsNorm
  *                                 (single device: the AllReduce is the identity)
  *   mx_quant_matmul_inplace_add   aclnnQuantBatchMatmulInplaceAdd (mx)
  *   mx_fp4_quant_matmul_inplace_add  the same, both operands MXFP4
+ *   wq_quant_matmul_inplace_add      the same Formula, INT8 x INT8 (A8W8)
+ *   wq_quant_matmul_inplace_add_w4   the same Formula, INT8 x packed INT4 (A8W4)
  *   wq_pack_fp4                   aclnnConvertWeightToINT4Pack (FLOAT -> E2M1)
  *   wq_weight_quant_matmul        \ the unfused chain that the fused operator's
  *   wq_add_rms_norm               / page names as its replacement
@@ -350,6 +352,34 @@ wq_status mx_quant_matmul_inplace_add(
 wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const float* x1_scale,
                                       const float* x2_scale, int64_t m, int64_t k, int64_t n,
                                       float* y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * INT8 x INT4 quantized matmul with in-place add (A8W4): the same Formula
+ * and roundings as wq_quant_matmul_inplace_add, with x2 given as INT4 codes
+ * packed by wq_pack_int4 (aclnnConvertWeightToINT4Pack page):
+ *
+ *   y[m,n] = (sum_k x1[m,k] * q[k,n]) * (x1_scale[m] * x2_scale[n]) + y[m,n]
+ *
+ * x1: int8 (m, k) row-major (wq_dynamic_quant's per-token INT8 output);
+ *     x1_scale: float32 (m).
+ * x2: the codes q in [-8, 7], logical (k, n), in WQ_LAYOUT_GFX950_B
+ *     (wq_pack_int4_bytes(k, n, layout) bytes, under 2^31); ND is
+ *     WQ_ERR_UNSUPPORTED. x2_scale: float32 (n).
+ * y:  float32 (m, n) row-major, read and written in place.
+ * The sum over k is exact (int32); then s = x1_scale[m] * x2_scale[n],
+ * t = float(sum) * s, y = y + t, each rounded to nearest even in float32.
+ * Device pointers owned by the caller; x1 and x2 16-byte aligned, the scales
+ * and y 4-byte aligned; y must not overlap an input. No workspace. m == 0 or
+ * n == 0 is an empty no-op.
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (m < 0, n outside [0, 65535], k
+ * outside [1, 65535] or not a multiple of 16, misaligned pointers, a weight
+ * of 2^31 bytes or more); WQ_ERR_UNSUPPORTED (x2_layout not GFX950_B);
+ * WQ_ERR_ALIAS (y overlapping an input).
+ * ---------------------------------------------------------------------- */
+wq_status wq_quant_matmul_inplace_add_w4(const void* x1, const void* x2, wq_layout x2_layout,
+                                         const float* x1_scale, const float* x2_scale,
+                                         int64_t m, int64_t k, int64_t n, float* y,
+                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Profiling of the contraction kernels (a measurement aid, not part of any

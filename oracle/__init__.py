@@ -22,7 +22,7 @@ from .pack import (pack_int4_nd, unpack_int4_nd, pack_int4_gfx950b,
 from .quant import dynamic_quant_per_token, dynamic_quant_mx, unpack_quant_output
 from .wq_matmul import dequantize_weight, wq_matmul_add_rmsnorm, weight_quant_matmul, add_rms_norm
 from .mx_matmul import decode_group_size, mx_quant_matmul_inplace_add, mxfp4_quant_matmul_inplace_add
-from .int8_matmul import quant_matmul_inplace_add_int8
+from .int8_matmul import quant_matmul_inplace_add_int8, quant_matmul_inplace_add_w4
 from .compare import rel_err_floor, as_f64
 
 __all__ = [
@@ -34,4 +34,5 @@ __all__ = [
     "dequantize_weight", "wq_matmul_add_rmsnorm", "weight_quant_matmul", "add_rms_norm",
     "decode_group_size", "mx_quant_matmul_inplace_add", "mxfp4_quant_matmul_inplace_add", "quant_matmul_inplace_add_int8",
     "rel_err_floor", "as_f64",
+    "quant_matmul_inplace_add_w4",
 ]

@@ -40,3 +40,17 @@ def quant_matmul_inplace_add_int8(x1, x2_t, scale1, scale2, y):
     # int64 -> float64 is exact below 2^53, so this is one rounding to float32
     t = (acc.astype(np.float64).astype(np.float32) * s).astype(np.float32)
     return (np.asarray(y, dtype=np.float32) + t).astype(np.float32)
+
+
+def quant_matmul_inplace_add_w4(x1, x2_codes, scale1, scale2, y):
+    """A8W4: the same formula and roundings with x2 an INT4 weight. x1 (M, K)
+    int8 values; x2_codes (K, N) the INT4 codes in [-8, 7] as the pack takes
+    them (aclnnConvertWeightToINT4Pack page: the packed layout is storage
+    only, the values are the codes); scale1 (M), scale2 (N) float32; y (M, N)
+    float32. Returns the updated y as float32."""
+    q = np.asarray(x2_codes, dtype=np.int64)
+    if q.ndim != 2:
+        raise ValueError("x2_codes is (K, N)")
+    if q.size and (q.min() < -8 or q.max() > 7):
+        raise ValueError("INT4 codes lie in [-8, 7]")
+    return quant_matmul_inplace_add_int8(x1, q.T, scale1, scale2, y)

@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -211,6 +211,32 @@ def test_int8_matmul_validation():
     assert _qmm(y=FAKE + 0x40000002) == wq.WQ_ERR_SHAPE    # float alignment
     assert _qmm(y=FAKE + 64) == wq.WQ_ERR_ALIAS            # y over x1
     assert _qmm(m=0) == wq.WQ_OK and _qmm(n=0) == wq.WQ_OK
+
+
+def _w4mm(**kw):
+    a = dict(x1=FAKE, x2=FAKE2, layout=wq.WQ_LAYOUT_GFX950_B, s1=FAKE3, s2=FAKE3 + 0x4000, m=32,
+             k=64, n=48, y=FAKE + 0x40000000, stream=0)
+    a.update(kw)
+    return wq.lib().wq_quant_matmul_inplace_add_w4(a["x1"], a["x2"], a["layout"], a["s1"], a["s2"],
+                                                   a["m"], a["k"], a["n"], a["y"], a["stream"])
+
+
+def test_a8w4_matmul_validation():
+    assert _w4mm(layout=wq.WQ_LAYOUT_ND) == wq.WQ_ERR_UNSUPPORTED
+    assert _w4mm(k=0) == wq.WQ_ERR_SHAPE
+    assert _w4mm(k=40) == wq.WQ_ERR_SHAPE                  # k % 16
+    assert _w4mm(k=65536) == wq.WQ_ERR_SHAPE
+    assert _w4mm(n=65536) == wq.WQ_ERR_SHAPE
+    assert _w4mm(m=-1) == wq.WQ_ERR_SHAPE
+    assert _w4mm(x1=None) == wq.WQ_ERR_NULLPTR
+    assert _w4mm(s1=None) == wq.WQ_ERR_NULLPTR
+    assert _w4mm(x2=FAKE2 + 8) == wq.WQ_ERR_SHAPE          # 16-byte weight records
+    assert _w4mm(y=FAKE + 0x40000002) == wq.WQ_ERR_SHAPE   # float alignment
+    # the packed weight of k = 65520, n = 65535 is 512 * 65536 * 64 = 2^31 bytes
+    assert wq.wq_pack_int4_bytes(65520, 65535, wq.WQ_LAYOUT_GFX950_B) == 1 << 31
+    assert _w4mm(k=65520, n=65535) == wq.WQ_ERR_SHAPE
+    assert _w4mm(y=FAKE2 + 64) == wq.WQ_ERR_ALIAS          # y over x2
+    assert _w4mm(m=0) == wq.WQ_OK and _w4mm(n=0) == wq.WQ_OK
 
 
 def _wqbmm(**kw):

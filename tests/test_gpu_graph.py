@@ -149,7 +149,7 @@ def test_w8_call_replays():
 
 
 def test_dynamic_quant_and_pack_replay():
-    note("graph: dynamic quant (per token int8, MX e4m3) and pack")
+    note("graph: dynamic quant (per token int8, MX e4m3 and e2m1) and pack (int4, fp4)")
     rng = np.random.default_rng(3)
     x = torch.from_numpy(rng.standard_normal((300, 1024))).to(torch.float16).to(DEV)
     sm = torch.from_numpy(rng.uniform(0.5, 2, 1024)).to(torch.float16).to(DEV)
@@ -159,30 +159,39 @@ def test_dynamic_quant_and_pack_replay():
     qmx = torch.empty((1024, 300), dtype=torch.uint8, device=DEV)
     smx = torch.empty((300, 32), dtype=torch.uint8, device=DEV)
     pk = torch.empty(wq.wq_pack_int4_bytes(512, 768, B), dtype=torch.uint8, device=DEV)
+    q4 = torch.empty((300, 512), dtype=torch.uint8, device=DEV)
+    s4 = torch.empty((300, 32), dtype=torch.uint8, device=DEV)
+    wf = torch.from_numpy(rng.standard_normal((512, 768)).astype(np.float32) * 3).to(DEV)
+    pf = torch.empty(wq.wq_pack_int4_bytes(512, 768, B), dtype=torch.uint8, device=DEV)
 
     def fn():
         wq.wq_dynamic_quant(x, wq.WQ_F16, 300, 1024, sm, wq.WQ_INT8, 0, 0, q8, s8)
         wq.wq_dynamic_quant(x, wq.WQ_F16, 300, 1024, sm, wq.WQ_FP8_E4M3, 32, 1, qmx, smx)
+        wq.wq_dynamic_quant(x, wq.WQ_F16, 300, 1024, sm, wq.WQ_FP4_E2M1, 32, 0, q4, s4)
         wq.wq_pack_int4(w, 512, 768, 0, B, pk)
+        wq.wq_pack_fp4(wf, 512, 768, 0, B, pf)
+    outs = (q8, s8, qmx, smx, q4, s4, pk, pf)
     fn()
     torch.cuda.synchronize()
-    want = [t.clone() for t in (q8, s8, qmx, smx, pk)]
+    want = [t.clone() for t in outs]
     g = _capture(fn)
     for r in range(3):
-        for t in (q8, qmx, smx, pk):
-            t.fill_(0x55)
-        s8.fill_(float("nan"))
+        for t in outs:
+            if t is s8:
+                t.fill_(float("nan"))
+            else:
+                t.fill_(0x55)
         _eager_noise()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip((q8, s8, qmx, smx, pk), want):
+        for a, b in zip(outs, want):
             assert torch.equal(a, b), f"replay {r}"
 
 
 def test_inplace_accumulators_replay():
-    # MX and INT8 add into y: replay r must equal r + 1 eager calls from the
-    # same start (the warm-up before capture is the first)
-    note("graph: MX and INT8 in-place add, replays accumulate")
+    # MX, INT8, INT8 x INT4 and MXFP4 add into y: replay r must equal r + 1 eager
+    # calls from the same start (the warm-up before capture is the first)
+    note("graph: MX, INT8, A8W4 and MXFP4 in-place add, replays accumulate")
     rng = np.random.default_rng(5)
     m, k, n = 256, 512, 384
     x1 = torch.from_numpy(rng.integers(-127, 128, (m, k), dtype=np.int8)).to(DEV)
@@ -198,19 +207,29 @@ def test_inplace_accumulators_replay():
     mx_s1 = torch.from_numpy(rng.integers(120, 128, (m, k // 32), dtype=np.uint8)).to(DEV)
     mx_s2 = torch.from_numpy(rng.integers(120, 128, (k // 32, n), dtype=np.uint8)).to(DEV)
 
-    y_i8, y_mx = y0.clone(), y0.clone()
+    # MXFP4: E2M1 x1 (m, k/2) bytes and a workspace of its own
+    f4_x1 = torch.from_numpy(rng.integers(0, 256, (m, k // 2), dtype=np.uint8)).to(DEV)
+    ws4 = torch.empty(wq.mx_fp4_quant_matmul_inplace_add_workspace_size(m, k, n), dtype=torch.uint8,
+                      device=DEV)
+
+    y_i8, y_mx, y_w4, y_f4 = y0.clone(), y0.clone(), y0.clone(), y0.clone()
 
     def fn():
         wq.quant_matmul_inplace_add(x1, x2, s1, s2, y_i8)
         wq.mx_matmul_inplace_add(mx_x1, mx_x2, mx_s1, mx_s2, y_mx, m, k, n)
+        # the packed nibbles of mx_x2 read as INT4 codes
+        wq.quant_matmul_inplace_add_w4(x1, mx_x2, n, s1, s2, y_w4)
+        wq.mxfp4_matmul_inplace_add(f4_x1, mx_x2, mx_s1, mx_s2, y_f4, m, k, n, workspace=ws4)
 
     # eager sequence on copies
-    e_i8, e_mx = y0.clone(), y0.clone()
+    e_i8, e_mx, e_w4, e_f4 = y0.clone(), y0.clone(), y0.clone(), y0.clone()
     seq = []
     for _ in range(4):
         wq.quant_matmul_inplace_add(x1, x2, s1, s2, e_i8)
         wq.mx_matmul_inplace_add(mx_x1, mx_x2, mx_s1, mx_s2, e_mx, m, k, n)
-        seq.append((e_i8.clone(), e_mx.clone()))
+        wq.quant_matmul_inplace_add_w4(x1, mx_x2, n, s1, s2, e_w4)
+        wq.mxfp4_matmul_inplace_add(f4_x1, mx_x2, mx_s1, mx_s2, e_f4, m, k, n, workspace=ws4)
+        seq.append((e_i8.clone(), e_mx.clone(), e_w4.clone(), e_f4.clone()))
     torch.cuda.synchronize()
     g = _capture(fn)                       # the warm-up ran once on y_i8 / y_mx
     for r in range(3):
@@ -219,6 +238,8 @@ def test_inplace_accumulators_replay():
         torch.cuda.synchronize()
         assert torch.equal(y_i8, seq[r + 1][0]), f"int8 replay {r}"
         assert torch.equal(y_mx, seq[r + 1][1]), f"mx replay {r}"
+        assert torch.equal(y_w4, seq[r + 1][2]), f"a8w4 replay {r}"
+        assert torch.equal(y_f4, seq[r + 1][3]), f"mxfp4 replay {r}"
 
 
 def test_unfused_chain_replays():
