@@ -14,9 +14,9 @@
 // operand instead). The rank-1 remainder sum_g rowsum_g(x) (o_g - 136 s_g) is
 // added at the end with MFMAs over the group axis on bf16 hi/lo splits of
 // both factors (three products; relative error ~2^-16 of a term that is a
-// small multiple of the result). Two pre-passes produce those factors: the
-// per-group row sums of x1 and the per-group column corrections, both stored
-// in MFMA operand order.
+// small multiple of the result). One pre-pass launch produces those factors:
+// the per-group row sums of x1 and the per-group column corrections, both
+// stored in MFMA operand order.
 //
 // Tile: 128 (m) x 512 (n) per workgroup of 8 waves, each wave 128 x 64 (8 x 4
 // MFMA 16x16x32 tiles), two waves per SIMD. Wide N because the 4-bit weight is
@@ -56,75 +56,104 @@ struct FastArgs {
   int64_t s_row, s_col;
   int64_t groups, gp;      // groups = ceil(k / group); gp = 32 * ceil(groups / 32)
   uint32_t s_bytes;        // extent of the scale tensor in bytes
-  uint32_t* zflag;         // [ceil(np / 512)] nonzero: a zero group scale in that column strip
+  const uint32_t* zflag;   // [ceil(np / 64)][ngb] nonzero: a zero scale in that 64-column x 32-group tile
+  int ngb;                 // group tiles: gp / 32
 };
 
 // ---------------------------------------------------------------------------
-// Pre-pass 1: per-group row sums of x1, written as bf16 hi/lo (zero padded to
-// gp groups). One workgroup per row; eight-element chunk sums in LDS, then
-// each group summed in a fixed order.
+// Pre-pass (one launch): the per-group row sums of x1 and the per-group
+// column corrections, both written as bf16 hi/lo in MFMA operand order.
+//   blocks [0, m): row b's sums, [m][2][gp] (zero padded to gp groups): eight-
+//     element chunk sums in LDS (each thread's loads issued together), then
+//     each group summed in a fixed order;
+//   blocks [m, m + ncb * ngb): a tile of 64 columns x 32 groups of
+//     o[g][n] - bias * s[g][n] (zero for padding), [np][2][gp]: read along the
+//     columns (coalesced), transposed through LDS, written along the groups.
+//     The tile also writes one word, nonzero when one of its scales is zero
+//     (zflag[ci * ngb + gi]); the main tile ORs the words of its strip.
 // ---------------------------------------------------------------------------
-template <int ACT>
-__global__ __launch_bounds__(256) void group_rowsum_kernel(const uint16_t* __restrict__ x1, int64_t k,
-                                                           int64_t group, int64_t groups, int64_t gp,
-                                                           uint16_t* __restrict__ rs,
-                                                           uint32_t* __restrict__ zflag, int nstrips) {
-  extern __shared__ float chunk_sum[];        // k / 8 floats
-  const int64_t row = blockIdx.x;
-  if (row == 0)                               // cleared here, set by the correction pass
-    for (int i = threadIdx.x; i < nstrips; i += 256) zflag[i] = 0u;
-  const uint16_t* xr = x1 + row * k;
-  const int64_t chunks = k / 8;
-  for (int64_t c = threadIdx.x; c < chunks; c += 256) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * c);
-    float s = lo_f32<ACT>(v.x) + hi_f32<ACT>(v.x);
-    s += lo_f32<ACT>(v.y) + hi_f32<ACT>(v.y);
-    s += lo_f32<ACT>(v.z) + hi_f32<ACT>(v.z);
-    s += lo_f32<ACT>(v.w) + hi_f32<ACT>(v.w);
-    chunk_sum[c] = s;
-  }
-  __syncthreads();
-  const int64_t per = group / 8;               // chunks per group
-  for (int64_t g = threadIdx.x; g < gp; g += 256) {
-    float s = 0.f;
-    if (g < groups) {
-      const int64_t c1 = (g + 1) * per < chunks ? (g + 1) * per : chunks;
-      for (int64_t c = g * per; c < c1; ++c) s += chunk_sum[c];
-    }
-    uint16_t hi, lo;
-    split_bf16(s, hi, lo);
-    rs[row * 2 * gp + g] = hi;
-    rs[row * 2 * gp + gp + g] = lo;
-  }
-}
+constexpr int PC_COLS = 64, PC_GROUPS = 32;
 
-// ---------------------------------------------------------------------------
-// Pre-pass 2: per-group column corrections o[g][n] - bias * s[g][n] (zero for
-// padding), written [np][2][gp] as bf16 hi/lo. One thread per (column, group).
-// Also flags each 512-column strip that holds a zero group scale.
-// ---------------------------------------------------------------------------
 template <int ACT>
-__global__ __launch_bounds__(256) void group_corr_kernel(const uint16_t* __restrict__ scale,
-                                                         const uint16_t* __restrict__ offset,
-                                                         int64_t n, int64_t np, int64_t groups,
-                                                         int64_t gp, int64_t s_row, int64_t s_col,
-                                                         uint16_t* __restrict__ corr,
-                                                         uint32_t* __restrict__ zflag) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= np * gp) return;
-  const int64_t col = idx / gp, g = idx % gp;
-  float c = 0.f;
-  if (col < n && g < groups) {
-    const int64_t si = g * s_row + col * s_col;
-    const float sv = to_f32<ACT>(scale[si]);
-    const float ov = offset ? to_f32<ACT>(offset[si]) : 0.f;
-    c = ov - Magic<ACT>::bias * sv;
-    if (sv == 0.f) atomicOr(&zflag[col / 512], 1u);   // the main tile's strip width
+__global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__ x1, int64_t m, int64_t k,
+                                                    int64_t group, int64_t groups, int64_t gp,
+                                                    uint16_t* __restrict__ rs,
+                                                    const uint16_t* __restrict__ scale,
+                                                    const uint16_t* __restrict__ offset, int64_t n,
+                                                    int64_t np, int64_t s_row, int64_t s_col, int ngb,
+                                                    uint16_t* __restrict__ corr,
+                                                    uint32_t* __restrict__ zflag) {
+  extern __shared__ float sh[];               // max(k / 8, 32 * 65) floats
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  if (b < m) {
+    const int64_t row = b;
+    const uint16_t* xr = x1 + row * k;
+    const int64_t chunks = k / 8;
+    for (int64_t c0 = 0; c0 < chunks; c0 += 1024) {
+      u32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + t + 256 * i;
+        v[i] = c < chunks ? *reinterpret_cast<const u32x4*>(xr + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + t + 256 * i;
+        float s = lo_f32<ACT>(v[i].x) + hi_f32<ACT>(v[i].x);
+        s += lo_f32<ACT>(v[i].y) + hi_f32<ACT>(v[i].y);
+        s += lo_f32<ACT>(v[i].z) + hi_f32<ACT>(v[i].z);
+        s += lo_f32<ACT>(v[i].w) + hi_f32<ACT>(v[i].w);
+        if (c < chunks) sh[c] = s;
+      }
+    }
+    __syncthreads();
+    const int64_t per = group / 8;             // chunks per group
+    for (int64_t g = t; g < gp; g += 256) {
+      float s = 0.f;
+      if (g < groups) {
+        const int64_t c1 = (g + 1) * per < chunks ? (g + 1) * per : chunks;
+        for (int64_t c = g * per; c < c1; ++c) s += sh[c];
+      }
+      uint16_t hi, lo;
+      split_bf16(s, hi, lo);
+      rs[row * 2 * gp + g] = hi;
+      rs[row * 2 * gp + gp + g] = lo;
+    }
+    return;
   }
-  uint16_t hi, lo;
-  split_bf16(c, hi, lo);
-  corr[col * 2 * gp + g] = hi;
-  corr[col * 2 * gp + gp + g] = lo;
+  const int64_t cb = b - m;
+  const int64_t ci = cb / ngb, gi = cb % ngb;
+  float (*tile)[PC_COLS + 1] = reinterpret_cast<float (*)[PC_COLS + 1]>(sh);
+  int zero = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int gl = t / PC_COLS + 4 * i, cl = t % PC_COLS;
+    const int64_t col = ci * PC_COLS + cl, g = gi * PC_GROUPS + gl;
+    float c = 0.f;
+    if (col < n && g < groups) {
+      const int64_t si = g * s_row + col * s_col;
+      const float sv = to_f32<ACT>(scale[si]);
+      const float ov = offset ? to_f32<ACT>(offset[si]) : 0.f;
+      c = ov - Magic<ACT>::bias * sv;
+      zero |= sv == 0.f;
+    }
+    tile[gl][cl] = c;
+  }
+  zero = __syncthreads_or(zero);
+  if (t == 0) zflag[cb] = zero ? 1u : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = t + 256 * i;
+    const int cl = idx / PC_GROUPS, gl = idx % PC_GROUPS;
+    const int64_t col = ci * PC_COLS + cl, g = gi * PC_GROUPS + gl;
+    if (col < np) {
+      uint16_t hi, lo;
+      split_bf16(tile[gl][cl], hi, lo);
+      corr[col * 2 * gp + g] = hi;
+      corr[col * 2 * gp + gp + g] = lo;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -550,7 +579,11 @@ __global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_
   // A tile with a zero group scale somewhere in its columns (flagged by the
   // correction pre-pass) or with columns past n runs the masked variant;
   // the branch is taken once, outside the K loop.
-  const bool masked = n0 + WD_BN > a.n || a.zflag[n0 / WD_BN] != 0;
+  uint32_t zf = 0;
+  const int64_t c_end = (a.np + PC_COLS - 1) / PC_COLS;
+  for (int64_t ci = n0 / PC_COLS; ci < n0 / PC_COLS + WD_BN / PC_COLS && ci < c_end; ++ci)
+    for (int gi = 0; gi < a.ngb; ++gi) zf |= a.zflag[ci * a.ngb + gi];
+  const bool masked = n0 + WD_BN > a.n || zf != 0;
   if (masked) wide_body<ACT, EVERY, true>(a, m0, n0, abuf0, abuf1, wbuf0, wbuf1);
   else wide_body<ACT, EVERY, false>(a, m0, n0, abuf0, abuf1, wbuf0, wbuf1);
 }
@@ -578,17 +611,17 @@ hipError_t launch_wide_t(const WqProblem& p, float* partial, uint16_t* rs, uint1
   a.groups = (p.k + a.group - 1) / a.group;
   a.gp = 32 * ((a.groups + 31) / 32);
   a.s_bytes = (uint32_t)(((a.groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
-  const int nstrips = (int)((a.np + WD_BN - 1) / WD_BN);
-  a.zflag = reinterpret_cast<uint32_t*>(corr + a.np * 2 * a.gp);
-  group_rowsum_kernel<ACT><<<dim3((unsigned)p.m), 256, (size_t)(p.k / 8) * sizeof(float), s>>>(
-      a.x1, p.k, a.group, a.groups, a.gp, rs, a.zflag, nstrips);
+  a.ngb = (int)(a.gp / PC_GROUPS);
+  uint32_t* zflag = reinterpret_cast<uint32_t*>(corr + a.np * 2 * a.gp);
+  a.zflag = zflag;
+  const int64_t ncb = (a.np + PC_COLS - 1) / PC_COLS;
+  const int64_t blocks = p.m + ncb * a.ngb;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int64_t sh_floats = p.k / 8 > PC_GROUPS * (PC_COLS + 1) ? p.k / 8 : PC_GROUPS * (PC_COLS + 1);
+  prefill_prep<ACT><<<dim3((unsigned)blocks), 256, (size_t)sh_floats * sizeof(float), s>>>(
+      a.x1, p.m, p.k, a.group, a.groups, a.gp, rs, a.scale, static_cast<const uint16_t*>(p.offset),
+      p.n, a.np, p.s_row, p.s_col, a.ngb, corr, zflag);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t cells = a.np * a.gp;
-  group_corr_kernel<ACT><<<dim3((unsigned)((cells + 255) / 256)), 256, 0, s>>>(
-      a.scale, static_cast<const uint16_t*>(p.offset), p.n, a.np, a.groups, a.gp, p.s_row,
-      p.s_col, corr, a.zflag);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tm = (p.m + WD_BM - 1) / WD_BM, tn = (p.n + WD_BN - 1) / WD_BN;
   prof_begin(s);
@@ -613,12 +646,13 @@ size_t fast_rowsum_bytes(int64_t m, int64_t k) {
   const int64_t gp = 32 * ((groups + 31) / 32);
   return ((size_t)(m * 2 * gp * 2) + 255) & ~(size_t)255;
 }
-// ... followed by the zero-scale flags of the 512-column strips
+// ... followed by the zero-scale flags of the 64-column x 32-group tiles
 size_t fast_corr_bytes(int64_t n, int64_t k) {
   const int64_t groups = (k + 127) / 128;
   const int64_t gp = 32 * ((groups + 31) / 32);
   const int64_t np = 16 * ((n + 15) / 16);
-  return ((size_t)(np * 2 * gp * 2 + (np + WD_BN - 1) / WD_BN * 4) + 255) & ~(size_t)255;
+  const int64_t flags = (np + PC_COLS - 1) / PC_COLS * (gp / PC_GROUPS);
+  return ((size_t)(np * 2 * gp * 2 + flags * 4) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint16_t* corr,
