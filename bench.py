@@ -16,7 +16,9 @@ own with the same warm-up and step counts, reported under ``extras``:
   wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 3's output)
                            x INT8 weight (4096, 8192), per-token x per-channel
   wq_quant_matmul_inplace_add_w4  the same with an INT4 weight: row 5's packed
-                           GFX950_B weight read as INT4 codes (8192, 4096)
+                           GFX950_B weight read as INT4 codes (8192, 4096);
+                           and with INT4 activations (the per-token INT4
+                           quant of the same x, made before timing)
   wq_dynamic_quant         MX E2M1 (row-major) + E8M0 of the same x
   mx_fp4_quant_matmul_inplace_add  y (4096, 4096) fp32 += E2M1 x row 5's
                            E2M1 weight, at the FP4 rate
@@ -57,7 +59,8 @@ CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "weight_quant_matmul
                     "mx_matmul_inplace_add": "mx_gemm_tile",
                     "quant_matmul_inplace_add_int8": "i8_gemm_tile",
                     "mxfp4_matmul_inplace_add": "mx4_gemm_tile",
-                    "quant_matmul_inplace_add_w4": "a8w4_gemm_tile"}
+                    "quant_matmul_inplace_add_w4": "a8w4_gemm_tile",
+                    "quant_matmul_inplace_add_a4w4": "a8w4_gemm_tile"}
 COPY_BYTES = 256 << 20         # calibration copy (--only copy)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
 
@@ -214,7 +217,19 @@ def main():
     def op_w4():
         # A8W4: the same INT8 activations times the packed MX weight's nibbles
         # read as INT4 codes (GFX950_B, logical (8192, 4096))
-        wq.wq_quant_matmul_inplace_add_w4(q8, x2mx, wq.WQ_LAYOUT_GFX950_B, q8s, w8s, MM, MK, MN, yw4)
+        wq.wq_quant_matmul_inplace_add_w4(q8, wq.WQ_INT8, x2mx, wq.WQ_LAYOUT_GFX950_B, q8s, w8s, MM, MK,
+                                          MN, yw4)
+
+    # A4W4: the per-token INT4 quant of the same x (made once here), times the
+    # same INT4 weight
+    q4 = torch.empty((MM, MK // 2), dtype=torch.uint8, device=dev)
+    q4s = torch.empty(MM, dtype=torch.float32, device=dev)
+    wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_INT4, 0, 0, q4, q4s)
+    ya4 = y8.clone()
+
+    def op_a4w4():
+        wq.wq_quant_matmul_inplace_add_w4(q4, wq.WQ_INT4, x2mx, wq.WQ_LAYOUT_GFX950_B, q4s, w8s, MM, MK,
+                                          MN, ya4)
 
     # the INT8 GEMM and the FP4 GEMM read the quants' outputs: fill them once
     # here so that every row runs on defined inputs whatever --only selects
@@ -238,6 +253,8 @@ def main():
          MM * MK + MN * MK + MM * 4 + MN * 4 + 2 * MM * MN * 4, "mfma"),
         ("quant_matmul_inplace_add_w4", op_w4, 2 * MM * MN * MK,
          MM * MK + x2mx.numel() + MM * 4 + MN * 4 + 2 * MM * MN * 4, "mfma"),
+        ("quant_matmul_inplace_add_a4w4", op_a4w4, 2 * MM * MN * MK,
+         MM * MK // 2 + x2mx.numel() + MM * 4 + MN * 4 + 2 * MM * MN * 4, "mfma"),
         ("dynamic_quant_mx_e2m1", op_quant_f4, 0, MM * MK * 2 + MK * 2 + MM * MK // 2 + s1f4.numel(), "hbm"),
         ("mxfp4_matmul_inplace_add", op_f4, 2 * MM * MN * MK,
          x1f4.numel() + x2mx.numel() + s1f4.numel() + s2.numel() + 2 * MM * MN * 4, "mfma"),
@@ -247,7 +264,8 @@ def main():
     # and MXFP4 paths) run as extras in a loop of their own, so that their
     # dense GEMMs do not heat the GPU under the step's rows
     EXTRA = {"weight_quant_matmul", "add_rms_norm", "quant_matmul_inplace_add_int8",
-             "quant_matmul_inplace_add_w4", "dynamic_quant_mx_e2m1", "mxfp4_matmul_inplace_add"}
+             "quant_matmul_inplace_add_w4", "quant_matmul_inplace_add_a4w4", "dynamic_quant_mx_e2m1",
+             "mxfp4_matmul_inplace_add"}
     core = [r for r in rows if want(r[0]) and r[0] not in EXTRA]
     extras = [r for r in rows if want(r[0]) and r[0] in EXTRA]
     if "copy" in only:
@@ -316,6 +334,7 @@ def main():
             peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS, "weight_quant_matmul": PEAK_BF16_TFLOPS,
                     "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS,
                     "quant_matmul_inplace_add_w4": PEAK_INT8_TOPS,
+                    "quant_matmul_inplace_add_a4w4": PEAK_INT8_TOPS,
                     "mxfp4_matmul_inplace_add": PEAK_FP4_TFLOPS}.get(name, PEAK_FP8_TFLOPS)
             d["frac_of_peak"] = round((flop / ms / 1e9) / peak if bound == "mfma"
                                       else (nbytes / ms / 1e6) / PEAK_HBM_GBS, 4)

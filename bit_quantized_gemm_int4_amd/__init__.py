@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
             "wq_quant_matmul_inplace_add": (I, [P, P, P, P, I64, I64, I64, P, P]),
-            "wq_quant_matmul_inplace_add_w4": (I, [P, P, I, P, P, I64, I64, I64, P, P]),
+            "wq_quant_matmul_inplace_add_w4": (I, [P, I, P, I, P, P, I64, I64, I64, P, P]),
             "mx_fp4_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_fp4_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I64, P, P, S, P]),
             "wq_weight_quant_matmul_workspace_size": (S, [I64, I64, I64]),
@@ -151,9 +151,9 @@ def wq_quant_matmul_inplace_add(x1, x2, x1_scale, x2_scale, m, k, n, y, stream=N
     return _check(st, "wq_quant_matmul_inplace_add", check)
 
 
-def wq_quant_matmul_inplace_add_w4(x1, x2, x2_layout, x1_scale, x2_scale, m, k, n, y, stream=None,
-                                   check=True) -> int:
-    st = lib().wq_quant_matmul_inplace_add_w4(_ptr(x1), _ptr(x2), x2_layout, _ptr(x1_scale),
+def wq_quant_matmul_inplace_add_w4(x1, x1_dtype, x2, x2_layout, x1_scale, x2_scale, m, k, n, y,
+                                   stream=None, check=True) -> int:
+    st = lib().wq_quant_matmul_inplace_add_w4(_ptr(x1), x1_dtype, _ptr(x2), x2_layout, _ptr(x1_scale),
                                               _ptr(x2_scale), m, k, n, _ptr(y), _stream(stream))
     return _check(st, "wq_quant_matmul_inplace_add_w4", check)
 
@@ -320,13 +320,14 @@ def quant_matmul_inplace_add(x1: torch.Tensor, x2_t: torch.Tensor, x1_scale: tor
 
 def quant_matmul_inplace_add_w4(x1: torch.Tensor, x2_packed: torch.Tensor, n: int,
                                 x1_scale: torch.Tensor, x2_scale: torch.Tensor, y: torch.Tensor,
-                                stream=None) -> torch.Tensor:
-    """y += (x1 @ q) * x1_scale[:, None] * x2_scale[None, :] with INT8 x1
-    (m, k), INT4 codes q (k, n) packed in GFX950_B, float32 scales and y
-    (m, n) updated in place."""
-    m, k = x1.shape
-    wq_quant_matmul_inplace_add_w4(x1, x2_packed, WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n,
-                                   y, stream)
+                                x1_int4: bool = False, stream=None) -> torch.Tensor:
+    """y += (x1 @ q) * x1_scale[:, None] * x2_scale[None, :] with x1 INT8
+    (m, k) or, with ``x1_int4``, INT4 codes packed (m, k/2); INT4 codes q
+    (k, n) packed in GFX950_B; float32 scales; y (m, n) updated in place."""
+    m = x1.shape[0]
+    k = x1.shape[1] * (2 if x1_int4 else 1)
+    wq_quant_matmul_inplace_add_w4(x1, WQ_INT4 if x1_int4 else WQ_INT8, x2_packed,
+                                   WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n, y, stream)
     return y
 
 

@@ -45,7 +45,11 @@ __device__ __forceinline__ void w4_unpack(uint2 raw, i32x4& out) {
   out[3] = (int)(__builtin_amdgcn_perm(s1, w1, 0x03070206u) & 0xF0F0F0F0u);
 }
 
-__global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restrict__ x1,
+// A4: x1 holds INT4 codes (M, K/2) bytes (the per-token quant's INT4 output,
+// even k in the low nibble) and enters the MFMA as 16 * a too: the
+// accumulator holds 256 * sum (256 * 65504 * 8 * 8 < 2^31), shifted back by 8.
+template <bool A4>
+__global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const uint8_t* __restrict__ x1,
                                                          const uint8_t* __restrict__ x2,
                                                          const float* __restrict__ s1,
                                                          const float* __restrict__ s2,
@@ -65,8 +69,26 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
   const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((int)(id % tiles_n)) * W4_BN;
   const int rows_a = (int)(M - m0 < W4_BM ? M - m0 : W4_BM);
   const int cols_b = (int)(N - n0 < W4_BN ? N - n0 : W4_BN);
-  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(x1 + m0 * K, (uint32_t)(rows_a * K));
+  // x1: INT8 rows through the INT8 ring's addressing; INT4 rows (K / 2 bytes)
+  // like the weight, one instruction per wave and stage: lane l fills row
+  // 32 w + l / 2, bytes 16 (l % 2) of the step's 32
+  const int64_t arow_bytes = A4 ? K / 2 : K;
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(x1 + m0 * arow_bytes, (uint32_t)(rows_a * arow_bytes));
   const I8Dma da = i8_dma_setup(rows_a, K);
+  const int arow4 = 32 * wave + (lane >> 1);
+  const uint32_t abase4 = (uint32_t)(arow4 * arow_bytes + 16 * (lane & 1));
+  auto dma_a = [&](int s, uint8_t* buf) {
+    if constexpr (A4) {
+      const bool ok = arow4 < rows_a && (int64_t)s * 32 + 16 * (lane & 1) < arow_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + wave * 1024), 16,
+                                               ok ? abase4 + 32u * (uint32_t)s : BUF_OOB, 0, 0, 0);
+    } else {
+      i8_dma(ra, da, 0, s * I8_BK, buf);
+      i8_dma(ra, da, 1, s * I8_BK, buf);
+    }
+  };
+  // DMA instructions per wave and stage: x1 (2, or 1 for INT4) + weight (1)
+  constexpr int DMA_N = A4 ? 2 : 3;
   // weight DMA: one instruction per wave and stage; lane l fills column
   // 32 w + l / 2 (16 bytes, half l % 2) of the stage, from the column's
   // record of 128-block s / 2, bytes 32 (s % 2) + 16 (l % 2). Columns past the
@@ -96,10 +118,12 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
   // chunk g of its row, for the weight bytes 8 g .. 8 g + 7 of its column's
   // 32 (codes 16 g .. 16 g + 15 in order). Byte i of both operands is K 16 g + i.
   const int g = lane >> 4, r16 = lane & 15;
-  const int a_off = (128 * wm + r16) * I8_BK + 16 * i8_pos(r16, g);
+  const int a_off = A4 ? (128 * wm + r16) * 32 + 8 * g : (128 * wm + r16) * I8_BK + 16 * i8_pos(r16, g);
   const int b_off = (64 * wn + r16) * 32 + 8 * g;
+  uint2 araw[8];
   auto read_a = [&](int i, const uint8_t* buf, i32x4 (&av)[8]) {
-    av[i] = *reinterpret_cast<const i32x4*>(buf + a_off + 16 * i * I8_BK);
+    if constexpr (A4) araw[i] = *reinterpret_cast<const uint2*>(buf + a_off + 16 * i * 32);
+    else av[i] = *reinterpret_cast<const i32x4*>(buf + a_off + 16 * i * I8_BK);
   };
   auto read_b = [&](int j, const uint8_t* buf, uint2 (&raw)[4]) {
     raw[j] = *reinterpret_cast<const uint2*>(buf + b_off + 16 * j * 32);
@@ -114,11 +138,10 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
   for (int st = 0; st < 3; ++st) {
     uint8_t* ab = st == 0 ? a0 : st == 1 ? a1 : a2;
     uint8_t* bb = st == 0 ? b0 : st == 1 ? b1 : b2;
-    i8_dma(ra, da, 0, st * I8_BK, ab);
-    i8_dma(ra, da, 1, st * I8_BK, ab);
+    dma_a(st, ab);
     dma_b(st, bb);
   }
-  wait_vm<6>();                      // this wave's stage 0 (in-order completion)
+  wait_vm<2 * DMA_N>();              // this wave's stage 0 (in-order completion)
   lds_barrier();
   i32x4 pa[8], qa[8], pb[4], qb[4];
   uint2 raw[4];
@@ -128,6 +151,10 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
   for (int j = 0; j < 4; ++j) read_b(j, b0, raw);
 #pragma unroll
   for (int j = 0; j < 4; ++j) w4_unpack(raw[j], pb[j]);
+  if constexpr (A4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w4_unpack(araw[i], pa[i]);
+  }
 
   // step s: stage s's operands are in registers (ca, cb); stage s + 3's
   // buffers were last read before the previous barrier. The first sixteen
@@ -144,12 +171,17 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       mfma(t >> 2, t & 3, ca, cb);
-      if (t == 1) i8_dma(ra, da, 0, (s + 3) * I8_BK, adma);
-      if (t == 3) i8_dma(ra, da, 1, (s + 3) * I8_BK, adma);
-      if (t == 5) dma_b(s + 3, bdma);
+      if constexpr (A4) {
+        if (t == 1) dma_a(s + 3, adma);
+        if (t == 3) dma_b(s + 3, bdma);
+      } else {
+        if (t == 1) i8_dma(ra, da, 0, (s + 3) * I8_BK, adma);
+        if (t == 3) i8_dma(ra, da, 1, (s + 3) * I8_BK, adma);
+        if (t == 5) dma_b(s + 3, bdma);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm<6>();
+    wait_vm<2 * DMA_N>();
     lds_barrier();
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -157,6 +189,9 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
       if (t < 4) read_b(t, bnxt, raw);
       else if (t < 12) read_a(t - 4, anxt, na);
       if (t >= 9 && (t & 1)) w4_unpack(raw[(t - 9) >> 1], nb[(t - 9) >> 1]);
+      if constexpr (A4) {
+        if (t >= 6 && t < 14) w4_unpack(araw[t - 6], na[t - 6]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -204,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const int8_t* __restric
         const int c = 64 * wn + 16 * j + r16;
         const bool ok = row < rows_a && c < cols_b;
         const float sc = __fmul_rn(sc1[r], sc2[j]);
-        const float t = __fmul_rn((float)(acc[i][j][r] >> 4), sc);
+        const float t = __fmul_rn((float)(acc[i][j][r] >> (A4 ? 8 : 4)), sc);
         const float out = __fadd_rn(yv[r][j], t);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ry, ok ? (uint32_t)((row * N + c) * 4) : BUF_OOB, 0, 0);
       }
@@ -219,8 +254,12 @@ hipError_t launch_a8w4_matmul(const A8W4Problem& p, hipStream_t s) {
   const int64_t np = 16 * ((p.n + 15) / 16);
   const uint32_t x2_bytes = (uint32_t)(((p.k + 127) / 128) * np * 64);
   prof_begin(s);
-  a8w4_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
-                                                           np, x2_bytes, tm, tn);
+  if (p.x1_int4)
+    a8w4_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k,
+                                                                   p.n, np, x2_bytes, tm, tn);
+  else
+    a8w4_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m,
+                                                                    p.k, p.n, np, x2_bytes, tm, tn);
   prof_end(s);
   return hipGetLastError();
 }

@@ -371,13 +371,17 @@ wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const floa
   return from_hip(wq::launch_i8_matmul(p, stream));
 }
 
-wq_status wq_quant_matmul_inplace_add_w4(const void* x1, const void* x2, wq_layout x2_layout,
-                                         const float* x1_scale, const float* x2_scale, int64_t m,
-                                         int64_t k, int64_t n, float* y, hipStream_t stream) {
+wq_status wq_quant_matmul_inplace_add_w4(const void* x1, wq_dtype x1_dtype, const void* x2,
+                                         wq_layout x2_layout, const float* x1_scale,
+                                         const float* x2_scale, int64_t m, int64_t k, int64_t n,
+                                         float* y, hipStream_t stream) {
+  if (x1_dtype != WQ_INT8 && x1_dtype != WQ_INT4) return WQ_ERR_DTYPE;
   if (x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
   if (m < 0 || n < 0 || m > kMaxRows || n > kMaxKN) return WQ_ERR_SHAPE;
-  // x1 rows of 16-byte chunks; 16 * sum stays inside int32 (k < 2^16)
-  if (k < 1 || k > kMaxKN || (k % 16)) return WQ_ERR_SHAPE;
+  // x1 rows of 16-byte chunks (INT8: k bytes, INT4: k / 2); the scaled sums
+  // (16 or 256 times the sum) stay inside int32 for k < 2^16
+  const bool a4 = x1_dtype == WQ_INT4;
+  if (k < 1 || k > kMaxKN || (k % (a4 ? 32 : 16))) return WQ_ERR_SHAPE;
   if (m == 0 || n == 0) return WQ_OK;
   if (!x1 || !x2 || !x1_scale || !x2_scale || !y) return WQ_ERR_NULLPTR;
   if (!aligned16(x1) || !aligned16(x2) || (reinterpret_cast<uintptr_t>(y) & 3) ||
@@ -386,12 +390,12 @@ wq_status wq_quant_matmul_inplace_add_w4(const void* x1, const void* x2, wq_layo
   const size_t wbytes = wq_pack_int4_bytes(k, n, WQ_LAYOUT_GFX950_B);
   if (wbytes >= (size_t(1) << 31)) return WQ_ERR_SHAPE;     // 32-bit buffer offsets
   const size_t ybytes = (size_t)(m * n) * 4;
-  if (overlap(y, ybytes, x1, (size_t)(m * k)) || overlap(y, ybytes, x2, wbytes) ||
+  if (overlap(y, ybytes, x1, (size_t)(m * (a4 ? k / 2 : k))) || overlap(y, ybytes, x2, wbytes) ||
       overlap(y, ybytes, x1_scale, (size_t)m * 4) || overlap(y, ybytes, x2_scale, (size_t)n * 4))
     return WQ_ERR_ALIAS;
   if ((m + 255) / 256 * ((n + 255) / 256) > 2147483647LL) return WQ_ERR_SHAPE;
-  wq::A8W4Problem p{static_cast<const int8_t*>(x1), static_cast<const uint8_t*>(x2), x1_scale,
-                    x2_scale, y, m, k, n};
+  wq::A8W4Problem p{static_cast<const uint8_t*>(x1), static_cast<const uint8_t*>(x2), x1_scale,
+                    x2_scale, y, m, k, n, a4};
   return from_hip(wq::launch_a8w4_matmul(p, stream));
 }
 

@@ -90,14 +90,16 @@ struct I8Problem {
 
 hipError_t launch_i8_matmul(const I8Problem& p, hipStream_t s);
 
-// INT8 x INT4 (GFX950_B) quantized matmul with in-place add (a8w4_gemm.hip).
+// INT8 (or INT4) x INT4 (GFX950_B) quantized matmul with in-place add
+// (a8w4_gemm.hip).
 struct A8W4Problem {
-  const int8_t* x1;      // (m, k)
+  const uint8_t* x1;     // int8 (m, k), or INT4 codes (m, k/2) bytes when x1_int4
   const uint8_t* x2;     // INT4 codes, logical (k, n), GFX950_B
   const float* s1;       // (m)
   const float* s2;       // (n)
   float* y;              // (m, n)
   int64_t m, k, n;
+  bool x1_int4;
 };
 
 hipError_t launch_a8w4_matmul(const A8W4Problem& p, hipStream_t s);

@@ -10,7 +10,7 @@
  *   mx_quant_matmul_inplace_add   aclnnQuantBatchMatmulInplaceAdd (mx)
  *   mx_fp4_quant_matmul_inplace_add  the same, both operands MXFP4
  *   wq_quant_matmul_inplace_add      the same Formula, INT8 x INT8 (A8W8)
- *   wq_quant_matmul_inplace_add_w4   the same Formula, INT8 x packed INT4 (A8W4)
+ *   wq_quant_matmul_inplace_add_w4   the same Formula, INT8 / INT4 x packed INT4
  *   wq_pack_fp4                   aclnnConvertWeightToINT4Pack (FLOAT -> E2M1)
  *   wq_weight_quant_matmul        \ the unfused chain that the fused operator's
  *   wq_add_rms_norm               / page names as its replacement
@@ -354,14 +354,17 @@ wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const floa
                                       float* y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * INT8 x INT4 quantized matmul with in-place add (A8W4): the same Formula
- * and roundings as wq_quant_matmul_inplace_add, with x2 given as INT4 codes
- * packed by wq_pack_int4 (aclnnConvertWeightToINT4Pack page):
+ * INT8 / INT4 x INT4 quantized matmul with in-place add (A8W4, A4W4): the
+ * same Formula and roundings as wq_quant_matmul_inplace_add, with x2 given
+ * as INT4 codes packed by wq_pack_int4 (aclnnConvertWeightToINT4Pack page)
+ * and x1 as either output of wq_dynamic_quant's per-token mode
+ * (aclnnDynamicQuant page: INT8, or INT4 codes two per byte):
  *
  *   y[m,n] = (sum_k x1[m,k] * q[k,n]) * (x1_scale[m] * x2_scale[n]) + y[m,n]
  *
- * x1: int8 (m, k) row-major (wq_dynamic_quant's per-token INT8 output);
- *     x1_scale: float32 (m).
+ * x1: x1_dtype WQ_INT8: int8 (m, k) row-major; WQ_INT4: codes in [-8, 7]
+ *     stored (m, k/2) bytes, even k in the low nibble. Other dtypes:
+ *     WQ_ERR_DTYPE. x1_scale: float32 (m).
  * x2: the codes q in [-8, 7], logical (k, n), in WQ_LAYOUT_GFX950_B
  *     (wq_pack_int4_bytes(k, n, layout) bytes, under 2^31); ND is
  *     WQ_ERR_UNSUPPORTED. x2_scale: float32 (n).
@@ -371,12 +374,14 @@ wq_status wq_quant_matmul_inplace_add(const void* x1, const void* x2, const floa
  * Device pointers owned by the caller; x1 and x2 16-byte aligned, the scales
  * and y 4-byte aligned; y must not overlap an input. No workspace. m == 0 or
  * n == 0 is an empty no-op.
- * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (m < 0, n outside [0, 65535], k
- * outside [1, 65535] or not a multiple of 16, misaligned pointers, a weight
- * of 2^31 bytes or more); WQ_ERR_UNSUPPORTED (x2_layout not GFX950_B);
- * WQ_ERR_ALIAS (y overlapping an input).
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_DTYPE; WQ_ERR_SHAPE (m < 0, n outside
+ * [0, 65535], k outside [1, 65535] or not a multiple of 16 (32 for an INT4
+ * x1), misaligned pointers, a weight of 2^31 bytes or more);
+ * WQ_ERR_UNSUPPORTED (x2_layout not GFX950_B); WQ_ERR_ALIAS (y overlapping
+ * an input).
  * ---------------------------------------------------------------------- */
-wq_status wq_quant_matmul_inplace_add_w4(const void* x1, const void* x2, wq_layout x2_layout,
+wq_status wq_quant_matmul_inplace_add_w4(const void* x1, wq_dtype x1_dtype,
+                                         const void* x2, wq_layout x2_layout,
                                          const float* x1_scale, const float* x2_scale,
                                          int64_t m, int64_t k, int64_t n, float* y,
                                          hipStream_t stream);

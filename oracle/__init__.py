@@ -19,7 +19,7 @@ from .formats import (e4m3_decode, e4m3_encode, e2m1_decode, e2m1_encode,
                       e8m0_decode, E4M3_MAX, E2M1_MAX)
 from .pack import (pack_int4_nd, unpack_int4_nd, pack_int4_gfx950b,
                    unpack_int4_gfx950b, gfx950b_bytes, pack_codes_gfx950b, pack_float_e2m1)
-from .quant import dynamic_quant_per_token, dynamic_quant_mx, unpack_quant_output
+from .quant import dynamic_quant_per_token, dynamic_quant_mx, encode_quant_output, unpack_quant_output
 from .wq_matmul import dequantize_weight, wq_matmul_add_rmsnorm, weight_quant_matmul, add_rms_norm
 from .mx_matmul import decode_group_size, mx_quant_matmul_inplace_add, mxfp4_quant_matmul_inplace_add
 from .int8_matmul import quant_matmul_inplace_add_int8, quant_matmul_inplace_add_w4
@@ -30,7 +30,7 @@ __all__ = [
     "E4M3_MAX", "E2M1_MAX",
     "pack_int4_nd", "unpack_int4_nd", "pack_int4_gfx950b", "unpack_int4_gfx950b",
     "gfx950b_bytes", "pack_codes_gfx950b", "pack_float_e2m1",
-    "dynamic_quant_per_token", "dynamic_quant_mx", "unpack_quant_output",
+    "dynamic_quant_per_token", "dynamic_quant_mx", "encode_quant_output", "unpack_quant_output",
     "dequantize_weight", "wq_matmul_add_rmsnorm", "weight_quant_matmul", "add_rms_norm",
     "decode_group_size", "mx_quant_matmul_inplace_add", "mxfp4_quant_matmul_inplace_add", "quant_matmul_inplace_add_int8",
     "rel_err_floor", "as_f64",

@@ -214,14 +214,17 @@ def test_int8_matmul_validation():
 
 
 def _w4mm(**kw):
-    a = dict(x1=FAKE, x2=FAKE2, layout=wq.WQ_LAYOUT_GFX950_B, s1=FAKE3, s2=FAKE3 + 0x4000, m=32,
-             k=64, n=48, y=FAKE + 0x40000000, stream=0)
+    a = dict(x1=FAKE, dt=wq.WQ_INT8, x2=FAKE2, layout=wq.WQ_LAYOUT_GFX950_B, s1=FAKE3,
+             s2=FAKE3 + 0x4000, m=32, k=64, n=48, y=FAKE + 0x40000000, stream=0)
     a.update(kw)
-    return wq.lib().wq_quant_matmul_inplace_add_w4(a["x1"], a["x2"], a["layout"], a["s1"], a["s2"],
-                                                   a["m"], a["k"], a["n"], a["y"], a["stream"])
+    return wq.lib().wq_quant_matmul_inplace_add_w4(a["x1"], a["dt"], a["x2"], a["layout"], a["s1"],
+                                                   a["s2"], a["m"], a["k"], a["n"], a["y"], a["stream"])
 
 
 def test_a8w4_matmul_validation():
+    assert _w4mm(dt=wq.WQ_FP8_E4M3) == wq.WQ_ERR_DTYPE
+    assert _w4mm(dt=wq.WQ_INT4, k=48) == wq.WQ_ERR_SHAPE    # INT4 x1: k % 32
+    assert _w4mm(dt=wq.WQ_INT4, m=0) == wq.WQ_OK
     assert _w4mm(layout=wq.WQ_LAYOUT_ND) == wq.WQ_ERR_UNSUPPORTED
     assert _w4mm(k=0) == wq.WQ_ERR_SHAPE
     assert _w4mm(k=40) == wq.WQ_ERR_SHAPE                  # k % 16
