@@ -256,3 +256,21 @@ def test_decode_every_row_count(m):
     note(f"wq decode rows m={m} 1024x640 g128")
     y, n = wq_on_gpu(c)
     check_wq(c, y, n)
+
+
+@pytest.mark.parametrize("m,k,n,g", [(40, 1024, 65535, 128),     # widest n: ragged, masked strips
+                                     (48, 65408, 256, 128),      # deepest k on the fast path
+                                     (3, 65408, 640, 128),       # the same k on the decode kernel
+                                     (24, 2048, 65535, 0)],      # widest n, decode, per channel
+                         ids=["n65535-prefill", "k65408-prefill", "k65408-decode", "n65535-decode"])
+def test_maximum_sizes_sampled_rows(m, k, n, g):
+    # the largest n and k the call takes (n <= 65535, k <= 65535 and a multiple
+    # of 128 for the fast kernels), checked on sampled rows (the full rows:
+    # normOut needs the whole row)
+    gran = "group" if g else "channel"
+    c = workloads.wq_case(f"max{m}x{k}x{n}", m, k, n, act=torch.bfloat16, w_bits=4, granularity=gran,
+                          group_size=g, offset_range=(-0.5, 0.5), bias_std=0.1, seed=k + n)
+    note(f"wq maximum size {m}x{k}x{n} g={g}")
+    y, nrm = wq_on_gpu(c)
+    rows = np.random.default_rng(5).choice(m, size=min(m, 4), replace=False)
+    check_wq(c, y, nrm, rows=rows)
