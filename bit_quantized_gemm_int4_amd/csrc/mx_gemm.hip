@@ -30,6 +30,8 @@
 //     accumulators start as y, so the in-place add costs no extra pass.
 //   - mx_gemm_kernel: any shape (partial K blocks, ragged M and N); a small
 //     64 x 64 tile that transposes A byte-wise.
+#include <utility>
+
 #include "wq_device.h"
 #include "wq_internal.h"
 
@@ -144,8 +146,13 @@ __device__ __forceinline__ void mf_dma(const uint8_t* __restrict__ x1t, const ui
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
+    // 64-byte record slot sl = 128 wn + 16 j + jl holds the tile's column
+    // 128 wn + 8 jl + j, so that a lane's eight columns (j = 0..7) are
+    // consecutive: their scales are one 8-byte read and their y one 32-byte run
     const int q = 2 * wave + i;
-    __builtin_amdgcn_global_load_lds((glb_void*)(x2 + ((int64_t)step * Np + n0) * 64 + q * 1024 + lane * 16),
+    const int sl = 16 * q + (lane >> 2);
+    const int col = (sl & 128) + 8 * (sl & 15) + ((sl >> 4) & 7);
+    __builtin_amdgcn_global_load_lds((glb_void*)(x2 + ((int64_t)step * Np + n0 + col) * 64 + 16 * (lane & 3)),
                                      (lds_void*)(bf.b + q * 1024), 16, 0, 0);
   }
   if (wave < 4) {   // scale1 rows m0 + 64 wave + lane, blocks 4 step .. 4 step + 3
@@ -155,6 +162,17 @@ __device__ __forceinline__ void mf_dma(const uint8_t* __restrict__ x1t, const ui
     __builtin_amdgcn_global_load_lds((glb_void*)(s2 + (4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane),
                                      (lds_void*)(bf.s2 + (wave - 4) * 256), 4, 0, 0);
   }
+}
+
+// The eight MFMAs of one A fragment (row block i) against the weight
+// fragments j = 0..7: weight fragment j's scale is byte j % 4 of sbw[j / 4]
+// (the instruction's byte select is an immediate).
+template <int... J>
+__device__ __forceinline__ void mf_row(f32x4 (&acc)[8], const i32x8& af, const u32x4 (&bv)[8], int sa,
+                                       const uint2& sbw, std::integer_sequence<int, J...>) {
+  ((acc[J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        af, (i32x8){(int)bv[J].x, (int)bv[J].y, (int)bv[J].z, (int)bv[J].w, 0, 0, 0, 0}, acc[J],
+        0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, sa, J & 3, (int)(J < 4 ? sbw.x : sbw.y))), ...);
 }
 
 __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict__ x1t,
@@ -187,8 +205,10 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   // accumulators start as y (the in-place add). y goes through a buffer
   // resource: a per-lane offset, a uniform row offset and an immediate column
   // offset, so no per-element address is kept across the K loop.
+  // Lane l holds rows 4 (l / 16) + r of each 16-row block and the tile
+  // columns 128 wn + 8 (l % 16) + j, j = 0..7: two 16-byte runs per row.
   const __amdgpu_buffer_rsrc_t ry = buf_rsrc(y, (uint32_t)(M * N * 4));
-  const uint32_t yl = (uint32_t)((4 * (lane >> 4)) * N + (lane & 15)) * 4u;
+  const uint32_t yl = (uint32_t)((4 * (lane >> 4)) * N + 8 * (lane & 15)) * 4u;
   const uint32_t yw = (uint32_t)(((m0 + 64 * wm) * N + n0 + 128 * wn) * 4);
   f32x4 acc[4][8];
 #pragma unroll
@@ -197,8 +217,13 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
     for (int r = 0; r < 4; ++r) {
       const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ry, yl + 64u * j, so, 0));
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, yl + 16u * h, so, 0));
+        acc[i][4 * h + 0][r] = __uint_as_float(v.x);
+        acc[i][4 * h + 1][r] = __uint_as_float(v.y);
+        acc[i][4 * h + 2][r] = __uint_as_float(v.z);
+        acc[i][4 * h + 3][r] = __uint_as_float(v.w);
+      }
     }
 
   mf_dma(x1t, x2, s1, s2, buf0, M, N, Np, KB, m0, n0, 0, wave, lane);
@@ -215,7 +240,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   const int abase = r0 * 256 + 8 * (jl & 1);
   const int boff = (128 * wn + jl) * 64 + g * 16;       // + 1024 j
   const int s1off = (64 * wm + jl) * 4 + g;             // + 64 i
-  const int s2off = g * 256 + 128 * wn + jl;            // + 16 j
+  const int s2off = g * 256 + 128 * wn + 8 * jl;        // columns 8 jl .. 8 jl + 7
 
   // One 128-deep step on buffer `cur` while the next step streams into
   // `nxt`. The single barrier at the end both publishes every wave's DMA into
@@ -223,12 +248,9 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   auto do_step = [&](int step, const MfBufs& cur, const MfBufs& nxt) {
     if (step + 1 < steps) mf_dma(x1t, x2, s1, s2, nxt, M, N, Np, KB, m0, n0, step + 1, wave, lane);
     u32x4 bv[8];
-    int sb[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bv[j] = *reinterpret_cast<const u32x4*>(cur.b + boff + 1024 * j);
-      sb[j] = cur.s2[s2off + 16 * j];
-    }
+    for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const u32x4*>(cur.b + boff + 1024 * j);
+    const uint2 sbw = *reinterpret_cast<const uint2*>(cur.s2 + s2off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       typedef int v2i __attribute__((ext_vector_type(2)));
@@ -240,11 +262,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
             cur.a + abase + achunk + ((tt & 1) * 8 + (tt >> 1) * 64) * 256));
       const i32x8 af = {p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
       const int sa = cur.s1[s1off + 64 * i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af, (i32x8){(int)bv[j].x, (int)bv[j].y, (int)bv[j].z, (int)bv[j].w, 0, 0, 0, 0}, acc[i][j],
-            0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, sa, 0, sb[j]);
+      mf_row(acc[i], af, bv, sa, sbw, std::make_integer_sequence<int, 8>{});
     }
     wait_vm<0>();            // this wave's DMA into `nxt` has landed
     __syncthreads();
@@ -260,8 +278,14 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
     for (int r = 0; r < 4; ++r) {
       const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, yl + 64u * j, so, 0);
+      for (int h = 0; h < 2; ++h) {
+        u32x4 v;
+        v.x = __float_as_uint(acc[i][4 * h + 0][r]);
+        v.y = __float_as_uint(acc[i][4 * h + 1][r]);
+        v.z = __float_as_uint(acc[i][4 * h + 2][r]);
+        v.w = __float_as_uint(acc[i][4 * h + 3][r]);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, yl + 16u * h, so, 0);
+      }
     }
 }
 }  // namespace
