@@ -149,3 +149,26 @@ def test_per_token_full_size():
     q, so = oracle.dynamic_quant_per_token(as_f64(c.x), as_f64(c.smooth), "int8")
     assert np.array_equal(s.cpu().numpy(), so)
     assert np.array_equal(y.cpu().numpy(), q.astype(np.int8))
+
+
+def test_mx_full_size_e2m1():
+    # the E2M1 mode (row-major (M, K/2) bytes, 16 x 512 tiles) at the bench size
+    c = workloads.mx(draw_w=False)
+    m, k, n = c.mkn
+    note(f"quant mx full size {m}x{k} e2m1")
+    y, sc = wq.dynamic_quant(c.x.to(DEV), c.smooth.to(DEV), wq.WQ_FP4_E2M1, 32, False)
+    codes, scales = oracle.dynamic_quant_mx(as_f64(c.x), as_f64(c.smooth), "e2m1")
+    assert np.array_equal(sc.cpu().numpy(), scales)
+    c8 = np.asarray(codes, dtype=np.int64)
+    assert np.array_equal(y.cpu().numpy(), (c8[:, 0::2] | (c8[:, 1::2] << 4)).astype(np.uint8))
+
+
+def test_per_token_int4_full_size():
+    # the INT4 output that feeds the A4W4 GEMM, at the bench size
+    c = workloads.mx(draw_w=False)
+    m, k, n = c.mkn
+    note(f"quant per-token full size {m}x{k} int4")
+    y, s = wq.dynamic_quant(c.x.to(DEV), c.smooth.to(DEV), wq.WQ_INT4)
+    q, so = oracle.dynamic_quant_per_token(as_f64(c.x), as_f64(c.smooth), "int4")
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(y.cpu().numpy(), oracle.encode_quant_output(q, "int4"))
