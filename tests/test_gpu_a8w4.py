@@ -161,3 +161,20 @@ def test_dynamic_quant_int4_feeds_a4w4():
     wq.quant_matmul_inplace_add_w4(xq, x2, n, xs, torch.from_numpy(ws).to(DEV), yd, x1_int4=True)
     torch.cuda.synchronize()
     assert np.array_equal(yd.cpu().numpy(), oracle.quant_matmul_inplace_add_w4(q, codes, s, ws, y))
+
+
+def test_a4w4_full_size_sampled_rows():
+    # the bench shape (4096 x 8192 x 4096) with INT4 activations: every output
+    # of 48 rows spread over the tiles, bit for bit
+    note("a4w4 matmul full size 4096x8192x4096 (sampled rows)")
+    m, k, n = 4096, 8192, 4096
+    rng = np.random.default_rng(25)
+    a = rng.integers(-8, 8, size=(m, k))
+    codes = rng.integers(-8, 8, size=(k, n)).astype(np.int32)
+    s1 = rng.uniform(1e-3, 2e-1, size=m).astype(np.float32)
+    s2 = rng.uniform(1e-3, 2e-2, size=n).astype(np.float32)
+    y = rng.normal(size=(m, n)).astype(np.float32)
+    got = _gpu_a4(a, codes, s1, s2, y)
+    rows = rng.choice(m, size=48, replace=False)
+    want = oracle.quant_matmul_inplace_add_w4(a[rows], codes, s1[rows], s2, y[rows])
+    assert np.array_equal(got[rows], want)
