@@ -1,4 +1,4 @@
-// INT8 x INT4 quantized matmul with in-place add: the
+// INT8 (or INT4) x INT4 quantized matmul with in-place add: the
 // aclnnQuantBatchMatmulInplaceAdd page's Formula read for an INT8 x1 (the
 // per-token output of the aclnnDynamicQuant page) and an INT4 weight packed by
 // the aclnnConvertWeightToINT4Pack page's operator, with one K group, a
@@ -21,6 +21,8 @@
 // stages (i8_ring.h): 16 KiB of x1 rows and 8 KiB of weight (the 32 bytes of
 // each column's GFX950_B record that hold the step's 64 codes), three DMA
 // instructions per wave per stage, issued about two and a half steps ahead.
+// The A4 variant takes INT4 activations (see the kernel's comment): its x1
+// stage is 8 KiB, two DMA instructions per wave per stage.
 #include "i8_ring.h"
 #include "wq_device.h"
 #include "wq_internal.h"
