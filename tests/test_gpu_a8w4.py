@@ -178,3 +178,25 @@ def test_a4w4_full_size_sampled_rows():
     rows = rng.choice(m, size=48, replace=False)
     want = oracle.quant_matmul_inplace_add_w4(a[rows], codes, s1[rows], s2, y[rows])
     assert np.array_equal(got[rows], want)
+
+
+def test_dynamic_quant_int32_feeds_a4w4():
+    # the INT32 output (eight nibbles per word, lowest first) holds the same
+    # bytes as the INT4 output, so it feeds the INT4-activation GEMM as is
+    note("dynamic quant int32 -> a4w4 matmul chain")
+    rng = np.random.default_rng(14)
+    m, k, n = 64, 256, 96
+    x = torch.from_numpy(rng.normal(size=(m, k))).to(torch.bfloat16)
+    x32, xs = wq.dynamic_quant(x.to(DEV), None, wq.WQ_INT32)
+    x4, xs4 = wq.dynamic_quant(x.to(DEV), None, wq.WQ_INT4)
+    assert torch.equal(x32.view(torch.uint8).reshape(m, k // 2), x4) and torch.equal(xs, xs4)
+    q, s = oracle.dynamic_quant_per_token(as_f64(x), None, "int32")
+    codes = rng.integers(-8, 8, size=(k, n)).astype(np.int32)
+    ws = rng.uniform(1e-3, 1e-2, size=n).astype(np.float32)
+    y = rng.normal(size=(m, n)).astype(np.float32)
+    yd = torch.from_numpy(y).to(DEV)
+    x2 = wq.pack_int4(torch.from_numpy(codes).to(DEV), wq.WQ_LAYOUT_GFX950_B)
+    wq.quant_matmul_inplace_add_w4(x32.view(torch.uint8).reshape(m, k // 2), x2, n, xs,
+                                   torch.from_numpy(ws).to(DEV), yd, x1_int4=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(yd.cpu().numpy(), oracle.quant_matmul_inplace_add_w4(q, codes, s, ws, y))
