@@ -233,6 +233,21 @@ def test_fast_zero_scale_in_one_strip(G):
     check_wq(c, y, nrm)
 
 
+def test_fast_zero_scale_in_a_later_group_tile():
+    # k = 8192 at group 128: 64 groups, so the correction pass flags two
+    # 32-group tiles per 64 columns; zero scales only in groups 40 and 63
+    # must still send their strips down the masked path
+    m, k, n = 160, 8192, 1024
+    c = workloads.wq_case("fast_zero_scale_late", m, k, n, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=128, scale_range=(0.002, 0.02),
+                          offset_range=(-1.0, 1.0), bias_std=0.1, seed=17)
+    c.scale[40, 300:303] = 0
+    c.scale[63, 900] = 0
+    note("wq fast tile zero scales in groups 40 and 63")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
+
+
 def test_decode_zero_scale_columns():
     # a zero group scale leaves only the offset: w = o for that group
     m, k, n, G = 4, 512, 64, 128
