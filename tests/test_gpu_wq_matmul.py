@@ -233,6 +233,19 @@ def test_fast_zero_scale_in_one_strip(G):
     check_wq(c, y, nrm)
 
 
+@pytest.mark.parametrize("m,k,n", [(300, 1024, 700), (4096, 2048, 1024)])
+def test_fast_tile_fp16_group128(m, k, n):
+    # the prefill tile's fp16 form (codes enter as q + 1032) with the group-128
+    # specialization, ragged and at a full-height m
+    c = workloads.wq_case(f"fast_f16_{m}x{k}x{n}", m, k, n, act=torch.float16, w_bits=4,
+                          granularity="group", group_size=128, offset_range=(-0.5, 0.5),
+                          bias_std=0.1, seed=m + k)
+    note(f"wq fast tile fp16 g128 {m}x{k}x{n}")
+    y, nrm = wq_on_gpu(c)
+    rows = None if m <= 512 else np.random.default_rng(3).choice(m, size=32, replace=False)
+    check_wq(c, y, nrm, rows=rows)
+
+
 def test_fast_zero_scale_in_a_later_group_tile():
     # k = 8192 at group 128: 64 groups, so the correction pass flags two
     # 32-group tiles per 64 columns; zero scales only in groups 40 and 63
