@@ -251,19 +251,29 @@ __global__ __launch_bounds__(512, 1) void a8w4_gemm_tile(const uint8_t* __restri
 
 }  // namespace
 
+// Rows in chunks of kRowChunk (independent row blocks), so that the grid
+// stays within the launch limit for every m the call accepts.
 hipError_t launch_a8w4_matmul(const A8W4Problem& p, hipStream_t s) {
-  const int64_t tm = (p.m + W4_BM - 1) / W4_BM, tn = (p.n + W4_BN - 1) / W4_BN;
   const int64_t np = 16 * ((p.n + 15) / 16);
   const uint32_t x2_bytes = (uint32_t)(((p.k + 127) / 128) * np * 64);
-  prof_begin(s);
-  if (p.x1_int4)
-    a8w4_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k,
-                                                                   p.n, np, x2_bytes, tm, tn);
-  else
-    a8w4_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m,
-                                                                    p.k, p.n, np, x2_bytes, tm, tn);
-  prof_end(s);
-  return hipGetLastError();
+  const int64_t row_bytes = p.x1_int4 ? p.k / 2 : p.k;
+  for (int64_t r0 = 0; r0 < p.m; r0 += kRowChunk) {
+    const int64_t m = p.m - r0 < kRowChunk ? p.m - r0 : kRowChunk;
+    const int64_t tm = (m + W4_BM - 1) / W4_BM, tn = (p.n + W4_BN - 1) / W4_BN;
+    const uint8_t* x1 = p.x1 + r0 * row_bytes;
+    float* y = p.y + r0 * p.n;
+    prof_begin(s);
+    if (p.x1_int4)
+      a8w4_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1 + r0, p.s2, y, m, p.k,
+                                                                     p.n, np, x2_bytes, tm, tn);
+    else
+      a8w4_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1 + r0, p.s2, y, m,
+                                                                      p.k, p.n, np, x2_bytes, tm, tn);
+    prof_end(s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace wq

@@ -147,15 +147,22 @@ hipError_t launch_add_rmsnorm(const void* x, const void* residual, const void* g
   const auto* gp = static_cast<const uint16_t*>(gamma);
   auto* yp = static_cast<uint16_t*>(y);
   auto* op = static_cast<uint16_t*>(norm_out);
-  const dim3 grid((unsigned)rows);
-  if (d % 8 == 0) {
-    if (bf16) add_rmsnorm_vec<ACT_BF16><<<grid, ARN_THREADS, 0, s>>>(xp, rp, gp, yp, op, d, eps);
-    else add_rmsnorm_vec<ACT_F16><<<grid, ARN_THREADS, 0, s>>>(xp, rp, gp, yp, op, d, eps);
-  } else {
-    if (bf16) add_rmsnorm_elem<ACT_BF16><<<grid, ARN_THREADS, 0, s>>>(xp, rp, gp, yp, op, d, eps);
-    else add_rmsnorm_elem<ACT_F16><<<grid, ARN_THREADS, 0, s>>>(xp, rp, gp, yp, op, d, eps);
+  // one workgroup per row, rows in chunks of kRowChunk (launch limit)
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowChunk) {
+    const int64_t nr = rows - r0 < kRowChunk ? rows - r0 : kRowChunk;
+    const int64_t o = r0 * d;
+    const dim3 grid((unsigned)nr);
+    if (d % 8 == 0) {
+      if (bf16) add_rmsnorm_vec<ACT_BF16><<<grid, ARN_THREADS, 0, s>>>(xp + o, rp + o, gp, yp + o, op + o, d, eps);
+      else add_rmsnorm_vec<ACT_F16><<<grid, ARN_THREADS, 0, s>>>(xp + o, rp + o, gp, yp + o, op + o, d, eps);
+    } else {
+      if (bf16) add_rmsnorm_elem<ACT_BF16><<<grid, ARN_THREADS, 0, s>>>(xp + o, rp + o, gp, yp + o, op + o, d, eps);
+      else add_rmsnorm_elem<ACT_F16><<<grid, ARN_THREADS, 0, s>>>(xp + o, rp + o, gp, yp + o, op + o, d, eps);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace wq

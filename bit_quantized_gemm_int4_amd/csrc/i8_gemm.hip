@@ -182,13 +182,20 @@ __global__ __launch_bounds__(512, 1) void i8_gemm_tile(const int8_t* __restrict_
 
 }  // namespace
 
+// Rows in chunks of kRowChunk (independent row blocks), so that the grid
+// stays within the launch limit for every m the call accepts.
 hipError_t launch_i8_matmul(const I8Problem& p, hipStream_t s) {
-  const int64_t tm = (p.m + I8_BM - 1) / I8_BM, tn = (p.n + I8_BN - 1) / I8_BN;
-  prof_begin(s);
-  i8_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2t, p.s1, p.s2, p.y, p.m, p.k, p.n,
-                                                         tm, tn);
-  prof_end(s);
-  return hipGetLastError();
+  for (int64_t r0 = 0; r0 < p.m; r0 += kRowChunk) {
+    const int64_t m = p.m - r0 < kRowChunk ? p.m - r0 : kRowChunk;
+    const int64_t tm = (m + I8_BM - 1) / I8_BM, tn = (p.n + I8_BN - 1) / I8_BN;
+    prof_begin(s);
+    i8_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1 + r0 * p.k, p.x2t, p.s1 + r0, p.s2,
+                                                           p.y + r0 * p.n, m, p.k, p.n, tm, tn);
+    prof_end(s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace wq

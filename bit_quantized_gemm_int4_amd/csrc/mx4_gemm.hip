@@ -289,24 +289,32 @@ __global__ __launch_bounds__(512, 1) void mx4_gemm_tile(const uint8_t* __restric
 
 }  // namespace
 
+// Rows run in chunks of kRowChunk (the launch limit), so the workspace covers
+// one chunk.
 size_t mx4_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  if (m > kRowChunk) m = kRowChunk;
   const int64_t steps = (k + F4_BK - 1) / F4_BK;
   return (size_t)(((m + F4_BM - 1) / F4_BM + (n + F4_BN - 1) / F4_BN) * steps * 1024);
 }
 
 hipError_t launch_mx4_matmul(const Mx4Problem& p, hipStream_t s) {
-  const int64_t tm = (p.m + F4_BM - 1) / F4_BM, tn = (p.n + F4_BN - 1) / F4_BN;
-  const int64_t steps = (p.k + F4_BK - 1) / F4_BK;
+  const int64_t steps = (p.k + F4_BK - 1) / F4_BK, kb = (p.k + 31) / 32;
   const int64_t np = 16 * ((p.n + 15) / 16);
-  uint32_t* sa = static_cast<uint32_t*>(p.workspace);
-  uint32_t* sb = sa + tm * steps * 256;
-  mx4_scale_prep<<<dim3((unsigned)((tm + tn) * steps)), 256, 0, s>>>(p.s1, p.s2, sa, sb, p.m, p.n,
-                                                                     (p.k + 31) / 32, steps, tm);
-  prof_begin(s);
-  mx4_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, sa, sb, p.y, p.m, p.k, p.n, np, tm,
-                                                          tn, steps);
-  prof_end(s);
-  return hipGetLastError();
+  for (int64_t r0 = 0; r0 < p.m; r0 += kRowChunk) {
+    const int64_t m = p.m - r0 < kRowChunk ? p.m - r0 : kRowChunk;
+    const int64_t tm = (m + F4_BM - 1) / F4_BM, tn = (p.n + F4_BN - 1) / F4_BN;
+    uint32_t* sa = static_cast<uint32_t*>(p.workspace);
+    uint32_t* sb = sa + tm * steps * 256;
+    mx4_scale_prep<<<dim3((unsigned)((tm + tn) * steps)), 256, 0, s>>>(p.s1 + r0 * kb, p.s2, sa, sb, m, p.n,
+                                                                       kb, steps, tm);
+    prof_begin(s);
+    mx4_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1 + r0 * (p.k / 2), p.x2, sa, sb,
+                                                            p.y + r0 * p.n, m, p.k, p.n, np, tm, tn, steps);
+    prof_end(s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace wq

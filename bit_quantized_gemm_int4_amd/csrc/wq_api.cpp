@@ -15,6 +15,7 @@ constexpr int64_t kMaxRows = 2147483647LL;   // b*s range (same)
 bool is_act(wq_dtype d) { return d == WQ_F16 || d == WQ_BF16; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // [a, a+na) and [b, b+nb) overlap (both non-empty).
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -220,6 +221,13 @@ wq_status wq_matmul_add_rmsnorm(const void* x1, int64_t m, int64_t k, wq_dtype a
   if (overlap(y, mn2, x1, (size_t)(m * k) * 2) || overlap(y, mn2, x2, wbytes) ||
       overlap(y, mn2, workspace, need))
     return WQ_ERR_ALIAS;
+  // the pre-pass writes the workspace before the GEMM reads its inputs
+  if (overlap(workspace, need, x1, (size_t)(m * k) * 2) || overlap(workspace, need, x2, wbytes) ||
+      overlap(workspace, need, antiquant_scale, sbytes) ||
+      overlap(workspace, need, antiquant_offset, sbytes) ||
+      overlap(workspace, need, bias, (size_t)n * 2) || overlap(workspace, need, residual, mn2) ||
+      overlap(workspace, need, gamma, (size_t)n * 2))
+    return WQ_ERR_ALIAS;
 
   p.x1 = x1;
   p.x2 = x2;
@@ -266,6 +274,10 @@ wq_status wq_weight_quant_matmul(const void* x1, int64_t m, int64_t k, wq_dtype 
   if (overlap(out, mn2, x1, (size_t)(m * k) * 2) || overlap(out, mn2, x2, wbytes) ||
       overlap(out, mn2, antiquant_scale, sbytes) || overlap(out, mn2, antiquant_offset, sbytes) ||
       overlap(out, mn2, bias, (size_t)n * 2) || overlap(out, mn2, workspace, need))
+    return WQ_ERR_ALIAS;
+  if (overlap(workspace, need, x1, (size_t)(m * k) * 2) || overlap(workspace, need, x2, wbytes) ||
+      overlap(workspace, need, antiquant_scale, sbytes) ||
+      overlap(workspace, need, antiquant_offset, sbytes) || overlap(workspace, need, bias, (size_t)n * 2))
     return WQ_ERR_ALIAS;
   p.x1 = x1;
   p.x2 = x2;
@@ -327,7 +339,8 @@ wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout 
   if (transpose_x1 != 1 || transpose_x2 != 0) return WQ_ERR_UNSUPPORTED;
   if (x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
   if (m < 0 || k < 0 || n < 0 || m > kMaxRows || k > kMaxRows || n > kMaxRows) return WQ_ERR_SHAPE;
-  if ((m + 63) / 64 > 65535) return WQ_ERR_SHAPE;
+  // the small-tile kernel's grid: m / 64 blocks in y, n / 64 of 256 threads in x
+  if ((m + 63) / 64 > 65535 || n >= (int64_t(1) << 30)) return WQ_ERR_SHAPE;
   // groupSize = K | N << 16 | M << 32; zero fields inferred from the shapes:
   // scale1 is (m, ceil(k/32)) and scale2 (ceil(k/32), n), so M and N infer to
   // 1 by exact division and K to 32.
@@ -337,7 +350,9 @@ wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout 
   if ((gk != 0 && gk != 32) || (gn != 0 && gn != 1) || (gm != 0 && gm != 1)) return WQ_ERR_GROUP;
   if (m == 0 || n == 0 || k == 0) return WQ_OK;
   if (!x1 || !x2 || !x1_scale || !x2_scale || !y) return WQ_ERR_NULLPTR;
-  if (!aligned16(x2) || !aligned16(y)) return WQ_ERR_SHAPE;
+  // the tiled kernel copies x1 in 16-byte and the scales in 4-byte pieces
+  if (!aligned16(x1) || !aligned16(x2) || !aligned16(y) || !aligned4(x1_scale) || !aligned4(x2_scale))
+    return WQ_ERR_SHAPE;
   const size_t ybytes = (size_t)(m * n) * 4;
   const int64_t kb = (k + 31) / 32;
   if (overlap(y, ybytes, x1, (size_t)(k * m)) ||

@@ -322,11 +322,15 @@ size_t partial_bytes(int64_t m, int64_t n) {
 
 // Workspace: per-(32-column tile, row) partial sums of y^2, then (fast path)
 // per-group row sums of x1 and per-group column corrections as bf16 hi/lo.
+// Rows run in chunks of kRowChunk, so the workspace covers one chunk.
 size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  if (m > kRowChunk) m = kRowChunk;
   return partial_bytes(m, n) + fast_rowsum_bytes(m, k) + fast_corr_bytes(n, k) + 256;
 }
 
-hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
+namespace {
+
+hipError_t wq_rows(const WqProblem& p, hipStream_t s) {
   GemmArgs a;
   a.x1 = static_cast<const uint16_t*>(p.x1);
   a.x2 = static_cast<const uint8_t*>(p.x2);
@@ -362,6 +366,25 @@ hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
   if (!p.norm_out) return hipSuccess;                 // the standalone matmul: no norm
   return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, 1, tiles, s)
                 : launch_finish<ACT_F16>(p, a, tiles, 1, tiles, s);
+}
+
+}  // namespace
+
+// Rows are independent: taller inputs run as chunks of kRowChunk rows, one
+// after the other on the stream (the workspace is reused), so that no grid
+// over rows passes the launch limit after an earlier kernel has written.
+hipError_t launch_wq_matmul_add_rmsnorm(const WqProblem& p, hipStream_t s) {
+  for (int64_t r0 = 0; r0 < p.m; r0 += kRowChunk) {
+    WqProblem c = p;
+    c.m = p.m - r0 < kRowChunk ? p.m - r0 : kRowChunk;
+    c.x1 = static_cast<const uint16_t*>(p.x1) + r0 * p.k;
+    if (p.residual) c.residual = static_cast<const uint16_t*>(p.residual) + r0 * p.n;
+    c.y = static_cast<uint16_t*>(p.y) + r0 * p.n;
+    if (p.norm_out) c.norm_out = static_cast<uint16_t*>(p.norm_out) + r0 * p.n;
+    const hipError_t e = wq_rows(c, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace wq

@@ -10,6 +10,12 @@
 
 namespace wq {
 
+// Rows per launch for kernels whose grid runs over rows: every row-parallel
+// operator splits taller inputs into independent chunks of this many rows, so
+// that no grid passes 2^32 threads in a dimension (the pages allow up to
+// 2^31 - 1 rows).
+constexpr int64_t kRowChunk = int64_t(1) << 20;
+
 // fp4: the 32-bit inputs are floats, encoded to E2M1 codes (else int4 values)
 hipError_t launch_pack_int4(const int32_t* w, int64_t k, int64_t n, bool transpose,
                             wq_layout layout, uint8_t* out, hipStream_t s, bool fp4);

@@ -3,8 +3,12 @@
 // pair of HIP events on its stream around its contraction kernel (the MFMA
 // tile, the decode weight stream or the generic tile), so a caller can time
 // that kernel alone, on the stream it runs on, without a profiler.
+// This is a measurement aid and the library's only process-wide state: with
+// profiling off (the default) a launch reads one atomic flag and takes no
+// lock.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -18,7 +22,7 @@ constexpr int kMaxPairs = 4096;
 
 struct Profile {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};
   std::vector<hipEvent_t> ev;   // 2 * kMaxPairs events, created on first enable
   int used = 0;                 // pairs recorded since the last enable / read
   int64_t launches = 0;         // launches seen (including any past kMaxPairs)
@@ -33,6 +37,7 @@ Profile& prof() {
 
 void prof_begin(hipStream_t s) {
   Profile& p = prof();
+  if (!p.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> g(p.mu);
   if (!p.on) return;
   ++p.launches;
@@ -41,6 +46,7 @@ void prof_begin(hipStream_t s) {
 
 void prof_end(hipStream_t s) {
   Profile& p = prof();
+  if (!p.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> g(p.mu);
   if (!p.on || p.used >= kMaxPairs) return;
   (void)hipEventRecord(p.ev[2 * p.used + 1], s);

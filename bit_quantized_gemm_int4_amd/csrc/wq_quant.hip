@@ -349,9 +349,11 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(
 
 }  // namespace
 
-hipError_t launch_quant_per_token(const void* x, bool bf16, int64_t rows, int64_t cols,
-                                  const void* smooth, wq_dtype y_dtype, void* y,
-                                  float* scale, hipStream_t s) {
+namespace {
+
+hipError_t quant_per_token_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                const void* smooth, wq_dtype y_dtype, void* y, float* scale,
+                                hipStream_t s) {
   const float dmax = y_dtype == WQ_INT8 ? 127.f : 7.f;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* sp = static_cast<const uint16_t*>(smooth);
@@ -373,9 +375,29 @@ hipError_t launch_quant_per_token(const void* x, bool bf16, int64_t rows, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols,
-                           const void* smooth, wq_dtype y_dtype, bool transpose_y,
-                           uint8_t* y, uint8_t* scale, hipStream_t s) {
+}  // namespace
+
+// One workgroup per row: rows go in chunks of kRowChunk so that no grid
+// exceeds the launch limit of 2^32 threads per dimension.
+hipError_t launch_quant_per_token(const void* x, bool bf16, int64_t rows, int64_t cols,
+                                  const void* smooth, wq_dtype y_dtype, void* y,
+                                  float* scale, hipStream_t s) {
+  const int64_t y_row = y_dtype == WQ_INT8 ? cols : cols / 2;     // bytes per output row
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowChunk) {
+    const int64_t nr = rows - r0 < kRowChunk ? rows - r0 : kRowChunk;
+    const hipError_t e = quant_per_token_rows(static_cast<const uint16_t*>(x) + r0 * cols, bf16, nr, cols,
+                                              smooth, y_dtype, static_cast<uint8_t*>(y) + r0 * y_row,
+                                              scale + r0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+namespace {
+
+hipError_t quant_mx_rows(const void* x, bool bf16, int64_t rows, int64_t cols,
+                         const void* smooth, wq_dtype y_dtype, bool transpose_y,
+                         uint8_t* y, uint8_t* scale, hipStream_t s) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* sp = static_cast<const uint16_t*>(smooth);
   // blocks of 128 x 64 (transposed output) or 16 x 512 (row-major output)
@@ -400,6 +422,25 @@ hipError_t launch_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols,
   }
 #undef WQ_MX_LAUNCH
   return hipGetLastError();
+}
+
+}  // namespace
+
+// The row-major output takes rows in chunks of kRowChunk (16-row blocks of
+// 256 threads would pass 2^32 threads per grid dimension beyond 2^28 rows);
+// the transposed output's grid (128-row blocks) always fits.
+hipError_t launch_quant_mx(const void* x, bool bf16, int64_t rows, int64_t cols,
+                           const void* smooth, wq_dtype y_dtype, bool transpose_y,
+                           uint8_t* y, uint8_t* scale, hipStream_t s) {
+  if (transpose_y) return quant_mx_rows(x, bf16, rows, cols, smooth, y_dtype, true, y, scale, s);
+  const int64_t y_row = y_dtype == WQ_FP8_E4M3 ? cols : cols / 2, s_row = (cols + 31) / 32;
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowChunk) {
+    const int64_t nr = rows - r0 < kRowChunk ? rows - r0 : kRowChunk;
+    const hipError_t e = quant_mx_rows(static_cast<const uint16_t*>(x) + r0 * cols, bf16, nr, cols, smooth,
+                                       y_dtype, false, y + r0 * y_row, scale + r0 * s_row, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace wq

@@ -165,6 +165,14 @@ def test_wq_matmul_validation_pointers_workspace_alias():
     assert _wqmm(norm=FAKE + 0x50000) == wq.WQ_ERR_ALIAS             # norm_out == y
     assert _wqmm(y=FAKE + 0x30010) == wq.WQ_ERR_ALIAS                # y partially over residual
     assert _wqmm(y=FAKE, m=16) == wq.WQ_ERR_ALIAS                    # y over x1
+    # the workspace is written before the inputs are read: it may overlap none
+    assert _wqmm(ws=FAKE) == wq.WQ_ERR_ALIAS                         # over x1
+    assert _wqmm(ws=FAKE + 0x10000) == wq.WQ_ERR_ALIAS               # over x2
+    assert _wqmm(ws=FAKE + 0x20000) == wq.WQ_ERR_ALIAS               # over the scale
+    assert _wqmm(ws=FAKE + 0x30000) == wq.WQ_ERR_ALIAS               # over residual
+    assert _wqmm(ws=FAKE + 0x40000) == wq.WQ_ERR_ALIAS               # over gamma
+    assert _wqmm(ws=FAKE + 0x80000, offset=FAKE + 0x80000) == wq.WQ_ERR_ALIAS  # over the offset
+    assert _wqmm(ws=FAKE + 0x80000, bias=FAKE + 0x80000) == wq.WQ_ERR_ALIAS    # over bias
 
 
 def _mx(**kw):
@@ -188,6 +196,10 @@ def test_mx_matmul_validation():
     assert _mx(y=None) == wq.WQ_ERR_NULLPTR
     assert _mx(y=FAKE2 + 4) == wq.WQ_ERR_SHAPE
     assert _mx(y=FAKE2 + 16) == wq.WQ_ERR_ALIAS                      # y over x2
+    # the tiled kernel copies x1 in 16-byte and the scales in 4-byte pieces
+    assert _mx(x1=FAKE + 8) == wq.WQ_ERR_SHAPE
+    assert _mx(s1=FAKE3 + 1) == wq.WQ_ERR_SHAPE
+    assert _mx(s2=FAKE3 + 0x10002) == wq.WQ_ERR_SHAPE
     assert _mx(m=0) == wq.WQ_OK and _mx(k=0) == wq.WQ_OK
 
 
@@ -271,6 +283,8 @@ def test_weight_quant_matmul_validation():
     assert _wqbmm(out=FAKE + 0x50008) == wq.WQ_ERR_SHAPE             # misaligned
     assert _wqbmm(out=FAKE + 0x10000) == wq.WQ_ERR_ALIAS             # out over x2
     assert _wqbmm(out=FAKE2 + 0x100) == wq.WQ_ERR_ALIAS              # out over the workspace
+    assert _wqbmm(ws=FAKE) == wq.WQ_ERR_ALIAS                        # workspace over x1
+    assert _wqbmm(ws=FAKE + 0x20000) == wq.WQ_ERR_ALIAS              # workspace over the scale
 
 
 def _arn(**kw):
