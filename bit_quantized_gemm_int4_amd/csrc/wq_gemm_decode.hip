@@ -15,10 +15,10 @@
 // scale/offset pair per column and block) before its first MFMA. The
 // per-wave sums meet in LDS and are added in a fixed wave order.
 //
-// Arithmetic per 128-deep block: the codes enter the MFMA as 16-bit B = q + 136
-// (fp16: q + 1032, see wq_unpack.h), one more MFMA against a ones fragment
-// gives the row sums of x, and the block is folded into the float32 result as
-//   acc += s * sum_k x B  +  (o - 136 s) * sum_k x
+// Arithmetic per 128-deep block: the codes enter the MFMA as 16-bit B = q + 24
+// (see wq_unpack.h), one more MFMA against a ones fragment gives the row sums
+// of x, and the block is folded into the float32 result as
+//   acc += s * sum_k x B  +  (o - 24 s) * sum_k x
 // with s, o the block's group scale and offset for the column.
 //
 // Epilogue: y = acc + bias + residual (stored rounded to the activation
@@ -140,15 +140,17 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs& a, const DecodeL
       ma.rs = mfma16<ACT>(av, ones, ma.rs);
 #pragma unroll
       for (int c = 0; c < CTW; ++c) {
-        const u32x4 b = unpack8(wv[j][c][w4], NIBBLE_MASK, Magic<ACT>::xbits);
+        const u32x4 b = unpack8<ACT>(wv[j][c][w4]);
         ma.part[c] = mfma16<ACT>(av, b, ma.part[c]);
       }
+      // one K step's operands at a time (bounds the live unpacked fragments)
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
       const float s = to_f32<ACT>((uint16_t)sr[j][c]);
       const float o = to_f32<ACT>((uint16_t)orw[j][c]) * a.omul;
-      const float cc = o - Magic<ACT>::bias * s;
+      const float cc = o - Unpack<ACT>::bias * s;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[c][i], fmaf(cc, ma.rs[i], acc[c][i]));
     }

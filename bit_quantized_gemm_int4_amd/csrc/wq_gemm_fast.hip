@@ -4,14 +4,13 @@
 // (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula); this file holds
 // the MFMA-bound tile used for large m.
 //
-// Arithmetic. With q the int4 code, u = q + 8 its offset-binary nibble and
-// B = 128 + u = q + 136 (exact in bf16: the bits 0x4300 | u; fp16 uses
-// 1024 + u = q + 1032, bits 0x6400 | u), no weight is ever dequantized:
-//   sum_k x[r,k] (q s + o) = s * sum_k x B  +  (o - 136 s) * sum_k x
+// Arithmetic. With q the int4 code and B = q + 24 its exact 16-bit operand
+// (wq_unpack.h), no weight is ever dequantized:
+//   sum_k x[r,k] (q s + o) = s * sum_k x B  +  (o - 24 s) * sum_k x
 // The MFMAs sum x * B straight into the float32 accumulator, kept in units of
 // the current group's scale (rescaled by s_prev / s_g at each group start: one
 // multiply per element per group; a zero scale zeroes that column's weight
-// operand instead). The rank-1 remainder sum_g rowsum_g(x) (o_g - 136 s_g) is
+// operand instead). The rank-1 remainder sum_g rowsum_g(x) (o_g - 24 s_g) is
 // added at the end with MFMAs over the group axis on bf16 hi/lo splits of
 // both factors (three products; relative error ~2^-16 of a term that is a
 // small multiple of the result). One pre-pass launch produces those factors:
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
       const int64_t si = g * s_row + col * s_col;
       const float sv = to_f32<ACT>(scale[si]);
       const float ov = offset ? to_f32<ACT>(offset[si]) : 0.f;
-      c = ov - Magic<ACT>::bias * sv;
+      c = ov - Unpack<ACT>::bias * sv;
       zero |= sv == 0.f;
     }
     tile[gl][cl] = c;
@@ -233,7 +232,7 @@ __device__ __forceinline__ void wd_dma_b(__amdgpu_buffer_rsrc_t rb, uint32_t v0,
 // group scale is zero (otherwise the unpack constants apply).
 template <int ACT, bool FIRST, bool MASKED, typename Dma>
 __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf,
-                                        const uint32_t (&mk)[4], const uint32_t (&mc)[4],
+                                        const UnpackKeys<ACT> (&keys)[4],
                                         const float (&ratio)[4], f32x4 (&acc)[8][4], const Dma& dma) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   // Step c gives lane group g = lane / 16 the 8 K values of dword
@@ -253,16 +252,19 @@ __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
   };
-  uint32_t w4;
-  // piece p (0..4) of unpacking dword w of column tile f into out
+  using U = Unpack<ACT>;
+  typename U::Src us;
+  // piece p (0..4) of unpacking dword w of column tile f into out: the
+  // sources, then one output dword per piece
   auto unpack_piece = [&](int p, uint32_t w, int f, u32x4& out) {
-    const uint32_t m = MASKED ? mk[f] : NIBBLE_MASK;
-    const uint32_t cc = MASKED ? mc[f] : Magic<ACT>::xbits;
-    if (p == 0) w4 = w >> 4;
-    if (p == 1) out.x = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C040C00u), m, cc);
-    if (p == 2) out.y = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C050C01u), m, cc);
-    if (p == 3) out.z = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C060C02u), m, cc);
-    if (p == 4) out.w = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C070C03u), m, cc);
+    UnpackKeys<ACT> kk;
+    if (MASKED) kk = keys[f];
+    else kk.set(true);
+    if (p == 0) us = U::src(w, kk.m1, kk.c1);
+    if (p == 1) out.x = U::template dword<0>(us, kk.m2, kk.c2);
+    if (p == 2) out.y = U::template dword<1>(us, kk.m2, kk.c2);
+    if (p == 3) out.z = U::template dword<2>(us, kk.m2, kk.c2);
+    if (p == 4) out.w = U::template dword<3>(us, kk.m2, kk.c2);
   };
 
   uint32_t rw[4];
@@ -377,7 +379,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
   // zeroes the column's weight operand and leaves acc and cs unchanged.
   float cs[4] = {0.f, 0.f, 0.f, 0.f};
   float ratio[4];
-  uint32_t mk[4], mc[4];                               // MASKED: per-lane unpack masks
+  UnpackKeys<ACT> keys[4];                             // MASKED: per-lane unpack keys
   int gpos = 0;                                        // slab index within its group
   int64_t gnext = 1;                                   // the next group
   auto step = [&](int s, const uint8_t* acur, uint8_t* anxt, const uint8_t* wcur, uint8_t* wnxt) {
@@ -395,10 +397,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
         const bool z = sg == 0.f;
         ratio[f] = (z || cs[f] == 0.f) ? 1.f : cs[f] * __builtin_amdgcn_rcpf(sg);   // ~2 ulp
         cs[f] = z ? cs[f] : sg;
-        if (MASKED) {
-          mk[f] = z ? 0u : NIBBLE_MASK;
-          mc[f] = z ? 0u : Magic<ACT>::xbits;
-        }
+        if (MASKED) keys[f].set(!z);
       }
       if (!EVERY) {
 #pragma unroll
@@ -409,7 +408,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
             for (int r = 0; r < 4; ++r) acc[i][f][r] *= ratio[f];
       }
     }
-    wd_slab<ACT, EVERY, MASKED>(acur, wcur, mk, mc, ratio, acc, dma);
+    wd_slab<ACT, EVERY, MASKED>(acur, wcur, keys, ratio, acc, dma);
     if (++gpos == spg) {
       gpos = 0;
       scur[0] = snxt[0];

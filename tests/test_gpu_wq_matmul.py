@@ -302,3 +302,37 @@ def test_maximum_sizes_sampled_rows(m, k, n, g):
     y, nrm = wq_on_gpu(c)
     rows = np.random.default_rng(5).choice(m, size=min(m, 4), replace=False)
     check_wq(c, y, nrm, rows=rows)
+
+
+# Activations of one sign make sum(x) over K large: the kernels' 16-bit weight
+# operand is q + 24, and the 24 * sum(x) it adds must cancel against the
+# rank-1 remainder without eating the result's precision. Codes in [-7, 7]
+# keep the weights' mean at zero, so the result itself stays small.
+ONE_SIGN = [  # m, k, n, granularity, group, offset, act
+    (256, 8192, 512, "group", 128, None, torch.float16),        # prefill tile, group 128
+    (256, 8192, 512, "group", 128, None, torch.bfloat16),
+    (256, 8192, 512, "group", 256, (-0.1, 0.1), torch.float16),  # prefill tile, 2 slabs per group
+    (130, 8192, 520, "channel", 0, None, torch.float16),        # one group over all of K, ragged
+    (130, 8192, 520, "channel", 0, None, torch.bfloat16),
+    (16, 8192, 1024, "group", 128, None, torch.float16),        # decode kernel
+    (16, 8192, 1024, "group", 128, None, torch.bfloat16),
+    (1, 8192, 1024, "channel", 0, (-0.1, 0.1), torch.float16),
+    (40, 8192, 256, "group", 64, None, torch.float16),          # generic tile (group 64)
+]
+
+
+@pytest.mark.parametrize("shape", ONE_SIGN,
+                         ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}-{str(s[6])[6:]}" for s in ONE_SIGN])
+def test_one_sign_activations(shape):
+    m, k, n, gran, G, off, act = shape
+    c = workloads.wq_case(f"one-sign {m}x{k}x{n} {gran}{G}", m, k, n, act=act, w_bits=4,
+                          granularity=gran, group_size=G, scale_range=(0.002, 0.02),
+                          offset_range=off, x1_abs=True, w_range=(-7, 7))
+    note(f"wq one-sign activations {shape}")
+    y, nrm = wq_on_gpu(c)
+    ey, en = check_wq(c, y, nrm)
+    if act == torch.float16:
+        # fp16 rounds its outputs to 2^-11: what remains visible is the
+        # arithmetic, which must sit well inside the bound (a nibble in the
+        # low mantissa bits gave ~4e-2 here)
+        assert ey <= 2e-3 and en <= 3e-3, (ey, en)

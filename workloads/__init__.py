@@ -76,20 +76,25 @@ class WQCase:
 def wq_case(name: str, m: int, k: int, n: int, *, act: torch.dtype, w_bits: int,
             granularity: str, group_size: int = 0, scale_range=(0.005, 0.02),
             offset_range=None, bias_std: Optional[float] = 0.1,
-            x1_shape=None, seed: int = 0) -> WQCase:
+            x1_shape=None, seed: int = 0, x1_abs: bool = False, w_range=None) -> WQCase:
     """A generic weight-quantized case with the configs' distributions.
 
-    x1 ~ N(0,1); weights uniform over the signed range of ``w_bits`` (int4:
-    [-8,7], int8: [-127,127]); scale ~ U[scale_range]; offset ~ U[offset_range]
+    x1 ~ N(0,1) (|N(0,1)| with ``x1_abs``: activations of one sign); weights
+    uniform over the signed range of ``w_bits`` (int4: [-8,7], int8:
+    [-127,127]) or over ``w_range`` = (lo, hi) inclusive; scale ~
+    U[scale_range]; offset ~ U[offset_range]
     (zeros when ``offset_range`` is None and ``granularity`` asks for one, no
     offset when it is the string "none"); bias ~ N(0, bias_std); residual ~
     N(0,1); gamma ~ U[0.9,1.1].
     """
     g = streams(seed, 7)
-    x1 = cast(g[0].standard_normal((m, k)), act)
+    x1d = g[0].standard_normal((m, k))
+    x1 = cast(np.abs(x1d) if x1_abs else x1d, act)
     if x1_shape is not None:
         x1 = x1.reshape(x1_shape)
     lo, hi = (-8, 8) if w_bits == 4 else (-127, 128)
+    if w_range is not None:
+        lo, hi = w_range[0], w_range[1] + 1
     w = torch.from_numpy(g[1].integers(lo, hi, size=(k, n), dtype=np.int32))
     if granularity == "tensor":
         sshape = (1,)
