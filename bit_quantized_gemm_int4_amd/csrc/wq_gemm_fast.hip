@@ -11,9 +11,14 @@
 // the current group's scale (rescaled by s_prev / s_g at each group start: one
 // multiply per element per group; a zero scale zeroes that column's weight
 // operand instead). The rank-1 remainder sum_g rowsum_g(x) (o_g - 24 s_g) is
-// added at the end with MFMAs over the group axis on bf16 hi/lo splits of
-// both factors (three products; relative error ~2^-16 of a term that is a
-// small multiple of the result). One pre-pass launch produces those factors:
+// added at the end with MFMAs over the group axis on bf16 splits of both
+// factors: the corrections in two parts (hi, lo), the row sums in three
+// (hi, mid, lo). Groups of 128 take the three products hi*hi, hi*lo, mid*hi
+// (relative error ~2^-16 per group, of independent sign across the many
+// groups); larger groups, whose row sums are larger and fewer, add mid*lo
+// and lo*hi (~2^-24): with activations of one sign a per-channel group's
+// 24 * rowsum * s is many times the result. One pre-pass launch produces
+// those factors:
 // the per-group row sums of x1 and the per-group column corrections, both
 // stored in MFMA operand order.
 //
@@ -39,6 +44,15 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = from_f32<ACT_BF16>(v - to_f32<ACT_BF16>(hi));
 }
 
+// three-part split: v ~= hi + mid + lo with |v - hi - mid - lo| <= 2^-24 |v|
+// (each remainder is exact in float32)
+__device__ __forceinline__ void split3_bf16(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = from_f32<ACT_BF16>(v);
+  const float r = v - to_f32<ACT_BF16>(hi);
+  mid = from_f32<ACT_BF16>(r);
+  lo = from_f32<ACT_BF16>(r - to_f32<ACT_BF16>(mid));
+}
+
 
 struct FastArgs {
   const uint16_t* x1;
@@ -48,7 +62,7 @@ struct FastArgs {
   const uint16_t* residual;
   uint16_t* y;
   float* partial;          // [m][ceil(n/32)]
-  const uint16_t* rs;      // [m][2][gp]  per-group row sums of x1, bf16 hi then lo
+  const uint16_t* rs;      // [m][3][gp]  per-group row sums of x1, bf16 hi, mid, lo
   const uint16_t* corr;    // [np][2][gp] per-group o - bias*s per column, hi then lo
   int64_t m, k, n, np;
   int64_t group;           // K length of a group (multiple of 128, or >= k)
@@ -62,7 +76,7 @@ struct FastArgs {
 // ---------------------------------------------------------------------------
 // Pre-pass (one launch): the per-group row sums of x1 and the per-group
 // column corrections, both written as bf16 hi/lo in MFMA operand order.
-//   blocks [0, m): row b's sums, [m][2][gp] (zero padded to gp groups): eight-
+//   blocks [0, m): row b's sums, [m][3][gp] (zero padded to gp groups): eight-
 //     element chunk sums in LDS (each thread's loads issued together), then
 //     each group summed in a fixed order;
 //   blocks [m, m + ncb * ngb): a tile of 64 columns x 32 groups of
@@ -114,10 +128,11 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
         const int64_t c1 = (g + 1) * per < chunks ? (g + 1) * per : chunks;
         for (int64_t c = g * per; c < c1; ++c) s += sh[c];
       }
-      uint16_t hi, lo;
-      split_bf16(s, hi, lo);
-      rs[row * 2 * gp + g] = hi;
-      rs[row * 2 * gp + gp + g] = lo;
+      uint16_t hi, mid, lo;
+      split3_bf16(s, hi, mid, lo);
+      rs[row * 3 * gp + g] = hi;
+      rs[row * 3 * gp + gp + g] = mid;
+      rs[row * 3 * gp + 2 * gp + g] = lo;
     }
     return;
   }
@@ -448,10 +463,12 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
     }
   };
   u32x4 res_cur[4];
-  load_res(0, res_cur);
+  // (the larger-group variant's five remainder products need the registers:
+  // it fetches the first quarter after them)
+  if (EVERY) load_res(0, res_cur);
 
   // ---- rank-1 remainder: acc += sum_g rowsum_g(x) * corr_g over the group
-  //      axis, three bf16 MFMA products per 32 groups ----
+  //      axis, three (group 128) or five bf16 MFMA products per 32 groups ----
   for (int64_t g0 = 0; g0 < a.gp; g0 += 32) {
     u32x4 chi[4], clo[4];
 #pragma unroll
@@ -466,17 +483,34 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
     for (int i = 0; i < 8; ++i) {
       int64_t row = m0 + 16 * i + (lane & 15);
       row = row < a.m ? row : a.m - 1;
-      const uint16_t* p = a.rs + row * 2 * a.gp + g0 + 8 * (lane >> 4);
+      const uint16_t* p = a.rs + row * 3 * a.gp + g0 + 8 * (lane >> 4);
       const u32x4 rhi = *reinterpret_cast<const u32x4*>(p);
-      const u32x4 rlo = *reinterpret_cast<const u32x4*>(p + a.gp);
+      const u32x4 rmid = *reinterpret_cast<const u32x4*>(p + a.gp);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         acc[i][f] = mfma16<ACT_BF16>(rhi, chi[f], acc[i][f]);
         acc[i][f] = mfma16<ACT_BF16>(rhi, clo[f], acc[i][f]);
-        acc[i][f] = mfma16<ACT_BF16>(rlo, chi[f], acc[i][f]);
+        acc[i][f] = mfma16<ACT_BF16>(rmid, chi[f], acc[i][f]);
+      }
+    }
+    if (!EVERY) {
+      // second pass (fewer operands live at once): mid * lo and lo * hi
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int64_t row = m0 + 16 * i + (lane & 15);
+        row = row < a.m ? row : a.m - 1;
+        const uint16_t* p = a.rs + row * 3 * a.gp + g0 + 8 * (lane >> 4);
+        const u32x4 rmid = *reinterpret_cast<const u32x4*>(p + a.gp);
+        const u32x4 rlo = *reinterpret_cast<const u32x4*>(p + 2 * a.gp);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          acc[i][f] = mfma16<ACT_BF16>(rmid, clo[f], acc[i][f]);
+          acc[i][f] = mfma16<ACT_BF16>(rlo, chi[f], acc[i][f]);
+        }
       }
     }
   }
+  if (!EVERY) load_res(0, res_cur);
 
   // ---- epilogue, four quarters of 32 rows: stage the wave's 32 x 64 fp32
   //      block in LDS (32 rows x 272 bytes of its 16 KiB region), then each
@@ -643,7 +677,7 @@ bool fast_path_ok(const WqProblem& p) {
 size_t fast_rowsum_bytes(int64_t m, int64_t k) {
   const int64_t groups = (k + 127) / 128;
   const int64_t gp = 32 * ((groups + 31) / 32);
-  return ((size_t)(m * 2 * gp * 2) + 255) & ~(size_t)255;
+  return ((size_t)(m * 3 * gp * 2) + 255) & ~(size_t)255;
 }
 // ... followed by the zero-scale flags of the 64-column x 32-group tiles
 size_t fast_corr_bytes(int64_t n, int64_t k) {
