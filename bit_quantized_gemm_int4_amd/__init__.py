@@ -292,7 +292,7 @@ def matmul_add_rmsnorm(x1: torch.Tensor, x2: torch.Tensor, k: int, n: int, w_dty
         norm_out = torch.empty_like(residual)
     ws = wq_matmul_add_rmsnorm_workspace_size(m, k, n)
     if workspace is None or workspace.numel() < ws:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=x1.device)
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=x1.device)
     wq_matmul_add_rmsnorm(x1, m, k, act_code(x1.dtype), x2, n, w_dtype, layout, transpose_x2,
                           scale, s_rows, s_cols, offset, group_size, bias, residual, gamma, eps,
                           y, norm_out, workspace, workspace.numel(), stream)
@@ -346,7 +346,7 @@ def weight_quant_matmul(x1: torch.Tensor, x2: torch.Tensor, k: int, n: int, w_dt
         out = torch.empty((m, n), dtype=x1.dtype, device=x1.device)
     ws = wq_weight_quant_matmul_workspace_size(m, k, n)
     if workspace is None or workspace.numel() < ws:
-        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=x1.device)
+        workspace = torch.zeros(max(ws, 1), dtype=torch.uint8, device=x1.device)
     wq_weight_quant_matmul(x1, m, k, act_code(x1.dtype), x2, n, w_dtype, layout, transpose_x2,
                            scale, s_rows, s_cols, offset, group_size, bias, out, workspace,
                            workspace.numel(), stream)

@@ -5,9 +5,8 @@
 //
 // Two launches on the caller's stream:
 //   1. a GEMM kernel whose epilogue adds bias and residual, stores y and
-//      writes per-(row, column tile) partial sums of y^2 (float32 y),
-//      row-major, to the workspace (32-column tiles; 16 for the decode
-//      kernel);
+//      writes partial sums of y^2 (float32 y) to the workspace: per (row,
+//      32-column tile), row-major; the decode kernel per (workgroup, row);
 //   2. rmsnorm_finish: sums a row's partials in a fixed order, forms
 //      1/RMS and writes normOut = y * rstd * gamma.
 // GEMM kernels:
@@ -321,11 +320,15 @@ size_t partial_bytes(int64_t m, int64_t n) {
 }  // namespace
 
 // Workspace: per-(32-column tile, row) partial sums of y^2, then (fast path)
-// per-group row sums of x1 and per-group column corrections as bf16 hi/lo.
-// Rows run in chunks of kRowChunk, so the workspace covers one chunk.
+// per-group row sums of x1 and per-group column corrections as bf16 splits;
+// or, for the decode kernel, its per-(workgroup, row) sums. Rows run in
+// chunks of kRowChunk, so the workspace covers one chunk. No call needs
+// initial contents: each writes what it reads.
 size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
   if (m > kRowChunk) m = kRowChunk;
-  return partial_bytes(m, n) + fast_rowsum_bytes(m, k) + fast_corr_bytes(n, k) + 256;
+  const size_t tiled = partial_bytes(m, n) + fast_rowsum_bytes(m, k) + fast_corr_bytes(n, k);
+  const size_t dec = decode_partial_bytes(n);
+  return (tiled > dec ? tiled : dec) + 256;
 }
 
 namespace {
@@ -348,13 +351,15 @@ hipError_t wq_rows(const WqProblem& p, hipStream_t s) {
   a.s_row = p.s_row;
   a.s_col = p.s_col;
   hipError_t e;
-  // partials are row-major: [row][tile], 32-column tiles (16 for decode)
-  int64_t tiles = (p.n + 31) / 32;
+  // partials: [row][tile] with 32-column tiles, or the decode kernel's
+  // [row][workgroup]: partial i of row r at i * ts + r * rstride
+  int64_t tiles = (p.n + 31) / 32, ts = 1, rstride = tiles;
   if (fast_path_ok(p) && decode_ok(p)) {
-    tiles = decode_tiles(p.n);
+    tiles = decode_grid(p.n);
+    rstride = tiles;
     e = launch_decode(p, a.partial, s);
   } else if (fast_path_ok(p)) {
-    uint8_t* ws = static_cast<uint8_t*>(p.workspace);
+    uint8_t* ws = reinterpret_cast<uint8_t*>(a.partial);
     uint16_t* rs = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n));
     uint16_t* corr = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n) +
                                                  fast_rowsum_bytes(p.m, p.k));
@@ -364,8 +369,8 @@ hipError_t wq_rows(const WqProblem& p, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   if (!p.norm_out) return hipSuccess;                 // the standalone matmul: no norm
-  return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, 1, tiles, s)
-                : launch_finish<ACT_F16>(p, a, tiles, 1, tiles, s);
+  return p.bf16 ? launch_finish<ACT_BF16>(p, a, tiles, ts, rstride, s)
+                : launch_finish<ACT_F16>(p, a, tiles, ts, rstride, s);
 }
 
 }  // namespace

@@ -1,29 +1,39 @@
 // Decode-shaped weight-quantized GEMM (m <= 32) for INT4 weights in the
 // GFX950_B layout, group a multiple of 128 along K (or per channel / per
 // tensor), k a multiple of 128. Same operator as wq_gemm.hip
-// (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula).
+// (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula); the RMSNorm
+// finish runs as the next launch (rmsnorm_finish), which on this GPU costs
+// less than any in-kernel grid synchronization: every cross-XCD handoff
+// through memory (a write-through store's acknowledgement, an atomic on one
+// address from every workgroup, a poll, a re-read) costs about as much as a
+// kernel boundary's one cache release, and a grid-wide finish needs several.
 //
-// At small m the packed weight is almost all of the bytes, so the kernel is a
-// weight stream: every byte of x2 is read once, 16 bytes per lane per load,
-// and the 1 KiB a wave loads per instruction is one 128-deep K block of 16
-// columns (the GFX950_B unit), contiguous in memory.
+// Weight stream. At small m the packed weight is almost all of the bytes.
+// Every byte of x2 is read once, 16 bytes per lane per load; the 1 KiB a
+// wave loads per instruction is one 128-deep K block of 16 columns (the
+// GFX950_B unit), contiguous in memory.
 //
-// Work split. A workgroup (8 waves) owns CTW column tiles of 16 over all of K;
-// CTW grows with n so that the grid stays within one wave of workgroups on the
-// 256 compute units. Its waves split K: wave w takes k-blocks [w*kpw,
-// (w+1)*kpw) and issues every load of a batch (weights, x1 fragments, one
-// scale/offset pair per column and block) before its first MFMA. The
-// per-wave sums meet in LDS and are added in a fixed wave order.
+// Work split. A workgroup (16 waves) owns CTW column tiles of 16 over all of
+// K; CTW grows with n so that up to n = 12288 the grid stays within one
+// workgroup per CU. Its waves split K: wave w takes 128-deep blocks
+// [w*kpw, (w+1)*kpw), two blocks in flight: the loads of block b + 1
+// (weights first, then the x1 fragments by buffer -> LDS DMA into one of the
+// wave's two LDS slots, then one scale / offset pair per column) are issued
+// before block b is multiplied. The waves' sums meet in LDS and are added in
+// a fixed wave order.
 //
-// Arithmetic per 128-deep block: the codes enter the MFMA as 16-bit B = q + 24
-// (see wq_unpack.h), one more MFMA against a ones fragment gives the row sums
-// of x, and the block is folded into the float32 result as
-//   acc += s * sum_k x B  +  (o - 24 s) * sum_k x
-// with s, o the block's group scale and offset for the column.
+// Arithmetic per 128-deep block: the codes enter the MFMA as 16-bit
+// B = q + 136 (fp16: q + 1032; wq_unpack.h, unpack8_low), one more MFMA
+// against a ones fragment gives the row sums of x, and the block is folded
+// into the float32 result as
+//   acc += s * sum_k x B  +  (o - 136 s) * sum_k x
+// with s, o the block's group scale and offset for the column: the constant
+// cancels within one block, so the cheaper unpack costs no accuracy here.
 //
 // Epilogue: y = acc + bias + residual (stored rounded to the activation
-// dtype) and per-(row, 16-column tile) sums of the float32 y^2 for the
-// RMSNorm finish.
+// dtype) and, per (workgroup, row), the sum of the float32 y^2 over the
+// workgroup's columns: partial[row][workgroup], so that the finish reads a
+// row's sums as one contiguous run.
 #include "wq_device.h"
 #include "wq_internal.h"
 #include "wq_unpack.h"
@@ -39,13 +49,13 @@ struct DecodeArgs {
   const uint16_t* scale;
   const uint16_t* offset;    // the scale array when there is no offset (omul = 0)
   const uint16_t* bias;      // may be null
-  const uint16_t* residual;
+  const uint16_t* residual;  // may be null (the standalone matmul)
   uint16_t* y;
-  float* partial;            // [m][np / 16]
+  float* partial;            // [m][grid]: sum of y^2 per (row, workgroup); null: none
   int64_t m, k, n, np, nct;  // nct = np / 16 column tiles
   int64_t row0;              // first of the 16 rows this launch computes
   int64_t s_row, s_col;      // scale element (g, n) at g * s_row + n * s_col
-  uint32_t x1_bytes, x2_bytes, s_bytes;
+  uint32_t x1_bytes, x2_bytes, s_bytes, res_bytes;
   int32_t kpw;               // 128-deep K blocks per wave
   int32_t bpg;               // 128-deep K blocks per quantization group
   float omul;                // 1 with an offset, 0 without
@@ -55,115 +65,100 @@ template <int CTW>
 struct DecodeLane {
   __amdgpu_buffer_rsrc_t w, x, s, o;
   uint32_t woff[CTW];        // lane's 16 weight bytes in a K block, per column tile
-  uint32_t xoff;             // x1 row l%16 + 32-deep sub-block l/16 (BUF_OOB for rows >= m)
+  uint32_t xoff;             // x1 row l%16, K sub-block l/16 (BUF_OOB for rows >= m)
   uint32_t soff[CTW];        // lane's scale element per tile (columns clamped to n - 1)
 };
 
+// One 128-deep block's register loads (its x1 fragments go to LDS).
+template <int CTW>
+struct DecodeBatch {
+  u32x4 w[CTW];              // packed codes: dword w4 feeds K step w4
+  uint32_t s[CTW], o[CTW];   // raw 16-bit scale and offset
+};
+
+// vector-memory instructions one batch issues
+template <int CTW>
+constexpr int batch_loads() { return CTW + 4 + 2 * CTW; }
+
 // Loop-carried MFMA accumulators of a wave: the block's partial sums per
-// column tile and the block's row sums of x. They live across the whole K
-// loop and every MFMA updates them in place (cleared in place by a multiply
-// with zero at each block start), so each MFMA's destination is exactly its
-// accumulator source and never overlaps its A or B operand.
+// column tile and the block's row sums of x. Every MFMA updates them in
+// place (cleared in place by a multiply with zero at each block start), so
+// each MFMA's destination is exactly its accumulator source and never
+// overlaps its A or B operand.
 template <int CTW>
 struct DecodeAcc {
   f32x4 part[CTW];
   f32x4 rs;
 };
 
-
-
-// Vector-memory loads decode_blocks issues after block j's four x1 DMAs.
-constexpr int loads_after_dma(int nb, int ctw, int j) {
-  return j < nb ? 4 * (nb - 1 - j) + 3 * nb * ctw : 0;
+// One buffer -> LDS DMA instruction: 16 bytes per lane, written to dst in
+// lane order.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
-// NB consecutive 128-deep K blocks starting at kb. Every load is issued
-// first, in the order of use: the wave's x1 fragments go by DMA into its LDS
-// slice xs (fragment (j, w4) of lane l at xs + 1024 (4j + w4) + 16 l: the
-// lane reads back exactly what it loaded), then the weights, then scales and
-// offsets into registers. Rows >= m read zeros; columns >= n read valid bytes
-// whose results are never stored.
-template <int ACT, int CTW, int NB>
-__device__ __forceinline__ void decode_blocks(const DecodeArgs& a, const DecodeLane<CTW>& ln,
-                                              uint8_t* xs, int kb, DecodeAcc<CTW>& ma,
-                                              f32x4 (&acc)[CTW]) {
-  static_assert(NB == 1 || NB == 2, "the DMA waits are written for one or two blocks");
+// K step w4 pairs the weight dword w4 of lane l (K values 32 (l/16) + 8 w4
+// .. + 7 of its column: the lane's GFX950_B sub-block) with the same eight K
+// values of x1 row l%16. That fragment sits at xs + 1024 w4 + 16 l: each DMA
+// instruction writes its 64 lanes' 16 bytes in lane order, so a lane reads
+// back exactly what it fetched.
+template <int CTW>
+__device__ __forceinline__ void issue_batch(const DecodeArgs& a, const DecodeLane<CTW>& ln, int kb,
+                                            uint8_t* xs, DecodeBatch<CTW>& b) {
+  const uint32_t wso = (uint32_t)kb * (uint32_t)a.np * 64u;
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+    b.w[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c], wso, 0));
+#pragma unroll
+  for (int w4 = 0; w4 < 4; ++w4)
+    dma16(ln.x, xs + 1024 * w4, ln.xoff + 16u * w4, (uint32_t)kb * 256u);
+  const uint32_t sso = (uint32_t)((kb / a.bpg) * a.s_row) * 2u;
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) {
+    b.s[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[c], sso, 0);
+    b.o[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[c], sso, 0);
+  }
+}
+
+template <int ACT, int CTW>
+__device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch<CTW>& b, const uint8_t* xs,
+                                          DecodeAcc<CTW>& ma, f32x4 (&acc)[CTW]) {
   const int lane = threadIdx.x & 63;
-  const uint32_t kslab = (uint32_t)a.np * 64u;
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.x, (lds_void*)(xs + 1024 * (4 * j + w4)), 16,
-                                               ln.xoff + 16u * w4, (uint32_t)(kb + j) * 256u, 0, 0);
-  // the DMAs stay first: the waits below count the loads issued after them
-  __builtin_amdgcn_sched_barrier(0);
-  u32x4 wv[NB][CTW];
-  uint32_t sr[NB][CTW], orw[NB][CTW];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const uint32_t wso = (uint32_t)(kb + j) * kslab;
-#pragma unroll
-    for (int c = 0; c < CTW; ++c)
-      wv[j][c] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c], wso, 0));
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const uint32_t sso = (uint32_t)(((kb + j) / a.bpg) * a.s_row) * 2u;
-#pragma unroll
-    for (int c = 0; c < CTW; ++c) {
-      sr[j][c] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[c], sso, 0);
-      orw[j][c] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[c], sso, 0);
-    }
-  }
-  // keep every load of the batch ahead of the first use (the scheduler would
-  // otherwise sink loads next to their uses and serialize their latencies)
-  __builtin_amdgcn_sched_barrier(0);
   const uint32_t one2 = pack2<ACT>(1.f, 1.f);
   const u32x4 ones = {one2, one2, one2, one2};
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    // block j's x1 DMAs are done once no more than the loads issued after
-    // them (later blocks' DMAs, all weights, scales and offsets) remain
-    if (j == 0) wait_vm<loads_after_dma(NB, CTW, 0)>();
-    else wait_vm<loads_after_dma(NB, CTW, 1)>();
+  for (int i = 0; i < 4; ++i) ma.rs[i] *= 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ma.rs[i] *= 0.f;
+  for (int c = 0; c < CTW; ++c)
 #pragma unroll
-    for (int c = 0; c < CTW; ++c)
+    for (int i = 0; i < 4; ++i) ma.part[c][i] *= 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ma.part[c][i] *= 0.f;
+  for (int w4 = 0; w4 < 4; ++w4) {
+    const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
+    ma.rs = mfma16<ACT>(av, ones, ma.rs);
 #pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * (4 * j + w4) + 16 * lane);
-      ma.rs = mfma16<ACT>(av, ones, ma.rs);
-#pragma unroll
-      for (int c = 0; c < CTW; ++c) {
-        const u32x4 b = unpack8<ACT>(wv[j][c][w4]);
-        ma.part[c] = mfma16<ACT>(av, b, ma.part[c]);
-      }
-      // one K step's operands at a time (bounds the live unpacked fragments)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int c = 0; c < CTW; ++c) {
-      const float s = to_f32<ACT>((uint16_t)sr[j][c]);
-      const float o = to_f32<ACT>((uint16_t)orw[j][c]) * a.omul;
-      const float cc = o - Unpack<ACT>::bias * s;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[c][i], fmaf(cc, ma.rs[i], acc[c][i]));
-    }
+    for (int c = 0; c < CTW; ++c) ma.part[c] = mfma16<ACT>(av, unpack8_low<ACT>(b.w[c][w4]), ma.part[c]);
+    // one K step's operands at a time (bounds the live unpacked fragments)
     __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) {
+    const float s = to_f32<ACT>((uint16_t)b.s[c]);
+    const float o = to_f32<ACT>((uint16_t)b.o[c]) * a.omul;
+    const float cc = o - UnpackLow<ACT>::bias * s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[c][i], fmaf(cc, ma.rs[i], acc[c][i]));
   }
 }
 
-template <int ACT, int CTW, int KBB>
+template <int ACT, int CTW>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_decode(DecodeArgs a) {
-  // per wave: its x1 fragments (KBB blocks), reused at the end for its share
-  // of the cross-wave sum
-  __shared__ __attribute__((aligned(16))) uint8_t xlds[DC_WAVES][KBB * 4096];
-  static_assert(16 * (CTW * 16 + 4) * 4 <= KBB * 4096, "reduction rows must fit a wave's slice");
+  constexpr int RS = CTW * 16 + 4;                  // reduction row stride (floats)
+  // per wave: two 4 KiB x1 slots, reused after the K loop for the wave's
+  // share of the cross-wave sum
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[DC_WAVES][2][4096];
+  static_assert(16 * RS * 4 <= 2 * 4096, "reduction rows must fit a wave's slots");
+  __shared__ float sq[16 * CTW * 8];                // per-thread sums of y^2
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);      // uniform: K ranges are scalar
   const int col = lane & 15, kq = lane >> 4;
@@ -180,8 +175,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   ln.x = buf_rsrc(a.x1, a.x1_bytes);
   ln.s = buf_rsrc(a.scale, a.s_bytes);
   ln.o = buf_rsrc(a.offset, a.s_bytes);
-  const int64_t row = a.row0 + col;
-  ln.xoff = row < a.m ? (uint32_t)(row * a.k * 2 + kq * 64) : BUF_OOB;
+  const int64_t xrow = a.row0 + col;
+  ln.xoff = xrow < a.m ? (uint32_t)(xrow * a.k * 2 + kq * 64) : BUF_OOB;
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
     const int64_t ct = ct0 + c < a.nct ? ct0 + c : a.nct - 1;
@@ -206,13 +201,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   // Unconditional buffer loads (an invalid element reads zero; no bias is a
   // zero-size buffer, as is no residual), so nothing forces a wait before the
   // stream is issued.
-  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual ? a.residual : a.x1, a.residual ? (uint32_t)(a.m * a.n * 2) : 0u);
-  const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias ? a.bias : a.residual, a.bias ? (uint32_t)(a.n * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rres = buf_rsrc(a.residual ? a.residual : a.x1, a.residual ? a.res_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t rbias = buf_rsrc(a.bias ? a.bias : a.x1, a.bias ? (uint32_t)(a.n * 2) : 0u);
   const uint32_t r0 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c0ok ? (uint32_t)(idx * 2) : BUF_OOB, 0, 0);
   const uint32_t r1 = __builtin_amdgcn_raw_buffer_load_b16(rres, rok && c1ok ? (uint32_t)(idx * 2 + 2) : BUF_OOB, 0, 0);
   const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b16(rbias, c0ok ? (uint32_t)(col0 * 2) : BUF_OOB, 0, 0);
   const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b16(rbias, c1ok ? (uint32_t)(col0 * 2 + 2) : BUF_OOB, 0, 0);
 
+  // ---- weight stream: blocks [kb0, kb1), two in flight ----
   const int kbs = (int)(a.k / 128);
   const int kb0 = wave * a.kpw;
   const int kb1 = kb0 + a.kpw < kbs ? kb0 + a.kpw : kbs;
@@ -224,76 +220,106 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     ma.part[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  int kb = kb0;
-  uint8_t* xs = xlds[wave];
-  for (; kb + KBB <= kb1; kb += KBB) decode_blocks<ACT, CTW, KBB>(a, ln, xs, kb, ma, acc);
-  for (; kb < kb1; ++kb) decode_blocks<ACT, CTW, 1>(a, ln, xs, kb, ma, acc);
+  // Batch b's loads complete in issue order, so once no more than the next
+  // batch's loads are outstanding, b's weights, DMA and scales have landed
+  // (the explicit wait also orders the LDS reads after the DMA, which the
+  // compiler does not do by itself). The scheduling barriers keep every load
+  // ahead of the first use.
+  uint8_t* xa = xlds[wave][0];
+  uint8_t* xb = xlds[wave][1];
+  DecodeBatch<CTW> ba, bb;
+  if (kb0 < kb1) issue_batch<CTW>(a, ln, kb0, xa, ba);
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    if (kb + 1 < kb1) issue_batch<CTW>(a, ln, kb + 1, xb, bb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 1 < kb1) wait_vm<batch_loads<CTW>()>();
+    else wait_vm<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma_batch<ACT, CTW>(a, ba, xa, ma, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 1 >= kb1) break;
+    if (kb + 2 < kb1) issue_batch<CTW>(a, ln, kb + 2, xa, ba);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 2 < kb1) wait_vm<batch_loads<CTW>()>();
+    else wait_vm<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma_batch<ACT, CTW>(a, bb, xb, ma, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ---- combine the waves' K slices in a fixed order ----
-  // (the wave's own x1 reads are complete: their values fed its MFMAs)
-  constexpr int RS = CTW * 16 + 4;                 // reduction row stride (floats)
-  float* red = reinterpret_cast<float*>(xs);
+  // (the wave's own LDS reads are complete: their values fed its MFMAs)
+  float* myred = reinterpret_cast<float*>(xlds[wave][0]);
 #pragma unroll
   for (int i = 0; i < CTW; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[(4 * kq + e) * RS + i * 16 + col] = acc[i][e];
+    for (int e = 0; e < 4; ++e) myred[(4 * kq + e) * RS + i * 16 + col] = acc[i][e];
   __syncthreads();
 
-  // ---- epilogue: y = acc + bias + residual, sums of y^2 per 16-column tile ----
-  if (!epi) return;
-  float v0 = 0.f, v1 = 0.f;
+  // ---- epilogue: y = acc + bias + residual; sums of y^2 ----
+  float ss = 0.f;
+  if (epi) {
+    float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-  for (int w = 0; w < DC_WAVES; ++w) {
-    const float* rw = reinterpret_cast<const float*>(xlds[w]);
-    v0 += rw[r * RS + c];
-    v1 += rw[r * RS + c + 1];
-  }
-  float y0 = 0.f, y1 = 0.f;
-  if (rok) {
-    y0 = v0 + to_f32<ACT>((uint16_t)b0) + to_f32<ACT>((uint16_t)r0);
-    y1 = v1 + to_f32<ACT>((uint16_t)b1) + to_f32<ACT>((uint16_t)r1);
-    const uint32_t o2 = pack2<ACT>(y0, y1);
-    if (pair) {
-      *reinterpret_cast<uint32_t*>(a.y + idx) = o2;
-    } else {
-      if (c0ok) a.y[idx] = (uint16_t)(o2 & 0xFFFFu);
-      if (c1ok) a.y[idx + 1] = (uint16_t)(o2 >> 16);
+    for (int w = 0; w < DC_WAVES; ++w) {
+      const float* rw = reinterpret_cast<const float*>(xlds[w][0]);
+      v0 += rw[r * RS + c];
+      v1 += rw[r * RS + c + 1];
     }
-    y0 = c0ok ? y0 : 0.f;                 // the sum of squares uses float32 y
-    y1 = c1ok ? y1 : 0.f;
+    if (rok) {
+      float y0 = v0 + to_f32<ACT>((uint16_t)b0) + to_f32<ACT>((uint16_t)r0);
+      float y1 = v1 + to_f32<ACT>((uint16_t)b1) + to_f32<ACT>((uint16_t)r1);
+      const uint32_t o2 = pack2<ACT>(y0, y1);
+      if (pair) {
+        *reinterpret_cast<uint32_t*>(a.y + idx) = o2;
+      } else {
+        if (c0ok) a.y[idx] = (uint16_t)(o2 & 0xFFFFu);
+        if (c1ok) a.y[idx + 1] = (uint16_t)(o2 >> 16);
+      }
+      y0 = c0ok ? y0 : 0.f;                 // the sum of squares uses float32 y
+      y1 = c1ok ? y1 : 0.f;
+      ss = y0 * y0 + y1 * y1;
+    }
+    sq[t] = ss;
   }
-  // sum of y^2 over the 16 columns of the tile: 8 aligned lanes
-  float ss = y0 * y0 + y1 * y1;
-  ss = quad_sum(ss);
-  ss += dpp_f32<0x141>(ss);
-  if ((cp & 7) == 0 && rok && tile_ok) a.partial[orow * a.nct + ct0 + (c >> 4)] = ss;
-}
-
-template <int ACT, int CTW>
-void launch_ct(const DecodeArgs& a, unsigned grid, hipStream_t s) {
-  prof_begin(s);
-  gemm_decode<ACT, CTW, 2><<<dim3(grid), 1024, 0, s>>>(a);
-  prof_end(s);
+  if (!a.partial) return;                   // the standalone matmul: no norm
+  __syncthreads();
+  if (t < 16 && a.row0 + t < a.m) {
+    float s = 0.f;
+    for (int i = 0; i < TPR; ++i) s += sq[t * TPR + i];
+    a.partial[(a.row0 + t) * gridDim.x + blockIdx.x] = s;
+  }
 }
 
 template <int ACT>
 void launch_act(const DecodeArgs& a, int ctw, unsigned grid, hipStream_t s) {
+  prof_begin(s);
   switch (ctw) {
-    case 1: launch_ct<ACT, 1>(a, grid, s); break;
-    case 2: launch_ct<ACT, 2>(a, grid, s); break;
-    default: launch_ct<ACT, 3>(a, grid, s); break;
+    case 1: gemm_decode<ACT, 1><<<dim3(grid), 1024, 0, s>>>(a); break;
+    case 2: gemm_decode<ACT, 2><<<dim3(grid), 1024, 0, s>>>(a); break;
+    default: gemm_decode<ACT, 3><<<dim3(grid), 1024, 0, s>>>(a); break;
   }
+  prof_end(s);
 }
 
-}  // namespace
+// column tiles per workgroup: keep the grid within one workgroup per CU up to
+// 768 tiles (n = 12288); wider layers take more workgroups of 3
+int decode_ctw(int64_t nct) { return nct <= 256 ? 1 : nct <= 512 ? 2 : 3; }
 
-int64_t decode_tiles(int64_t n) { return (n + 15) / 16; }
+}  // namespace
 
 // The weight stream addresses the packed weight through one buffer resource
 // whose out-of-range offset is 2^31: the weight must stay below 2 GiB.
 bool decode_ok(const WqProblem& p) {
   return p.m <= 32 && (p.k / 128) * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
 }
+
+// Per-(row, workgroup) sums of y^2 of the decode kernel: [32][grid] at most.
+int64_t decode_grid(int64_t n) {
+  const int64_t nct = (n + 15) / 16;
+  return (nct + decode_ctw(nct) - 1) / decode_ctw(nct);
+}
+size_t decode_partial_bytes(int64_t n) { return (size_t)(decode_grid(n) * 32 * 4); }
 
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   DecodeArgs a;
@@ -305,7 +331,7 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   a.bias = static_cast<const uint16_t*>(p.bias);
   a.residual = static_cast<const uint16_t*>(p.residual);
   a.y = static_cast<uint16_t*>(p.y);
-  a.partial = partial;
+  a.partial = p.norm_out ? partial : nullptr;
   a.m = p.m;
   a.k = p.k;
   a.n = p.n;
@@ -319,12 +345,11 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   a.x1_bytes = (uint32_t)(p.m * p.k * 2);
   a.x2_bytes = (uint32_t)(p.k / 128 * a.np * 64);
   a.s_bytes = (uint32_t)(((groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
+  a.res_bytes = (uint32_t)(p.m * p.n * 2);
   const int64_t kbs = p.k / 128;
   a.kpw = (int32_t)((kbs + DC_WAVES - 1) / DC_WAVES);
-  // column tiles per workgroup: keep the grid within one workgroup per CU
-  // up to 768 tiles (n = 12288); wider layers take more workgroups of 3
-  const int ctw = a.nct <= 256 ? 1 : a.nct <= 512 ? 2 : 3;
-  const unsigned grid = (unsigned)((a.nct + ctw - 1) / ctw);
+  const int ctw = decode_ctw(a.nct);
+  const unsigned grid = (unsigned)decode_grid(p.n);
   // one launch per 16 rows (m <= 32: at most two; the second finds the
   // weights in the last-level cache)
   for (a.row0 = 0; a.row0 < p.m; a.row0 += 16) {

@@ -69,9 +69,11 @@ hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint
                           hipStream_t s);
 
 // Weight-streaming kernel for m <= 32 on the same fast-path problems; writes
-// sums of y^2 per (row, 16-column tile), row-major: decode_tiles(n) per row.
-int64_t decode_tiles(int64_t n);
+// one sum of y^2 per (row, workgroup) at partial[row * decode_grid(n) +
+// workgroup].
 bool decode_ok(const WqProblem& p);
+int64_t decode_grid(int64_t n);
+size_t decode_partial_bytes(int64_t n);
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s);
 
 struct MxProblem {

@@ -110,4 +110,28 @@ __device__ __forceinline__ u32x4 unpack8(uint32_t w) {
   return r;
 }
 
+// Eight codes of one dword -> four dwords of (q + 136) (bf16) or (q + 1032)
+// (fp16): the nibble in the low mantissa bits, one shift per dword and one
+// permute plus one bitop3 per output dword (9 operations per 8 codes). The
+// larger constant is harmless where the partial sums are folded into float32
+// every 128 K values (the decode kernel); accumulators that run over many
+// groups use the q + 24 form above.
+template <int ACT>
+struct UnpackLow {
+  static constexpr float bias = ACT == ACT_BF16 ? 136.f : 1032.f;
+  static constexpr uint32_t xbits = ACT == ACT_BF16 ? 0x43084308u : 0x64086408u;
+};
+
+template <int ACT>
+__device__ __forceinline__ u32x4 unpack8_low(uint32_t w) {
+  constexpr uint32_t m = 0x000F000Fu, c = UnpackLow<ACT>::xbits;
+  const uint32_t w4 = w >> 4;
+  u32x4 r;
+  r.x = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C040C00u), m, c);
+  r.y = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C050C01u), m, c);
+  r.z = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C060C02u), m, c);
+  r.w = xor_and(__builtin_amdgcn_perm(w4, w, 0x0C070C03u), m, c);
+  return r;
+}
+
 }  // namespace wq

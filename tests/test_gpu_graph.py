@@ -65,7 +65,7 @@ class _WQCall:
         self.y = torch.empty_like(self.residual)
         self.norm = torch.empty_like(self.residual)
         self.ws_n = wq.wq_matmul_add_rmsnorm_workspace_size(m, k, n)
-        self.ws = torch.empty(max(self.ws_n, 1), dtype=torch.uint8, device=DEV)
+        self.ws = torch.zeros(max(self.ws_n, 1), dtype=torch.uint8, device=DEV)
 
     def __call__(self):
         s = self.scale
@@ -252,7 +252,7 @@ def test_unfused_chain_replays():
     res, gam = c.residual.to(DEV).reshape(m, n), c.gamma.to(DEV)
     mm = torch.empty((m, n), dtype=x1.dtype, device=DEV)
     y, nrm = torch.empty_like(mm), torch.empty_like(mm)
-    ws = torch.empty(wq.wq_weight_quant_matmul_workspace_size(m, k, n), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wq.wq_weight_quant_matmul_workspace_size(m, k, n), dtype=torch.uint8, device=DEV)
 
     def fn():
         wq.weight_quant_matmul(x1, x2, k, n, wq.WQ_INT4, sc, off, c.group_size, bias, out=mm,

@@ -93,3 +93,22 @@ def test_operand_range_is_exact_and_positive():
     vals = halves(unpack_bf16(pack_codes(list(range(-8, 0)))), "bf16") + \
         halves(unpack_f16(pack_codes(list(range(0, 8)))), "f16")
     assert vals == [float(v) for v in range(16, 32)]
+
+
+def unpack_low(w: int, fmt: str):
+    """The decode kernel's 9-operation form: nibble in the low mantissa bits,
+    q + 136 (bf16, exponent bits 0x4300) or q + 1032 (fp16, 0x6400)."""
+    c = 0x43084308 if fmt == "bf16" else 0x64086408
+    w4 = w >> 4
+    return [bitop3_6a(perm(w4, w, 0x0C040C00 + 0x00010001 * j), 0x000F000F, c) for j in range(4)]
+
+
+def test_low_mantissa_form_every_code_pair():
+    for fmt, bias in (("bf16", 136.0), ("f16", 1032.0)):
+        for a in range(-8, 8):
+            for b in range(-8, 8):
+                for pos in range(0, 8, 2):
+                    codes = [(7 * i + 1) % 16 - 8 for i in range(8)]
+                    codes[pos], codes[pos + 1] = a, b
+                    got = halves(unpack_low(pack_codes(codes), fmt), fmt)
+                    assert got == [c + bias for c in codes], (fmt, codes, got)
