@@ -34,12 +34,14 @@ WQ_INT32, WQ_FP8_E4M3, WQ_FP4_E2M1, WQ_E8M0 = 6, 7, 8, 9
 WQ_LAYOUT_ND, WQ_LAYOUT_GFX950_B = 0, 1
 
 MX_GROUP_SIZE = 32 | (1 << 16) | (1 << 32)
+WQ_NOALLOC_MAX_WORKSPACE = 32 << 20      # the allocation-free call's device array
 
 EXPORTS = (
     "wq_status_string", "wq_abi_version",
     "wq_pack_int4_bytes", "wq_pack_int4", "wq_pack_fp4",
     "wq_dynamic_quant",
     "wq_matmul_add_rmsnorm_workspace_size", "wq_matmul_add_rmsnorm",
+    "wq_matmul_add_rmsnorm_noalloc",
     "mx_quant_matmul_inplace_add_workspace_size", "mx_quant_matmul_inplace_add",
     "wq_quant_matmul_inplace_add", "wq_quant_matmul_inplace_add_w4",
     "mx_fp4_quant_matmul_inplace_add_workspace_size", "mx_fp4_quant_matmul_inplace_add",
@@ -75,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "wq_matmul_add_rmsnorm_workspace_size": (S, [I64, I64, I64]),
             "wq_matmul_add_rmsnorm": (I, [P, I64, I64, I, P, I64, I, I, I, P, I64, I64, P, I64,
                                           P, P, P, D, P, P, P, S, P]),
+            "wq_matmul_add_rmsnorm_noalloc": (I, [P, I64, I64, I, P, I64, I, I, I, P, I64, I64, P,
+                                                  I64, P, P, P, D, P, P, P]),
             "mx_quant_matmul_inplace_add_workspace_size": (S, [I64, I64, I64]),
             "mx_quant_matmul_inplace_add": (I, [P, P, I, P, P, I64, I64, I64, I, I, I64, P, P, S, P]),
             "wq_quant_matmul_inplace_add": (I, [P, P, P, P, I64, I64, I64, P, P]),
@@ -186,6 +190,17 @@ def wq_matmul_add_rmsnorm(x1, m, k, act_dtype, x2, n, w_dtype, x2_layout, transp
         _ptr(residual), _ptr(gamma), float(epsilon), _ptr(y), _ptr(norm_out),
         _ptr(workspace), workspace_size, _stream(stream))
     return _check(st, "wq_matmul_add_rmsnorm", check)
+
+
+def wq_matmul_add_rmsnorm_noalloc(x1, m, k, act_dtype, x2, n, w_dtype, x2_layout, transpose_x2,
+                                  scale, scale_rows, scale_cols, offset, group_size, bias,
+                                  residual, gamma, epsilon, y, norm_out, stream=None,
+                                  check=True) -> int:
+    st = lib().wq_matmul_add_rmsnorm_noalloc(
+        _ptr(x1), m, k, act_dtype, _ptr(x2), n, w_dtype, x2_layout, int(transpose_x2),
+        _ptr(scale), scale_rows, scale_cols, _ptr(offset), group_size, _ptr(bias),
+        _ptr(residual), _ptr(gamma), float(epsilon), _ptr(y), _ptr(norm_out), _stream(stream))
+    return _check(st, "wq_matmul_add_rmsnorm_noalloc", check)
 
 
 def wq_pack_fp4(weight, k, n, transpose, layout, out, stream=None, check=True) -> int:

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_profile.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
            "wq_gemm_decode.hip", "mx_gemm.hip", "i8_gemm.hip", "add_rmsnorm.hip",
-           "mx4_gemm.hip", "a8w4_gemm.hip"]
+           "mx4_gemm.hip", "a8w4_gemm.hip", "wq_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -213,6 +213,32 @@ wq_status wq_matmul_add_rmsnorm(
     void* workspace, size_t workspace_size, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The same operator for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * allocation. Arguments and results are those of wq_matmul_add_rmsnorm
+ * without the workspace: the kernels use a library-owned device array of
+ * WQ_NOALLOC_MAX_WORKSPACE bytes instead (one per GPU, held until the process
+ * ends; its address is looked up once per device, with the calling thread's
+ * current device). The call allocates and frees nothing.
+ * A problem whose wq_matmul_add_rmsnorm_workspace_size(m, k, n) exceeds
+ * WQ_NOALLOC_MAX_WORKSPACE returns WQ_ERR_WORKSPACE before any other check;
+ * so does any non-empty problem when the array cannot be located. Every
+ * other rule and error is wq_matmul_add_rmsnorm's.
+ * Every call on one GPU shares that GPU's array (the kernels need no initial
+ * contents): calls that can overlap on one GPU (different streams without
+ * ordering) race on it and must not be issued.
+ * ---------------------------------------------------------------------- */
+#define WQ_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+wq_status wq_matmul_add_rmsnorm_noalloc(
+    const void* x1, int64_t m, int64_t k, wq_dtype act_dtype,
+    const void* x2, int64_t n, wq_dtype w_dtype, wq_layout x2_layout,
+    int transpose_x2,
+    const void* antiquant_scale, int64_t scale_rows, int64_t scale_cols,
+    const void* antiquant_offset, int64_t antiquant_group_size,
+    const void* bias, const void* residual, const void* gamma,
+    double epsilon, void* y, void* norm_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * MXFP4 x MXFP4 quantized matmul with in-place add.
  * aclnnQuantBatchMatmulInplaceAdd page, Formula (mx quantization), read with
  * both operands FLOAT4_E2M1:

@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -173,6 +173,25 @@ def test_wq_matmul_validation_pointers_workspace_alias():
     assert _wqmm(ws=FAKE + 0x40000) == wq.WQ_ERR_ALIAS               # over gamma
     assert _wqmm(ws=FAKE + 0x80000, offset=FAKE + 0x80000) == wq.WQ_ERR_ALIAS  # over the offset
     assert _wqmm(ws=FAKE + 0x80000, bias=FAKE + 0x80000) == wq.WQ_ERR_ALIAS    # over bias
+
+
+def test_noalloc_validation_without_a_device():
+    # the size rule is checked first, on the host: nothing touches the GPU
+    F = FAKE
+    assert wq.wq_matmul_add_rmsnorm_workspace_size(65536, 8192, 8192) > wq.WQ_NOALLOC_MAX_WORKSPACE
+    st = wq.lib().wq_matmul_add_rmsnorm_noalloc(
+        F, 65536, 8192, wq.WQ_BF16, F + (1 << 32), 8192, wq.WQ_INT4, wq.WQ_LAYOUT_GFX950_B, 0,
+        F + (2 << 32), 64, 8192, None, 128, None, F + (3 << 32), F + (4 << 32), 1e-6,
+        F + (5 << 32), F + (6 << 32), 0)
+    assert st == wq.WQ_ERR_WORKSPACE
+    # the workspace call's rules apply unchanged; an empty problem is a no-op
+    L = wq.lib()
+    args = lambda m, act, G: (F, m, 256, act, F + 0x10000, 128, wq.WQ_INT4, wq.WQ_LAYOUT_GFX950_B, 0,
+                              F + 0x20000, 8, 128, None, G, None, F + 0x30000, F + 0x40000, 1e-6,
+                              F + 0x50000, F + 0x60000, 0)
+    assert L.wq_matmul_add_rmsnorm_noalloc(*args(0, wq.WQ_BF16, 32)) == wq.WQ_OK
+    assert L.wq_matmul_add_rmsnorm_noalloc(*args(16, wq.WQ_F32, 32)) == wq.WQ_ERR_DTYPE
+    assert L.wq_matmul_add_rmsnorm_noalloc(*args(16, wq.WQ_BF16, 48)) == wq.WQ_ERR_GROUP
 
 
 def _mx(**kw):
