@@ -174,6 +174,7 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
 // Main tile
 // ---------------------------------------------------------------------------
 constexpr int WD_BM = 128, WD_BN = 512, WD_KS = 128;
+constexpr int WD_GM = 4;                           // tile-rows per group of the tile order
 constexpr int WD_LROW = WD_KS * 2;                 // LDS bytes per x1 row
 constexpr int WD_ABUF = WD_BM * WD_LROW;           // x1 slab: 32 KiB
 constexpr int WD_BBUF = WD_BN * 64;                // weight slab: 32 KiB
@@ -593,18 +594,19 @@ __global__ __launch_bounds__(512, 1) void gemm_b_wide(FastArgs a, int64_t tiles_
   const int t = threadIdx.x, lane = t & 63, wave = wave_id();
 
   // XCD-aware tile order: consecutive workgroups land on different XCDs, so
-  // give each XCD a contiguous range of tiles, walked two tile-rows at a time.
+  // give each XCD a contiguous range of tiles. The range is walked in groups
+  // of WD_GM tile-rows, down each group's rows and then across its columns:
+  // the 32 tiles an XCD runs at once then span 4 tile-rows x 8 weight strips
+  // (per 128-deep slab 4 x 32 KiB of x1 + 8 x 32 KiB of weight through its
+  // L2), not 2 rows x 16 strips (2 x 32 + 16 x 32 KiB).
   const int64_t T = tiles_m * tiles_n;
   int64_t id = blockIdx.x;
   if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
-  const int64_t band = id / (2 * tiles_n);
-  const int64_t rem = id % (2 * tiles_n);
-  int64_t tm = band * 2 + (rem & 1);
-  int64_t tn = rem >> 1;
-  if (band * 2 + 1 >= tiles_m && (tiles_m & 1)) {  // last odd band: one tile-row
-    tm = band * 2;
-    tn = rem;
-  }
+  const int64_t grp = id / (WD_GM * tiles_n);
+  const int64_t rows_g = tiles_m - grp * WD_GM < WD_GM ? tiles_m - grp * WD_GM : WD_GM;
+  const int64_t rem = id - grp * WD_GM * tiles_n;
+  const int64_t tm = grp * WD_GM + rem % rows_g;
+  const int64_t tn = rem / rows_g;
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // tile origin (and the buffer resources built from it) in scalar registers
   const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)tm) * WD_BM;
