@@ -183,17 +183,20 @@ static_assert(32 * WD_EROW <= 16384, "epilogue staging must fit a wave's 16 KiB 
 
 // x1 slab (128 rows x 128 K) -> LDS: 32 DMA instructions of 1 KiB (4 rows);
 // wave w issues 4w + j: rows 16w + 4j + lane/16. LDS rows are 256 bytes; the
-// 16-byte chunk of row r at position p holds logical chunk p ^ (r & 15), so
-// the A-fragment reads of 16 lanes (16 rows, one K chunk) hit 16 distinct
-// bank groups. With r & 15 = lane/16 + 4j the lane's source chunk is
-// c0 ^ 4j, c0 = (lane & 15) ^ (lane / 16), and its byte offset is
-// (v0 ^ 64j) + 8jk with v0 = (16w + lane/16) * 2k + 16 c0 (2k is a multiple
-// of 256, so the XOR only touches the chunk bits). The buffer resource
-// starts at the slab and ends after the tile's last row: rows past m read 0.
+// 16-byte chunk of row r at position p holds logical chunk p ^ h(r & 15),
+// h(r) = (r mod 4) * 4 + r / 4: the 16-byte A-fragment reads (16 rows, one
+// K chunk per lane group) then run at the rate of linear reads, measured
+// with an LDS probe on gfx950 (p ^ r, whose 16 positions are distinct in
+// every group of 16 lanes, ran 1.38x slower). With r & 15 = 4j + lane/16,
+// h(r) = 4 (lane/16) + j, so the lane's source chunk is c0 ^ j, c0 =
+// (lane & 15) ^ 4 (lane / 16), and its byte offset is (v0 ^ 16j) + 8jk with
+// v0 = (16w + lane/16) * 2k + 16 c0 (2k is a multiple of 256, so the XOR only
+// touches the chunk bits). The buffer resource starts at the slab and ends
+// after the tile's last row: rows past m read 0.
 __device__ __forceinline__ void wd_dma_a1(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf,
                                           int j) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (4 * wave_id() + j) * 4 * WD_LROW), 16,
-                                           (v0 ^ (64u * j)) + 8u * j * k, 0, 0, 0);
+                                           (v0 ^ (16u * j)) + 8u * j * k, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wd_dma_a(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf) {
@@ -256,10 +259,11 @@ __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf
   // makes the weight reads conflict-free; each group still covers its block
   // once over the four steps.
   const int g = lane >> 4, cl = lane & 15;
+  const int hcl = ((cl & 3) << 2) | (cl >> 2);           // the row swizzle h(cl)
   const uint8_t* arow = abuf + cl * WD_LROW;
   const uint8_t* brow = wbuf + wave * 4096 + 16 * (4 * cl + (g ^ (cl >> 2)));
   auto a_at = [&](int i, int c) {
-    return *reinterpret_cast<const u32x4*>(arow + i * 16 * WD_LROW + (((4 * g + ((c + g) & 3)) ^ cl) * 16));
+    return *reinterpret_cast<const u32x4*>(arow + i * 16 * WD_LROW + (((4 * g + ((c + g) & 3)) ^ hcl) * 16));
   };
   auto b_at = [&](int f, int c) {
     return *reinterpret_cast<const uint32_t*>(brow + f * 1024 + 4 * ((c + g) & 3));
@@ -341,7 +345,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
   //      resources are rebuilt per slab in scalar registers ----
   const int rows_left = (int)(a.m - m0 < WD_BM ? a.m - m0 : WD_BM);
   const uint32_t a_v0 = (uint32_t)(16 * wave + (lane >> 4)) * 2u * k +
-                        16u * (uint32_t)((lane & 15) ^ (lane >> 4));
+                        16u * (uint32_t)((lane & 15) ^ ((lane >> 4) << 2));
   const uint32_t b_v0 = wd_b_v0(wave, lane);
   const int64_t slab_bytes = a.np * 64;
   // (the slab after the last one gets empty resources: its DMA, issued
