@@ -114,10 +114,12 @@ def test_integer_valued_and_linear(k, m, n):
     assert np.array_equal(y2, 2 * want)
 
 
-def test_full_pipeline_from_float_inputs_sampled():
+def test_full_pipeline_from_float_inputs():
     """x (4096, 8192) fp16 with smooth scales -> MX E4M3 (transposed) on the
     GPU; W (8192, 4096) N(0,1) quantized to MXFP4 by the oracle; y += on the
-    GPU; checked on sampled rows against the oracle on the same codes."""
+    GPU; every output checked against the oracle on the same codes (the
+    oracle runs over 16 row blocks in parallel threads), then a second call
+    on the same inputs reproduces the first bit for bit."""
     c = workloads.mx()
     m, k, n = c.mkn
     note(f"mx full pipeline {m}x{k}x{n}")
@@ -127,16 +129,24 @@ def test_full_pipeline_from_float_inputs_sampled():
     s2 = s2_t.T.copy()                                         # (kb, n)
     x2p = wq.pack_int4(torch.from_numpy(x2_codes.astype(np.int32)).to(DEV), wq.WQ_LAYOUT_GFX950_B)
     y = c.y.to(DEV)
-    wq.mx_matmul_inplace_add(x1q, x2p, s1, torch.from_numpy(s2).to(DEV), y, m, k, n)
+    s2d = torch.from_numpy(s2).to(DEV)
+    wq.mx_matmul_inplace_add(x1q, x2p, s1, s2d, y, m, k, n)
+    y2 = c.y.to(DEV)
+    wq.mx_matmul_inplace_add(x1q, x2p, s1, s2d, y2, m, k, n)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 63, 64, 2047, 4095])
+    assert torch.equal(y, y2), "two calls on the same inputs differ"
     x1_codes = x1q.cpu().numpy()                               # (k, m): GPU-quantized, checked
     codes_x, s1_o = oracle.dynamic_quant_mx(as_f64(c.x), as_f64(c.smooth), "e4m3")
     assert np.array_equal(s1.cpu().numpy(), s1_o) and np.array_equal(x1_codes, codes_x.T)
-    want = oracle.mx_quant_matmul_inplace_add(codes_x.T[:, rows], x2_codes, s1_o[rows], s2,
-                                              as_f64(c.y)[rows])
-    got = y.cpu().numpy()[rows].astype(np.float64)
+    y0 = as_f64(c.y)
+    from concurrent.futures import ThreadPoolExecutor
+    blocks = [np.arange(r, r + 256) for r in range(0, m, 256)]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        want = np.concatenate(list(ex.map(
+            lambda rows: oracle.mx_quant_matmul_inplace_add(codes_x.T[:, rows], x2_codes, s1_o[rows], s2,
+                                                            y0[rows]), blocks)))
+    got = y.cpu().numpy().astype(np.float64)
     err = oracle.rel_err_floor(got, want)
-    note(f"  rel err {err:.3e}")
+    note(f"  rel err {err:.3e} over all {m * n} outputs")
     assert err <= 2e-2
-    assert np.all(np.isfinite(y.cpu().numpy()))
+    assert np.all(np.isfinite(got))
