@@ -354,8 +354,8 @@ hipError_t wq_rows(const WqProblem& p, hipStream_t s) {
   // partials: [row][tile] with 32-column tiles, or the decode kernel's
   // [row][workgroup]: partial i of row r at i * ts + r * rstride
   int64_t tiles = (p.n + 31) / 32, ts = 1, rstride = tiles;
-  if (fast_path_ok(p) && decode_ok(p)) {
-    tiles = decode_grid(p.n);
+  if (decode_ok(p)) {
+    tiles = decode_grid(p);
     rstride = tiles;
     e = launch_decode(p, a.partial, s);
   } else if (fast_path_ok(p)) {

@@ -1,6 +1,6 @@
 // Decode-shaped weight-quantized GEMM (m <= 32) for INT4 weights in the
-// GFX950_B layout, group a multiple of 128 along K (or per channel / per
-// tensor), k a multiple of 128. Same operator as wq_gemm.hip
+// GFX950_B layout, any group the pages allow (a multiple of 32 along K, or
+// per channel / per tensor), k a multiple of 128. Same operator as wq_gemm.hip
 // (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula); the RMSNorm
 // finish runs as the next launch (rmsnorm_finish), which on this GPU costs
 // less than any in-kernel grid synchronization: every cross-XCD handoff
@@ -24,11 +24,23 @@
 //
 // Arithmetic per 128-deep block: the codes enter the MFMA as 16-bit
 // B = q + 136 (fp16: q + 1032; wq_unpack.h, unpack8_low), one more MFMA
-// against a ones fragment gives the row sums of x, and the block is folded
-// into the float32 result as
+// against a ones fragment gives the row sums of x, and each group's share of
+// the block is folded into the float32 result as
 //   acc += s * sum_k x B  +  (o - 136 s) * sum_k x
-// with s, o the block's group scale and offset for the column: the constant
-// cancels within one block, so the cheaper unpack costs no accuracy here.
+// with s, o that group's scale and offset for the column: the constant
+// cancels within one fold, so the cheaper unpack costs no accuracy here.
+//
+// Groups shorter than 128 (SPG = 32-deep K steps per fold: 1 for a group
+// that is an odd multiple of 32, 2 for an odd multiple of 64, 4 otherwise).
+// The GFX950_B load gives lane row R (lanes 16R .. 16R + 15) the four dwords
+// of 32-deep sub-block R, so one MFMA step would mix all four sub-blocks.
+// Two rounds of cross-row lane swaps (v_permlane32_swap, then
+// v_permlane16_swap) transpose the 4 x 4 dwords: afterwards step j holds
+// sub-block j in every row, i.e. K values 128 kb + 32 j .. + 31, which lie in
+// one group, and the x1 fragments are fetched to match (row R, K values
+// 32 j + 8 R .. + 7). Each fold unit then has its own MFMA accumulators, and
+// its scale and offset, loaded by the lanes of one row, reach the other rows
+// by the same swaps.
 //
 // Epilogue: y = acc + bias + residual (stored rounded to the activation
 // dtype) and, per (workgroup, row), the sum of the float32 y^2 over the
@@ -57,15 +69,20 @@ struct DecodeArgs {
   int64_t s_row, s_col;      // scale element (g, n) at g * s_row + n * s_col
   uint32_t x1_bytes, x2_bytes, s_bytes, res_bytes;
   int32_t kpw;               // 128-deep K blocks per wave
-  int32_t bpg;               // 128-deep K blocks per quantization group
+  int32_t bpg;               // 128-deep K blocks per quantization group (SPG = 4)
+  float upg_rcp;             // 1 / (fold units per group) (SPG < 4)
   float omul;                // 1 with an offset, 0 without
 };
+
+// fold units per 128-deep block
+template <int SPG>
+constexpr int fold_units() { return 4 / SPG; }
 
 template <int CTW>
 struct DecodeLane {
   __amdgpu_buffer_rsrc_t w, x, s, o;
   uint32_t woff[CTW];        // lane's 16 weight bytes in a K block, per column tile
-  uint32_t xoff;             // x1 row l%16, K sub-block l/16 (BUF_OOB for rows >= m)
+  uint32_t xoff;             // x1 row l%16, first K fragment of the lane (BUF_OOB for rows >= m)
   uint32_t soff[CTW];        // lane's scale element per tile (columns clamped to n - 1)
 };
 
@@ -85,10 +102,10 @@ constexpr int batch_loads() { return CTW + 4 + 2 * CTW; }
 // place (cleared in place by a multiply with zero at each block start), so
 // each MFMA's destination is exactly its accumulator source and never
 // overlaps its A or B operand.
-template <int CTW>
+template <int CTW, int U>
 struct DecodeAcc {
-  f32x4 part[CTW];
-  f32x4 rs;
+  f32x4 part[U][CTW];        // per fold unit
+  f32x4 rs[U];
 };
 
 // One buffer -> LDS DMA instruction: 16 bytes per lane, written to dst in
@@ -102,42 +119,109 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, ui
 // values of x1 row l%16. That fragment sits at xs + 1024 w4 + 16 l: each DMA
 // instruction writes its 64 lanes' 16 bytes in lane order, so a lane reads
 // back exactly what it fetched.
-template <int CTW>
+//
+// With SPG < 4 the fragment of step w4 is x1 K values 32 w4 + 8 (l/16) ..
+// + 7 (the transposed weights), i.e. offset xoff + 64 w4, and lane row R
+// loads the scale and offset of fold unit R / SPG: group
+// floor((unit + 1/2) / upg) with upg fold units per group, exact in float32
+// for every unit index below 2^11 (k < 2^16).
+template <int CTW, int SPG>
 __device__ __forceinline__ void issue_batch(const DecodeArgs& a, const DecodeLane<CTW>& ln, int kb,
                                             uint8_t* xs, DecodeBatch<CTW>& b) {
   const uint32_t wso = (uint32_t)kb * (uint32_t)a.np * 64u;
 #pragma unroll
   for (int c = 0; c < CTW; ++c)
     b.w[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c], wso, 0));
+  constexpr uint32_t xstep = SPG == 4 ? 16u : 64u;
 #pragma unroll
   for (int w4 = 0; w4 < 4; ++w4)
-    dma16(ln.x, xs + 1024 * w4, ln.xoff + 16u * w4, (uint32_t)kb * 256u);
-  const uint32_t sso = (uint32_t)((kb / a.bpg) * a.s_row) * 2u;
+    dma16(ln.x, xs + 1024 * w4, ln.xoff + xstep * w4, (uint32_t)kb * 256u);
+  uint32_t vso = 0u, sso = 0u;
+  if constexpr (SPG == 4) {
+    sso = (uint32_t)((kb / a.bpg) * a.s_row) * 2u;
+  } else {
+    const int unit = kb * fold_units<SPG>() + (int)((threadIdx.x & 63) >> 4) / SPG;
+    const uint32_t g = (uint32_t)(((float)unit + 0.5f) * a.upg_rcp);
+    vso = g * (uint32_t)a.s_row * 2u;
+  }
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
-    b.s[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[c], sso, 0);
-    b.o[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[c], sso, 0);
+    b.s[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[c] + vso, sso, 0);
+    b.o[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[c] + vso, sso, 0);
   }
 }
 
-template <int ACT, int CTW>
+// Cross-row lane swaps (rows of 16 lanes, r0 .. r3), in the layout of the
+// gfx950 instructions:
+//   v_permlane32_swap(a, b): a' = [a0, a1, b0, b1], b' = [a2, a3, b2, b3]
+//   v_permlane16_swap(a, b): a' = [a0, b0, a2, b2], b' = [a1, b1, a3, b3]
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// 4 x 4 transpose of (lane row, register): register j of row R <- register
+// R of row j.
+__device__ __forceinline__ u32x4 transpose_rows(u32x4 d) {
+  uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3];
+  swap32(d0, d2);
+  swap32(d1, d3);
+  swap16(d0, d1);
+  swap16(d2, d3);
+  return (u32x4){d0, d1, d2, d3};
+}
+
+// Row u * SPG of v to every row, for each fold unit u.
+template <int SPG>
+__device__ __forceinline__ void bcast_units(float v, float (&out)[fold_units<SPG>()]) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  swap32(a, b);                              // a = [r0, r1, r0, r1], b = [r2, r3, r2, r3]
+  if constexpr (SPG == 2) {
+    out[0] = __builtin_bit_cast(float, a);
+    out[1] = __builtin_bit_cast(float, b);
+  } else {
+    uint32_t a2 = a, b2 = b;
+    swap16(a, a2);                           // a = r0 everywhere, a2 = r1
+    swap16(b, b2);                           // b = r2, b2 = r3
+    out[0] = __builtin_bit_cast(float, a);
+    out[1] = __builtin_bit_cast(float, a2);
+    out[2] = __builtin_bit_cast(float, b);
+    out[3] = __builtin_bit_cast(float, b2);
+  }
+}
+
+template <int ACT, int CTW, int SPG>
 __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch<CTW>& b, const uint8_t* xs,
-                                          DecodeAcc<CTW>& ma, f32x4 (&acc)[CTW]) {
+                                          DecodeAcc<CTW, fold_units<SPG>()>& ma, f32x4 (&acc)[CTW]) {
+  constexpr int U = fold_units<SPG>();
   const int lane = threadIdx.x & 63;
   const uint32_t one2 = pack2<ACT>(1.f, 1.f);
   const u32x4 ones = {one2, one2, one2, one2};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ma.rs[i] *= 0.f;
+  for (int u = 0; u < U; ++u) {
 #pragma unroll
-  for (int c = 0; c < CTW; ++c)
+    for (int i = 0; i < 4; ++i) ma.rs[u][i] *= 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ma.part[c][i] *= 0.f;
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ma.part[u][c][i] *= 0.f;
+  }
+  u32x4 w[CTW];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) w[c] = SPG == 4 ? b.w[c] : transpose_rows(b.w[c]);
 #pragma unroll
   for (int w4 = 0; w4 < 4; ++w4) {
+    const int u = w4 / SPG;
     const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
-    ma.rs = mfma16<ACT>(av, ones, ma.rs);
+    ma.rs[u] = mfma16<ACT>(av, ones, ma.rs[u]);
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) ma.part[c] = mfma16<ACT>(av, unpack8_low<ACT>(b.w[c][w4]), ma.part[c]);
+    for (int c = 0; c < CTW; ++c) ma.part[u][c] = mfma16<ACT>(av, unpack8_low<ACT>(w[c][w4]), ma.part[u][c]);
     // one K step's operands at a time (bounds the live unpacked fragments)
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -146,12 +230,23 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
     const float s = to_f32<ACT>((uint16_t)b.s[c]);
     const float o = to_f32<ACT>((uint16_t)b.o[c]) * a.omul;
     const float cc = o - UnpackLow<ACT>::bias * s;
+    if constexpr (SPG == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[c][i], fmaf(cc, ma.rs[i], acc[c][i]));
+      for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[0][c][i], fmaf(cc, ma.rs[0][i], acc[c][i]));
+    } else {
+      float su[U], cu[U];
+      bcast_units<SPG>(s, su);
+      bcast_units<SPG>(cc, cu);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[c][i] = fmaf(su[u], ma.part[u][c][i], fmaf(cu[u], ma.rs[u][i], acc[c][i]));
+    }
   }
 }
 
-template <int ACT, int CTW>
+template <int ACT, int CTW, int SPG>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_decode(DecodeArgs a) {
   constexpr int RS = CTW * 16 + 4;                  // reduction row stride (floats)
   // per wave: two 4 KiB x1 slots, reused after the K loop for the wave's
@@ -176,7 +271,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   ln.s = buf_rsrc(a.scale, a.s_bytes);
   ln.o = buf_rsrc(a.offset, a.s_bytes);
   const int64_t xrow = a.row0 + col;
-  ln.xoff = xrow < a.m ? (uint32_t)(xrow * a.k * 2 + kq * 64) : BUF_OOB;
+  ln.xoff = xrow < a.m ? (uint32_t)(xrow * a.k * 2 + kq * (SPG == 4 ? 64 : 16)) : BUF_OOB;
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
     const int64_t ct = ct0 + c < a.nct ? ct0 + c : a.nct - 1;
@@ -213,13 +308,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const int kb0 = wave * a.kpw;
   const int kb1 = kb0 + a.kpw < kbs ? kb0 + a.kpw : kbs;
   f32x4 acc[CTW];
-  DecodeAcc<CTW> ma;
-  ma.rs = (f32x4){0.f, 0.f, 0.f, 0.f};
+  DecodeAcc<CTW, fold_units<SPG>()> ma;
 #pragma unroll
-  for (int i = 0; i < CTW; ++i) {
-    acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    ma.part[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < fold_units<SPG>(); ++u) {
+    ma.rs[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < CTW; ++i) ma.part[u][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int i = 0; i < CTW; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // Batch b's loads complete in issue order, so once no more than the next
   // batch's loads are outstanding, b's weights, DMA and scales have landed
   // (the explicit wait also orders the LDS reads after the DMA, which the
@@ -228,22 +325,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   uint8_t* xa = xlds[wave][0];
   uint8_t* xb = xlds[wave][1];
   DecodeBatch<CTW> ba, bb;
-  if (kb0 < kb1) issue_batch<CTW>(a, ln, kb0, xa, ba);
+  if (kb0 < kb1) issue_batch<CTW, SPG>(a, ln, kb0, xa, ba);
   for (int kb = kb0; kb < kb1; kb += 2) {
-    if (kb + 1 < kb1) issue_batch<CTW>(a, ln, kb + 1, xb, bb);
+    if (kb + 1 < kb1) issue_batch<CTW, SPG>(a, ln, kb + 1, xb, bb);
     __builtin_amdgcn_sched_barrier(0);
     if (kb + 1 < kb1) wait_vm<batch_loads<CTW>()>();
     else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
-    mma_batch<ACT, CTW>(a, ba, xa, ma, acc);
+    mma_batch<ACT, CTW, SPG>(a, ba, xa, ma, acc);
     __builtin_amdgcn_sched_barrier(0);
     if (kb + 1 >= kb1) break;
-    if (kb + 2 < kb1) issue_batch<CTW>(a, ln, kb + 2, xa, ba);
+    if (kb + 2 < kb1) issue_batch<CTW, SPG>(a, ln, kb + 2, xa, ba);
     __builtin_amdgcn_sched_barrier(0);
     if (kb + 2 < kb1) wait_vm<batch_loads<CTW>()>();
     else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
-    mma_batch<ACT, CTW>(a, bb, xb, ma, acc);
+    mma_batch<ACT, CTW, SPG>(a, bb, xb, ma, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -292,34 +389,68 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 }
 
 template <int ACT>
-void launch_act(const DecodeArgs& a, int ctw, unsigned grid, hipStream_t s) {
+void launch_act(const DecodeArgs& a, int spg, int ctw, unsigned grid, hipStream_t s) {
   prof_begin(s);
-  switch (ctw) {
-    case 1: gemm_decode<ACT, 1><<<dim3(grid), 1024, 0, s>>>(a); break;
-    case 2: gemm_decode<ACT, 2><<<dim3(grid), 1024, 0, s>>>(a); break;
-    default: gemm_decode<ACT, 3><<<dim3(grid), 1024, 0, s>>>(a); break;
+  if (spg == 4) {
+    switch (ctw) {
+      case 1: gemm_decode<ACT, 1, 4><<<dim3(grid), 1024, 0, s>>>(a); break;
+      case 2: gemm_decode<ACT, 2, 4><<<dim3(grid), 1024, 0, s>>>(a); break;
+      default: gemm_decode<ACT, 3, 4><<<dim3(grid), 1024, 0, s>>>(a); break;
+    }
+  } else if (spg == 2) {
+    if (ctw == 1) gemm_decode<ACT, 1, 2><<<dim3(grid), 1024, 0, s>>>(a);
+    else gemm_decode<ACT, 2, 2><<<dim3(grid), 1024, 0, s>>>(a);
+  } else {
+    gemm_decode<ACT, 1, 1><<<dim3(grid), 1024, 0, s>>>(a);
   }
   prof_end(s);
 }
 
+// 32-deep K steps per fold: a group (>= 32, a multiple of 32) that is not a
+// multiple of 128 folds every 64 (an even multiple of 32) or every 32 K.
+int decode_spg(const WqProblem& p) {
+  if (p.group >= p.k || p.group % 128 == 0) return 4;
+  return p.group % 64 == 0 ? 2 : 1;
+}
+
 // column tiles per workgroup: keep the grid within one workgroup per CU up to
-// 768 tiles (n = 12288); wider layers take more workgroups of 3
-int decode_ctw(int64_t nct) { return nct <= 256 ? 1 : nct <= 512 ? 2 : 3; }
+// 768 tiles (n = 12288); wider layers take more workgroups of 3. The per-unit
+// accumulators of short groups cap the tiles at 2 (SPG = 2) or 1 (SPG = 1)
+// within the register budget of 16 waves per CU.
+int decode_ctw(int64_t nct, int spg) {
+  const int ctw = nct <= 256 ? 1 : nct <= 512 ? 2 : 3;
+  const int cap = spg == 4 ? 3 : spg == 2 ? 2 : 1;
+  return ctw < cap ? ctw : cap;
+}
 
 }  // namespace
 
-// The weight stream addresses the packed weight through one buffer resource
-// whose out-of-range offset is 2^31: the weight must stay below 2 GiB.
+// INT4 in the GFX950_B layout, k a multiple of 128, m <= 32. The weight
+// stream addresses the packed weight through one buffer resource whose
+// out-of-range offset is 2^31: the weight must stay below 2 GiB.
 bool decode_ok(const WqProblem& p) {
-  return p.m <= 32 && (p.k / 128) * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
+  if (p.w_bits != 4 || p.layout != WQ_LAYOUT_GFX950_B || p.k % 128 != 0 || p.m > 32) return false;
+  if (p.group < p.k && p.group % 32 != 0) return false;
+  return (p.k / 128) * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
 }
 
 // Per-(row, workgroup) sums of y^2 of the decode kernel: [32][grid] at most.
-int64_t decode_grid(int64_t n) {
-  const int64_t nct = (n + 15) / 16;
-  return (nct + decode_ctw(nct) - 1) / decode_ctw(nct);
+int64_t decode_grid(const WqProblem& p) {
+  const int64_t nct = (p.n + 15) / 16;
+  const int ctw = decode_ctw(nct, decode_spg(p));
+  return (nct + ctw - 1) / ctw;
 }
-size_t decode_partial_bytes(int64_t n) { return (size_t)(decode_grid(n) * 32 * 4); }
+size_t decode_partial_bytes(int64_t n) {
+  // the largest grid over the fold shapes
+  const int64_t nct = (n + 15) / 16;
+  int64_t grid = 0;
+  for (int spg = 1; spg <= 4; spg *= 2) {
+    const int ctw = decode_ctw(nct, spg);
+    const int64_t g = (nct + ctw - 1) / ctw;
+    grid = g > grid ? g : grid;
+  }
+  return (size_t)(grid * 32 * 4);
+}
 
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   DecodeArgs a;
@@ -339,7 +470,9 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   a.nct = a.np / 16;
   const int64_t group = p.group >= p.k ? p.k : p.group;
   const int64_t groups = (p.k + group - 1) / group;
+  const int spg = decode_spg(p);
   a.bpg = (int32_t)(group / 128);
+  a.upg_rcp = 1.f / (float)(group / (32 * spg));
   a.s_row = p.s_row;
   a.s_col = p.s_col;
   a.x1_bytes = (uint32_t)(p.m * p.k * 2);
@@ -348,13 +481,13 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   a.res_bytes = (uint32_t)(p.m * p.n * 2);
   const int64_t kbs = p.k / 128;
   a.kpw = (int32_t)((kbs + DC_WAVES - 1) / DC_WAVES);
-  const int ctw = decode_ctw(a.nct);
-  const unsigned grid = (unsigned)decode_grid(p.n);
+  const int ctw = decode_ctw(a.nct, spg);
+  const unsigned grid = (unsigned)decode_grid(p);
   // one launch per 16 rows (m <= 32: at most two; the second finds the
   // weights in the last-level cache)
   for (a.row0 = 0; a.row0 < p.m; a.row0 += 16) {
-    if (p.bf16) launch_act<ACT_BF16>(a, ctw, grid, s);
-    else launch_act<ACT_F16>(a, ctw, grid, s);
+    if (p.bf16) launch_act<ACT_BF16>(a, spg, ctw, grid, s);
+    else launch_act<ACT_F16>(a, spg, ctw, grid, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -68,11 +68,12 @@ size_t fast_corr_bytes(int64_t n, int64_t k);
 hipError_t launch_prefill(const WqProblem& p, float* partial, uint16_t* rs, uint16_t* corr,
                           hipStream_t s);
 
-// Weight-streaming kernel for m <= 32 on the same fast-path problems; writes
-// one sum of y^2 per (row, workgroup) at partial[row * decode_grid(n) +
-// workgroup].
+// Weight-streaming kernel for m <= 32 (INT4, GFX950_B, k a multiple of 128,
+// any group); writes one sum of y^2 per (row, workgroup) at
+// partial[row * decode_grid(p) + workgroup]; decode_partial_bytes(n) bounds
+// that array over every group size.
 bool decode_ok(const WqProblem& p);
-int64_t decode_grid(int64_t n);
+int64_t decode_grid(const WqProblem& p);
 size_t decode_partial_bytes(int64_t n);
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s);
 

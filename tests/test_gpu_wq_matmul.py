@@ -149,10 +149,14 @@ def test_integer_valued_y_is_bit_exact(act, k, G):
     assert oracle.rel_err_floor(nrm, on) <= 1e-2
 
 
-def test_one_hot_rows_pin_group_indexing():
-    k, n, G = 256, 32, 32
-    m = 8
-    rows = [0, 31, 32, 100, 128, 200, 224, 255]
+@pytest.mark.parametrize("G", [32, 64, 96, 128])
+def test_one_hot_rows_pin_group_indexing(G):
+    # x1 rows one-hot at K values on both sides of group and 32-step
+    # boundaries: y row i is weight row rows[i] dequantized with its own
+    # group's scale and offset (the m <= 32 weight stream, every fold shape)
+    k, n = 384, 32
+    rows = [0, 31, 32, 63, 64, 95, 96, 127, 128, 191, 192, 255, 256, 287, 320, 383]
+    m = len(rows)
     x1 = torch.zeros((m, k), dtype=torch.bfloat16)
     for i, r in enumerate(rows):
         x1[i, r] = 1.0
@@ -160,7 +164,7 @@ def test_one_hot_rows_pin_group_indexing():
                           group_size=G, offset_range=(-1, 1), bias_std=None, seed=5)
     c.x1 = x1
     c.residual = torch.zeros_like(c.residual)
-    note("wq one-hot rows")
+    note(f"wq one-hot rows g={G}")
     y, nrm = wq_on_gpu(c)
     _, oy, _ = oracle.wq_matmul_add_rmsnorm(as_f64(x1), c.w.numpy(), as_f64(c.scale),
                                             as_f64(c.offset), G, None, np.zeros((m, n)),
@@ -206,6 +210,19 @@ DECODE = [  # m, k, n, granularity, group, offset, bias, act: the m <= 32 weight
     (31, 640, 13000, "group", 128, "none", 0.1, torch.bfloat16),
     (32, 8192, 1000, "channel2d", 0, (-0.5, 0.5), 0.1, torch.float16),
     (5, 1152, 2000, "group", 384, (-1.0, 1.0), None, torch.float16),
+    # groups shorter than 128 or not dividing it: folds every 32 (odd
+    # multiples of 32) or every 64 (odd multiples of 64) K values, a last
+    # partial group where G does not divide k
+    (3, 512, 300, "group", 32, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (16, 1024, 520, "group", 64, (-0.5, 0.5), None, torch.float16),
+    (21, 768, 1000, "group", 96, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (8, 1152, 700, "group", 192, None, 0.1, torch.float16),
+    (4, 1280, 333, "group", 160, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (6, 640, 90, "group", 192, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (2, 512, 48, "group", 224, (-0.5, 0.5), 0.1, torch.float16),
+    (5, 4096, 4100, "group", 32, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (32, 2048, 6000, "group", 64, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (19, 4096, 11008, "group", 32, (-1.0, 1.0), None, torch.float16),
 ]
 
 
@@ -265,15 +282,17 @@ def test_fast_zero_scale_in_a_later_group_tile():
     check_wq(c, y, nrm)
 
 
-def test_decode_zero_scale_columns():
+@pytest.mark.parametrize("G", [128, 64, 32])
+def test_decode_zero_scale_columns(G):
     # a zero group scale leaves only the offset: w = o for that group
-    m, k, n, G = 4, 512, 64, 128
+    m, k, n = 4, 512, 64
     c = workloads.wq_case("dec_zero_scale", m, k, n, act=torch.bfloat16, w_bits=4,
                           granularity="group", group_size=G, scale_range=(0.002, 0.02),
                           offset_range=(-1.0, 1.0), bias_std=0.1, seed=11)
     c.scale[1, :] = 0
     c.scale[:, 5] = 0
-    note("wq decode zero-scale groups and columns")
+    c.scale[c.scale.shape[0] - 1, 17] = 0
+    note(f"wq decode zero-scale groups and columns g={G}")
     y, nrm = wq_on_gpu(c)
     check_wq(c, y, nrm)
 
