@@ -10,8 +10,8 @@
 //   2. rmsnorm_finish: sums a row's partials in a fixed order, forms
 //      1/RMS and writes normOut = y * rstd * gamma.
 // GEMM kernels:
-//   - gemm_decode (wq_gemm_decode.hip): m <= 32, INT4 GFX950_B, group a
-//     multiple of 128 (or per channel / tensor): a weight stream;
+//   - gemm_decode (wq_gemm_decode.hip): m <= 32, INT4 GFX950_B, k a
+//     multiple of 128, any group: a weight stream;
 //   - gemm_b_wide (wq_gemm_fast.hip): the same weights at larger m, the
 //     MFMA-bound tile;
 //   - gemm_generic: any weight layout (INT4 ND / ND transposed / GFX950_B,
