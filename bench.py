@@ -100,6 +100,18 @@ def measured_traffic():
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +163,10 @@ def main():
     mxc = workloads.mx(draw_w=False)
     MM, MK, MN = mxc.mkn
     xq_in, smooth = mxc.x.to(dev), mxc.smooth.to(dev)
+    # the MX quant row reads its own copy of x: it runs right after the
+    # per-token row, which would otherwise leave x in the 256 MB last-level
+    # cache
+    xq_in_mx = xq_in.clone()
     q8 = torch.empty((MM, MK), dtype=torch.int8, device=dev)
     q8s = torch.empty(MM, dtype=torch.float32, device=dev)
     x1q = torch.empty((MK, MM), dtype=torch.uint8, device=dev)
@@ -195,7 +211,7 @@ def main():
         wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_INT8, 0, 0, q8, q8s)
 
     def op_quant_mx():
-        wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_FP8_E4M3, 32, 1, x1q, s1)
+        wq.wq_dynamic_quant(xq_in_mx, wq.WQ_F16, MM, MK, smooth, wq.WQ_FP8_E4M3, 32, 1, x1q, s1)
 
     def op_mx():
         wq.mx_quant_matmul_inplace_add(x1q, x2mx, wq.WQ_LAYOUT_GFX950_B, s1, s2, MM, MK, MN, 1, 0,
@@ -434,6 +450,92 @@ def main():
                                         "kernel_GB/s": round(kbytes / kmed / 1e6, 1),
                                         "kernel_bytes": kbytes})
 
+    # ---------------- the small configurations (latency-bound) ----------------
+    # tiny W4A16 group 32 (m 16) and W8A16 per channel (m 512): per call with
+    # the inputs resident, eagerly and as a captured HIP graph of 50 calls
+    # (no host launch gap), plus the GEMM kernel alone (the library's event
+    # pair around its launch)
+    small = {}
+    if want("configs"):
+        for key, case, layout in (("tiny_w4a16_g32", workloads.tiny(), wq.WQ_LAYOUT_GFX950_B),
+                                  ("w8a16_per_channel", workloads.w8(), wq.WQ_LAYOUT_ND)):
+            cm, ck, cn = case.mkn
+            cx = case.x1.to(dev).reshape(cm, ck)
+            if case.w_bits == 4:
+                cw = wq.pack_int4(case.w.to(dev), layout)
+                wdt = wq.WQ_INT4
+            else:
+                cw = case.w.to(torch.int8).to(dev)
+                wdt = wq.WQ_INT8
+            cs = case.scale.to(dev)
+            sr, sc = (cs.shape[0], cs.shape[1]) if cs.dim() == 2 else (1, cs.numel())
+            co = None if case.offset is None else case.offset.to(dev)
+            cb = None if case.bias is None else case.bias.to(dev)
+            cr = case.residual.to(dev).reshape(cm, cn)
+            cg = case.gamma.to(dev)
+            cy, cnrm = torch.empty_like(cr), torch.empty_like(cr)
+            cwn = wq.wq_matmul_add_rmsnorm_workspace_size(cm, ck, cn)
+            cws = torch.zeros(cwn, dtype=torch.uint8, device=dev)
+            act = wq.act_code(cx.dtype)
+            call = lambda: wq.wq_matmul_add_rmsnorm(cx, cm, ck, act, cw, cn, wdt, layout, 0, cs, sr, sc,
+                                                    co, case.group_size, cb, cr, cg, case.eps, cy, cnrm,
+                                                    cws, cwn)
+            for _ in range(20):
+                call()
+            evs = []
+            for _ in range(200):
+                a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                call()
+                b0.record(stream)
+                evs.append((a0, b0))
+            torch.cuda.synchronize()
+            eager = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+            wq.wq_profile_enable(True)
+            for _ in range(200):
+                call()
+            torch.cuda.synchronize()
+            kt = wq.wq_profile_read()
+            wq.wq_profile_enable(False)
+            reps = 50
+            gs = torch.cuda.Stream()
+            gs.wait_stream(stream)
+            with torch.cuda.stream(gs):
+                for _ in range(reps):
+                    call()
+            stream.wait_stream(gs)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    call()
+            graph.replay()
+            torch.cuda.synchronize()
+            gts = []
+            for _ in range(10):
+                a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                graph.replay()
+                b0.record(stream)
+                gts.append((a0, b0))
+            torch.cuda.synchronize()
+            gper = statistics.median(a0.elapsed_time(b0) for a0, b0 in gts) / reps
+            del graph
+            flop = 2 * cm * cn * ck
+            nbytes = (cx.numel() * 2 + cw.numel() * cw.element_size() + 2 * cs.numel() * 2
+                      + 3 * cm * cn * 2 + 2 * cn * 2)
+            d = {"m": cm, "k": ck, "n": cn, "w_bits": case.w_bits, "group_size": case.group_size,
+                 "act": str(cx.dtype).replace("torch.", ""), "us": round(eager * 1e3, 3),
+                 "graph_us": round(gper * 1e3, 3), "TFLOP/s": round(flop / gper / 1e9, 2),
+                 "GB/s": round(nbytes / gper / 1e6, 1), "flop": flop, "bytes": nbytes,
+                 "frac_of_mfma_peak": round(flop / gper / 1e9 / PEAK_BF16_TFLOPS, 4),
+                 "frac_of_hbm_peak": round(nbytes / gper / 1e6 / PEAK_HBM_GBS, 4)}
+            if kt:
+                km = statistics.median(kt)
+                d.update({"kernel_us": round(km * 1e3, 3), "kernel_TFLOP/s": round(flop / km / 1e9, 2)})
+            small[key] = d
+            del cx, cw, cr, cy, cnrm, cws
+
     # ---------------- achievable ceilings on this GPU (context, not targets) -------------
     ceilings = None
     if not args.no_ceilings and not only:
@@ -538,7 +640,7 @@ def main():
                "cores": cores, "kind": "oracle",
                "sample": f"prefill W4A16 g128 + AddRmsNorm, first {sample_rows} of {M} rows "
                          f"(k {K}, n {N}), float64 numpy, {reps} call(s), "
-                         f"{per_call:.2f} s per call", "cpu": platform.processor() or platform.machine()}
+                         f"{per_call:.2f} s per call", "cpu": cpu_model()}
 
     head = out_rows.get("wq_matmul_add_rmsnorm")
     value = head["TFLOP/s"] if head else None
@@ -563,6 +665,7 @@ def main():
         "rows": out_rows,
         "extras": out_extras,
         "decode": decode,
+        "configs": small,
         "cpu_baseline": cpu,
         "ceilings": ceilings,
     }

@@ -14,6 +14,8 @@
 //     multiple of 128, any group: a weight stream;
 //   - gemm_b_wide (wq_gemm_fast.hip): the same weights at larger m, the
 //     MFMA-bound tile;
+//   - gemm_w8 (wq_gemm_w8.hip): INT8 weights, row-major or transposed, k a
+//     multiple of 16: a 64 x 64 tile with loads two K steps ahead;
 //   - gemm_generic: any weight layout (INT4 ND / ND transposed / GFX950_B,
 //     INT8 ND / transposed), any group size, 64x64x32 tiles with both operands staged
 //     in LDS; integer codes go to the MFMA and each group's scale and
@@ -364,6 +366,8 @@ hipError_t wq_rows(const WqProblem& p, hipStream_t s) {
     uint16_t* corr = reinterpret_cast<uint16_t*>(ws + partial_bytes(p.m, p.n) +
                                                  fast_rowsum_bytes(p.m, p.k));
     e = launch_prefill(p, a.partial, rs, corr, s);
+  } else if (w8_ok(p)) {
+    e = launch_w8(p, a.partial, s);
   } else {
     e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
   }

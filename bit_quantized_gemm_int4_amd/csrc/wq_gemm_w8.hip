@@ -1,0 +1,464 @@
+// INT8-weight tile of the weight-quantized matmul + AddRmsNorm
+// (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula; x2 int8 (k, n)
+// or its transpose (n, k), Constraints section). Same operator and numerics
+// as wq_gemm.hip: the codes enter the MFMA as exact 16-bit values q, each
+// group's scale and offset are applied to its float32 partial sums, the
+// epilogue writes y = acc + bias + residual and per-(row, 32-column tile)
+// sums of y^2 for the rmsnorm_finish launch.
+//
+// Tile: 64 x 64 outputs per workgroup, K in steps of 64 (two 32-deep MFMA
+// steps). The workgroup's 16 waves form four K slices of four waves (each
+// wave 32 x 32 outputs, 2 x 2 MFMA tiles of 16 x 16); slice q multiplies a
+// contiguous quarter of the steps and the slices' sums are added in LDS in
+// slice order at the end. One wave per SIMD would leave every latency
+// (LDS round trips, conversions, MFMA dependencies, barriers) exposed at
+// small m; four slices keep four waves on each SIMD. Both operands are
+// staged through LDS in 16-bit form, so every code is converted once per
+// slice:
+//   - x1: 16 halves per thread and step (two 16-byte loads), copied;
+//   - x2 transposed (n, k): 16 consecutive K bytes of one column per
+//     thread (one 16-byte load);
+//   - x2 row-major (k, n): four K rows x four columns per thread (four
+//     4-byte loads), transposed in registers with byte permutes.
+// Loads run two K steps ahead of the MFMAs (two register stages, LDS double
+// buffer, one barrier per step): at small m the tile is latency-bound, and
+// two steps in flight halve the exposed load latency.
+//
+// Conversion to exact 16-bit values:
+//   fp16: u = q + 128 (sign bit flipped) placed under the exponent byte 0x64
+//         gives 1024 + u = q + 1152 exactly (ulp 1 on [1024, 2048)); one
+//         packed half subtraction of 1152 leaves q;
+//   bf16: each signed byte to float32 (byte-select conversions), two per
+//         packed bf16 conversion (|q| <= 128 has at most 8 significant
+//         bits: exact).
+#include "wq_device.h"
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+constexpr int W8_BM = 64, W8_BN = 64, W8_BK = 64, W8_KS = 4;
+constexpr int W8_LDS = W8_BK + 8;   // halves per LDS row: 144 bytes, conflict-free 16-byte reads
+
+struct W8Args {
+  const uint16_t* x1;
+  const uint8_t* x2;
+  const uint16_t* scale;
+  const uint16_t* offset;   // may be null
+  const uint16_t* bias;     // may be null
+  const uint16_t* residual;  // may be null (the standalone matmul)
+  uint16_t* y;
+  float* partial;           // [m][ceil(n / 32)]
+  int64_t m, k, n, s_row, s_col;
+  int upg;                  // 32-deep units per group; INT32_MAX: one group over all of K
+  uint32_t s_bytes;
+};
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two 16-bit values in one dword: fp16 (1024 + u) for the bytes u of the
+// two selected positions, minus 1152 -> q.
+__device__ __forceinline__ uint32_t f16_pair(uint32_t u, uint32_t sel) {
+  const uint32_t biased = __builtin_amdgcn_perm(0x64646464u, u, sel);
+  const f16x2 v = __builtin_bit_cast(f16x2, biased) - (f16x2){(_Float16)1152.f, (_Float16)1152.f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// signed byte j of w -> float q
+__device__ __forceinline__ float sbyte(uint32_t w, int j) { return (float)(int)(int8_t)(w >> (8 * j)); }
+
+// two floats -> one dword of two bf16 (one packed conversion; the values
+// here are exact in bf16)
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// 16 consecutive K codes of one column (four dwords, K ascending from the
+// low byte) -> eight dwords of 16-bit q, K ascending.
+template <int ACT>
+__device__ __forceinline__ void convert_k16(const u32x4& w, u32x4& lo, u32x4& hi) {
+  uint32_t o[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (ACT == ACT_F16) {
+      const uint32_t u = w[d] ^ 0x80808080u;
+      o[2 * d] = f16_pair(u, 0x04010400u);      // bytes 0, 1
+      o[2 * d + 1] = f16_pair(u, 0x04030402u);  // bytes 2, 3
+    } else {
+      o[2 * d] = bf16_pair(sbyte(w[d], 0), sbyte(w[d], 1));
+      o[2 * d + 1] = bf16_pair(sbyte(w[d], 2), sbyte(w[d], 3));
+    }
+  }
+  lo = (u32x4){o[0], o[1], o[2], o[3]};
+  hi = (u32x4){o[4], o[5], o[6], o[7]};
+}
+
+// Four K rows of four columns (r[i] = row i, byte j = column j) -> per
+// column j the four K values as 16-bit q: out[j] = {rows 0-1, rows 2-3}.
+template <int ACT>
+__device__ __forceinline__ void convert_rows4(const uint32_t (&r)[4], u32x2 (&out)[4]) {
+  if constexpr (ACT == ACT_F16) {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = r[i] ^ 0x80808080u;
+    // pair rows (0, 1) and (2, 3) byte by byte: p01l = [u0.b0, u1.b0, u0.b1,
+    // u1.b1], p01h = the same for bytes 2, 3
+    const uint32_t p01l = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
+    const uint32_t p01h = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
+    const uint32_t p23l = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+    const uint32_t p23h = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+    out[0] = (u32x2){f16_pair(p01l, 0x04010400u), f16_pair(p23l, 0x04010400u)};
+    out[1] = (u32x2){f16_pair(p01l, 0x04030402u), f16_pair(p23l, 0x04030402u)};
+    out[2] = (u32x2){f16_pair(p01h, 0x04010400u), f16_pair(p23h, 0x04010400u)};
+    out[3] = (u32x2){f16_pair(p01h, 0x04030402u), f16_pair(p23h, 0x04030402u)};
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      out[j] = (u32x2){bf16_pair(sbyte(r[0], j), sbyte(r[1], j)), bf16_pair(sbyte(r[2], j), sbyte(r[3], j))};
+  }
+}
+
+// One K step's register stage: raw x1 halves, raw weight bytes, and (threads
+// t < 128) the scale / offset of column t % 64 for the group that 32-deep
+// half t / 64 closes. The scales go to LDS with the tiles, so that no value
+// loaded for a later step is held across the loop's back edge in registers
+// the compiler would have to copy (and wait for).
+struct W8Stage {
+  u32x4 a0, a1;
+  u32x4 b;                  // transposed: 16 K bytes of one column; row-major: 4 rows x 4 columns
+  uint32_t sv, ov;
+};
+
+struct W8Lane {
+  __amdgpu_buffer_rsrc_t x, w, s, o;
+  int rows, cols;           // valid rows / columns of the workgroup's tile
+};
+
+// Place of a 32-deep unit of K in its group: the unit's index within the
+// group and the group. Units are visited in order, so moving to the next is
+// a compare and an add on scalars (no division in the loop).
+struct FoldPos {
+  int pos, g;
+  __device__ __forceinline__ FoldPos next(int upg) const {
+    return pos + 1 == upg ? FoldPos{0, g + 1} : FoldPos{pos + 1, g};
+  }
+};
+
+// A 32-deep half at unit position f starting at K value kh closes a group
+// when it holds K values of the slice (which ends at kend) and it is its
+// group's last unit or the slice's last (a group split between slices is
+// folded by each with the same scale and offset).
+__device__ __forceinline__ bool closes_group(const W8Args& a, int kend, int kh, FoldPos f) {
+  return (kh < kend) & ((f.pos == a.upg - 1) | (kh + 32 >= kend));
+}
+
+// The loads of one step of one slice: K values [k0, k0 + 64) below kend.
+template <bool ND>
+__device__ __forceinline__ void load_stage(const W8Args& a, const W8Lane& ln, int64_t n0, int kend, int k0,
+                                           FoldPos& fp, W8Stage& st) {
+  const int t = threadIdx.x & 255, lane = t & 63;
+  {
+    const int r = t >> 2, kc = (t & 3) * 16;
+    const uint32_t v = (r < ln.rows) & (k0 + kc < kend) ? (uint32_t)((r * (int)a.k + k0 + kc) * 2) : BUF_OOB;
+    st.a0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.x, v, 0, 0));
+    st.a1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.x, v + 16u, 0, 0));
+  }
+  if constexpr (!ND) {
+    const int c = t >> 2, kc = (t & 3) * 16;
+    const uint32_t v = (c < ln.cols) & (k0 + kc < kend) ? (uint32_t)(c * (int)a.k + k0 + kc) : BUF_OOB;
+    st.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, v, 0, 0));
+  } else {
+    const int rg = t >> 4, c4 = (t & 15) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t kk = k0 + 4 * rg + i;
+      const uint32_t v = (c4 < ln.cols) & (kk < kend) ? (uint32_t)(kk * a.n + c4) : BUF_OOB;
+      st.b[i] = __builtin_amdgcn_raw_buffer_load_b32(ln.w, v, 0, 0);
+    }
+  }
+  // the scale and offset of a half that closes a group (else, or for
+  // t >= 128, an out-of-range offset: the load reads nothing). Every load of
+  // a stage is issued on every path, so the compiler's wait before a stage's
+  // first use counts only the loads issued after it.
+  {
+    const FoldPos f0 = fp, f1 = fp.next(a.upg);
+    fp = f1.next(a.upg);
+    const bool fold0 = closes_group(a, kend, k0, f0), fold1 = closes_group(a, kend, k0 + 32, f1);
+    const bool h = (t >> 6) & 1;
+    const bool fold = (h ? fold1 : fold0) & (t < 128);
+    const int64_t g = h ? f1.g : f0.g;              // < groups when fold
+    int64_t col = n0 + lane;
+    col = col < a.n ? col : a.n - 1;
+    const uint32_t so = fold ? (uint32_t)((g * a.s_row + col * a.s_col) * 2) : BUF_OOB;
+    st.sv = __builtin_amdgcn_raw_buffer_load_b16(ln.s, so, 0, 0);
+    st.ov = __builtin_amdgcn_raw_buffer_load_b16(ln.o, so, 0, 0);
+  }
+}
+
+// Scales and offsets of one buffer: [half][column] raw 16-bit values.
+struct W8Scales {
+  uint16_t s[2][W8_BN], o[2][W8_BN];
+};
+
+template <int ACT, bool ND>
+__device__ __forceinline__ void store_stage(const W8Stage& st, uint16_t* As, uint16_t* Bs, W8Scales& ss) {
+  const int t = threadIdx.x & 255;
+  if (t < 128) {
+    ss.s[t >> 6][t & 63] = (uint16_t)st.sv;
+    ss.o[t >> 6][t & 63] = (uint16_t)st.ov;
+  }
+  {
+    const int r = t >> 2, kc = (t & 3) * 16;
+    *reinterpret_cast<u32x4*>(As + r * W8_LDS + kc) = st.a0;
+    *reinterpret_cast<u32x4*>(As + r * W8_LDS + kc + 8) = st.a1;
+  }
+  if constexpr (!ND) {
+    const int c = t >> 2, kc = (t & 3) * 16;
+    u32x4 lo, hi;
+    convert_k16<ACT>(st.b, lo, hi);
+    *reinterpret_cast<u32x4*>(Bs + c * W8_LDS + kc) = lo;
+    *reinterpret_cast<u32x4*>(Bs + c * W8_LDS + kc + 8) = hi;
+  } else {
+    const int rg = t >> 4, c4 = (t & 15) * 4;
+    const uint32_t r[4] = {st.b[0], st.b[1], st.b[2], st.b[3]};
+    u32x2 out[4];
+    convert_rows4<ACT>(r, out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Bs + (c4 + j) * W8_LDS + 4 * rg) = out[j];
+  }
+}
+
+struct W8Acc {
+  f32x4 acc[2][2], part[2][2], rs[2];
+};
+
+// The two 32-deep halves of one K step from LDS (past the end of K they
+// hold zeros); a half that closes a group folds it:
+// acc += s * sum x q + o * sum x.
+template <int ACT>
+__device__ __forceinline__ void compute_stage(const W8Args& a, const uint16_t* As, const uint16_t* Bs,
+                                              const W8Scales& ss, int kend, int k0, FoldPos& fp, W8Acc& z) {
+  const int t = threadIdx.x & 255, lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const uint32_t one2 = pack2<ACT>(1.f, 1.f);
+  const u32x4 ones = {one2, one2, one2, one2};
+  const bool off = a.offset != nullptr;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kq = 32 * h + 8 * (lane >> 4);
+    u32x4 af[2], bf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      af[i] = *reinterpret_cast<const u32x4*>(As + (wr * 32 + 16 * i + (lane & 15)) * W8_LDS + kq);
+      bf[i] = *reinterpret_cast<const u32x4*>(Bs + (wc * 32 + 16 * i + (lane & 15)) * W8_LDS + kq);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) z.part[i][j] = mfma16<ACT>(af[i], bf[j], z.part[i][j]);
+      if (off) z.rs[i] = mfma16<ACT>(af[i], ones, z.rs[i]);
+    }
+    const bool fold = closes_group(a, kend, k0 + 32 * h, fp);
+    fp = fp.next(a.upg);
+    if (__builtin_expect(fold, 0)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = wc * 32 + 16 * j + (lane & 15);
+        const float s = to_f32<ACT>(ss.s[h][c]);
+        const float o = off ? to_f32<ACT>(ss.o[h][c]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            z.acc[i][j][e] = fmaf(s, z.part[i][j][e], z.acc[i][j][e]);
+            if (off) z.acc[i][j][e] = fmaf(o, z.rs[i][e], z.acc[i][j][e]);
+            z.part[i][j][e] = 0.f;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) z.rs[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+template <int ACT, bool ND>
+__global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
+  // per slice: x1 and weight tiles, double-buffered, and the fold scales;
+  // after the K loop the tiles hold the slices' sums
+  __shared__ __attribute__((aligned(16))) uint16_t As[W8_KS][2][W8_BM * W8_LDS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[W8_KS][2][W8_BN * W8_LDS];
+  __shared__ W8Scales Ss[W8_KS][2];
+  const int q = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));   // K slice
+  const int t = threadIdx.x & 255, lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * W8_BM;
+  const int64_t n0 = (int64_t)blockIdx.x * W8_BN;
+
+  // Buffer resources start at the workgroup's rows / columns, so every
+  // offset stays below 2^31 (x1: 64 rows; the transposed weight: 64
+  // columns; the row-major weight is below 2 GiB as a whole).
+  W8Lane ln;
+  ln.rows = (int)(a.m - m0 < W8_BM ? a.m - m0 : W8_BM);
+  ln.cols = (int)(a.n - n0 < W8_BN ? a.n - n0 : W8_BN);
+  ln.x = buf_rsrc(a.x1 + m0 * a.k, (uint32_t)(ln.rows * a.k * 2));
+  if constexpr (ND) ln.w = buf_rsrc(a.x2 + n0, (uint32_t)((a.k - 1) * a.n + ln.cols));
+  else ln.w = buf_rsrc(a.x2 + n0 * a.k, (uint32_t)(ln.cols * a.k));
+  ln.s = buf_rsrc(a.scale, a.s_bytes);
+  ln.o = buf_rsrc(a.offset ? a.offset : a.scale, a.s_bytes);
+
+  W8Acc z;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    z.rs[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      z.acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      z.part[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Slice q: steps [q * sps, (q + 1) * sps), K values below kend. Steps s + 1
+  // and s + 2 in flight while step s is multiplied: stage sa holds even
+  // steps, sb odd ones; LDS buffer s % 2 holds step s. Every slice runs the
+  // same even number of steps with every load unconditional (a step past its
+  // slice reads zeros through out-of-range offsets and multiplies nothing),
+  // so the barriers match and the waits see one straight sequence of loads.
+  const int steps = (int)((a.k + W8_BK - 1) / W8_BK);
+  const int sps = (steps + W8_KS - 1) / W8_KS;
+  const int kb = q * sps * W8_BK;
+  const int kend = (q + 1) * sps * W8_BK < (int)a.k ? (q + 1) * sps * W8_BK : (int)a.k;
+  uint16_t* A0 = As[q][0];
+  uint16_t* A1 = As[q][1];
+  uint16_t* B0 = Bs[q][0];
+  uint16_t* B1 = Bs[q][1];
+  // unit positions of the loads (two steps ahead) and of the MFMAs
+  const int u0 = kb >> 5;
+  FoldPos fl = {u0 % a.upg, u0 / a.upg};
+  FoldPos fc = fl;
+  W8Stage sa, sb;
+  load_stage<ND>(a, ln, n0, kend, kb, fl, sa);
+  load_stage<ND>(a, ln, n0, kend, kb + W8_BK, fl, sb);
+  store_stage<ACT, ND>(sa, A0, B0, Ss[q][0]);
+  __syncthreads();
+  for (int s = 0; s < sps; s += 2) {
+    const int k0 = kb + s * W8_BK;
+    load_stage<ND>(a, ln, n0, kend, k0 + 2 * W8_BK, fl, sa);
+    compute_stage<ACT>(a, A0, B0, Ss[q][0], kend, k0, fc, z);
+    store_stage<ACT, ND>(sb, A1, B1, Ss[q][1]);
+    __syncthreads();
+    load_stage<ND>(a, ln, n0, kend, k0 + 3 * W8_BK, fl, sb);
+    compute_stage<ACT>(a, A1, B1, Ss[q][1], kend, k0 + W8_BK, fc, z);
+    store_stage<ACT, ND>(sa, A0, B0, Ss[q][0]);
+    __syncthreads();
+  }
+
+  // ---- the slices' sums: each slice's 64 x 64 tile to its LDS (rows of 68
+  // floats: the 16 columns of a row and the four rows one MFMA lane group
+  // apart land in distinct banks), then every thread adds four adjacent
+  // outputs over the slices in slice order ----
+  // (every slice's LDS reads are complete: the loop ended with a barrier)
+  constexpr int CS = W8_BN + 4;
+  static_assert(W8_BM * CS * 4 <= 2 * W8_BM * W8_LDS * 2, "a slice's sums fit its tiles");
+  {
+    float* cq = reinterpret_cast<float*>(As[q][0]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cq[(wr * 32 + 16 * i + 4 * (lane >> 4) + e) * CS + wc * 32 + 16 * j + (lane & 15)] = z.acc[i][j][e];
+  }
+  __syncthreads();
+
+  // ---- epilogue: thread T takes row T / 16, columns 4 (T % 16) .. + 3:
+  // y = sum + bias + residual, and the sum of y^2 over each 32-column tile
+  // (eight threads) ----
+  const int T = threadIdx.x, er = T >> 4, ec = (T & 15) * 4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(As[0][0]) + er * CS + ec);
+#pragma unroll
+  for (int p = 1; p < W8_KS; ++p) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(As[p][0]) + er * CS + ec);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += w[e];
+  }
+  const int64_t row = m0 + er, col = n0 + ec;
+  float ss = 0.f;
+  if (row < a.m) {
+    const int64_t idx = row * a.n + col;
+    if ((a.n & 3) == 0 && col + 3 < a.n) {
+      // 8-byte accesses: rows start 8-byte aligned when n % 4 == 0
+      const u32x2 bb = a.bias ? *reinterpret_cast<const u32x2*>(a.bias + col) : (u32x2){0u, 0u};
+      const u32x2 rr = a.residual ? *reinterpret_cast<const u32x2*>(a.residual + idx) : (u32x2){0u, 0u};
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        y[2 * e] = v[2 * e] + lo_f32<ACT>(bb[e]) + lo_f32<ACT>(rr[e]);
+        y[2 * e + 1] = v[2 * e + 1] + hi_f32<ACT>(bb[e]) + hi_f32<ACT>(rr[e]);
+      }
+      *reinterpret_cast<u32x2*>(a.y + idx) = (u32x2){pack2<ACT>(y[0], y[1]), pack2<ACT>(y[2], y[3])};
+      ss = (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < a.n) {
+          const float y = v[e] + (a.bias ? to_f32<ACT>(a.bias[col + e]) : 0.f) +
+                          (a.residual ? to_f32<ACT>(a.residual[idx + e]) : 0.f);
+          a.y[idx + e] = from_f32<ACT>(y);
+          ss += y * y;
+        }
+    }
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  ss += __shfl_xor(ss, 4);
+  if ((T & 7) == 0 && row < a.m && col < a.n) a.partial[row * ((a.n + 31) / 32) + col / 32] = ss;
+}
+
+template <int ACT>
+hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
+  W8Args a;
+  a.x1 = static_cast<const uint16_t*>(p.x1);
+  a.x2 = static_cast<const uint8_t*>(p.x2);
+  a.scale = static_cast<const uint16_t*>(p.scale);
+  a.offset = static_cast<const uint16_t*>(p.offset);
+  a.bias = static_cast<const uint16_t*>(p.bias);
+  a.residual = static_cast<const uint16_t*>(p.residual);
+  a.y = static_cast<uint16_t*>(p.y);
+  a.partial = partial;
+  a.m = p.m;
+  a.k = p.k;
+  a.n = p.n;
+  const int64_t group = p.group >= p.k ? p.k : p.group;
+  a.upg = p.group >= p.k ? INT32_MAX : (int)(group / 32);
+  a.s_row = p.s_row;
+  a.s_col = p.s_col;
+  const int64_t groups = (p.k + group - 1) / group;
+  a.s_bytes = (uint32_t)(((groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
+  const dim3 grid((unsigned)((p.n + W8_BN - 1) / W8_BN), (unsigned)((p.m + W8_BM - 1) / W8_BM));
+  prof_begin(s);
+  if (p.transpose_x2) gemm_w8<ACT, false><<<grid, 256 * W8_KS, 0, s>>>(a);
+  else gemm_w8<ACT, true><<<grid, 256 * W8_KS, 0, s>>>(a);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// INT8 weights, k a multiple of 16 (16-byte loads never straddle a row of
+// x1 or of the transposed weight); row-major weights with n a multiple of 4
+// (4-byte column groups) and below 2 GiB (one buffer resource).
+bool w8_ok(const WqProblem& p) {
+  if (p.w_bits != 8 || p.k % 16 != 0) return false;
+  if (p.transpose_x2) return true;
+  return p.n % 4 == 0 && p.k * p.n < (int64_t(1) << 31);
+}
+
+hipError_t launch_w8(const WqProblem& p, float* partial, hipStream_t s) {
+  return p.bf16 ? launch_w8_t<ACT_BF16>(p, partial, s) : launch_w8_t<ACT_F16>(p, partial, s);
+}
+
+}  // namespace wq

@@ -77,6 +77,12 @@ int64_t decode_grid(const WqProblem& p);
 size_t decode_partial_bytes(int64_t n);
 hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s);
 
+// INT8-weight tile (any m; k a multiple of 16; row-major weights with n a
+// multiple of 4 below 2 GiB, or transposed); partials as gemm_generic's:
+// [row][ceil(n / 32)].
+bool w8_ok(const WqProblem& p);
+hipError_t launch_w8(const WqProblem& p, float* partial, hipStream_t s);
+
 struct MxProblem {
   const uint8_t* x1;     // (k, m) e4m3
   const uint8_t* x2;     // GFX950_B e2m1

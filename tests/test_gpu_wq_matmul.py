@@ -108,6 +108,68 @@ def test_edge_shapes_int8(shape, transpose):
     check_wq(c, y, nrm)
 
 
+W8 = [  # m, k, n, granularity, group, offset, bias, act: the INT8 64 x 64 tile
+    (64, 1024, 64, "channel", 0, (-0.5, 0.5), 0.1, torch.float16),
+    (100, 208, 132, "group", 32, (-1.0, 1.0), 0.1, torch.bfloat16),   # last K step 16 deep
+    (300, 1024, 200, "group", 128, (-0.5, 0.5), None, torch.float16),
+    (7, 512, 1000, "group", 64, "none", 0.1, torch.bfloat16),
+    (513, 1024, 1028, "channel", 0, (-0.5, 0.5), 0.1, torch.float16),
+    (40, 384, 96, "group", 96, (-1.0, 1.0), 0.1, torch.bfloat16),     # folds mid-step
+    (1, 2048, 4096, "tensor", 0, "none", 0.1, torch.bfloat16),
+    (129, 4096, 260, "group", 192, None, 0.1, torch.float16),
+    (48, 16, 8, "channel2d", 0, (-0.5, 0.5), 0.1, torch.float16),     # one 16-deep step
+    (200, 640, 300, "group", 160, (-1.0, 1.0), 0.1, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", W8, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in W8])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_int8_tile_shapes(shape, transpose):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"w8tile{m}x{k}x{n}", m, k, n, act=act, w_bits=8, granularity=gran,
+                          group_size=g, scale_range=(0.001, 0.01), offset_range=off,
+                          bias_std=bias, seed=5 * m + k + n)
+    note(f"wq int8 tile {c.name} {gran} g={g} {act} transpose={transpose}")
+    y, nrm = wq_on_gpu(c, transpose_x2=transpose)
+    check_wq(c, y, nrm)
+    y2, n2 = wq_on_gpu(c, transpose_x2=transpose, inplace=True)
+    assert torch.equal(y, y2) and torch.equal(nrm, n2)
+
+
+@pytest.mark.parametrize("act", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("k,G", [(256, 32), (320, 64), (512, 0)])
+def test_int8_integer_valued_y_is_bit_exact(act, transpose, k, G):
+    # x1 rows one-hot with sign +-1 (rows 0..3 on K = 0 and 1, where the
+    # codes are -128 and 127), INT8 codes over the whole range, scale 1, no
+    # offset, zero bias, integer residual: y = +-q[p, :] + residual, integers
+    # with |y| <= 132, exact in fp16 and bf16
+    m, n = 36, 72
+    rng = np.random.default_rng(7 * k + G + transpose)
+    pos = rng.integers(0, k, m)
+    pos[:4] = [0, 1, 0, 1]
+    sign = rng.choice([-1.0, 1.0], m)
+    xv = np.zeros((m, k))
+    xv[np.arange(m), pos] = sign
+    x1 = torch.from_numpy(xv.astype(np.float32)).to(act)
+    wv = rng.integers(-128, 128, (k, n), dtype=np.int32)
+    wv[0, :] = -128
+    wv[1, :] = 127
+    w = torch.from_numpy(wv)
+    srows = (k + G - 1) // G if G else 1
+    scale = torch.ones((srows, n) if G else (1,), dtype=act)
+    res = torch.from_numpy(rng.integers(-4, 5, (1, m, n)).astype(np.float32)).to(act)
+    c = workloads.WQCase("intexact8", x1, w, 8, scale, None, G, torch.zeros(n, dtype=act), res,
+                         torch.ones(n, dtype=act), 1e-6)
+    _, oy, on = oracle.wq_matmul_add_rmsnorm(as_f64(x1), wv, as_f64(scale), None, G, None,
+                                             as_f64(res).reshape(m, n), np.ones(n), 1e-6)
+    assert np.max(np.abs(oy)) <= 132            # the case's own precondition
+    note(f"wq int8 integer-exact {act} k={k} G={G} transpose={transpose}")
+    y, nrm = wq_on_gpu(c, transpose_x2=transpose)
+    assert np.array_equal(as_f64(y).reshape(m, n), oy)
+    assert oracle.rel_err_floor(nrm, on) <= 1e-2
+
+
 def test_inplace_matches_out_of_place():
     c = workloads.tiny()
     note("wq inplace tiny")
@@ -342,6 +404,10 @@ ONE_SIGN = [  # m, k, n, granularity, group, offset, act
     (1, 8192, 1024, "channel", 0, (-0.1, 0.1), torch.float16),
     (40, 8192, 256, "group", 64, None, torch.float16),          # generic tile (group 64)
 ]
+ONE_SIGN_W8 = [  # the INT8 tile: one group over all of K, and group 64
+    (130, 8192, 520, "channel", 0, None, torch.float16),
+    (64, 8192, 256, "group", 64, (-0.1, 0.1), torch.bfloat16),
+]
 
 
 @pytest.mark.parametrize("shape", ONE_SIGN,
@@ -351,8 +417,23 @@ def test_one_sign_activations(shape):
     c = workloads.wq_case(f"one-sign {m}x{k}x{n} {gran}{G}", m, k, n, act=act, w_bits=4,
                           granularity=gran, group_size=G, scale_range=(0.002, 0.02),
                           offset_range=off, x1_abs=True, w_range=(-7, 7))
-    note(f"wq one-sign activations {shape}")
-    y, nrm = wq_on_gpu(c)
+    _one_sign_check(c, shape, act)
+
+
+@pytest.mark.parametrize("shape", ONE_SIGN_W8,
+                         ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}-{str(s[6])[6:]}" for s in ONE_SIGN_W8])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_one_sign_activations_int8(shape, transpose):
+    m, k, n, gran, G, off, act = shape
+    c = workloads.wq_case(f"one-sign8 {m}x{k}x{n} {gran}{G}", m, k, n, act=act, w_bits=8,
+                          granularity=gran, group_size=G, scale_range=(0.001, 0.01),
+                          offset_range=off, x1_abs=True, w_range=(-127, 127))
+    _one_sign_check(c, shape, act, transpose)
+
+
+def _one_sign_check(c, shape, act, transpose=False):
+    note(f"wq one-sign activations {shape} w{c.w_bits} transpose={transpose}")
+    y, nrm = wq_on_gpu(c, transpose_x2=transpose)
     ey, en = check_wq(c, y, nrm)
     if act == torch.float16:
         # fp16 rounds its outputs to 2^-11: what remains visible is the
