@@ -38,9 +38,10 @@
 // v_permlane16_swap) transpose the 4 x 4 dwords: afterwards step j holds
 // sub-block j in every row, i.e. K values 128 kb + 32 j .. + 31, which lie in
 // one group, and the x1 fragments are fetched to match (row R, K values
-// 32 j + 8 R .. + 7). Each fold unit then has its own MFMA accumulators, and
-// its scale and offset, loaded by the lanes of one row, reach the other rows
-// by the same swaps.
+// 32 j + 8 R .. + 7). Each fold unit accumulates into one of two MFMA
+// accumulator sets and is folded while the next unit's MFMAs run; its scale
+// and offset, loaded by the lanes of one row, reach the other rows by the
+// same swaps.
 //
 // Epilogue: y = acc + bias + residual (stored rounded to the activation
 // dtype) and, per (workgroup, row), the sum of the float32 y^2 over the
@@ -74,9 +75,12 @@ struct DecodeArgs {
   float omul;                // 1 with an offset, 0 without
 };
 
-// fold units per 128-deep block
+// fold units per 128-deep block, and MFMA accumulator sets (two for short
+// groups: one unit accumulates while the previous one is folded)
 template <int SPG>
 constexpr int fold_units() { return 4 / SPG; }
+template <int SPG>
+constexpr int acc_sets() { return SPG == 4 ? 1 : 2; }
 
 template <int CTW>
 struct DecodeLane {
@@ -102,10 +106,10 @@ constexpr int batch_loads() { return CTW + 4 + 2 * CTW; }
 // place (cleared in place by a multiply with zero at each block start), so
 // each MFMA's destination is exactly its accumulator source and never
 // overlaps its A or B operand.
-template <int CTW, int U>
+template <int CTW, int NS>
 struct DecodeAcc {
-  f32x4 part[U][CTW];        // per fold unit
-  f32x4 rs[U];
+  f32x4 part[NS][CTW];       // per accumulator set
+  f32x4 rs[NS];
 };
 
 // One buffer -> LDS DMA instruction: 16 bytes per lane, written to dst in
@@ -177,71 +181,102 @@ __device__ __forceinline__ u32x4 transpose_rows(u32x4 d) {
   return (u32x4){d0, d1, d2, d3};
 }
 
-// Row u * SPG of v to every row, for each fold unit u.
-template <int SPG>
-__device__ __forceinline__ void bcast_units(float v, float (&out)[fold_units<SPG>()]) {
+// Row U * SPG of v (the value that lane row loaded for fold unit U) to
+// every row.
+template <int SPG, int U>
+__device__ __forceinline__ float bcast_unit(float v) {
   uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
   swap32(a, b);                              // a = [r0, r1, r0, r1], b = [r2, r3, r2, r3]
-  if constexpr (SPG == 2) {
-    out[0] = __builtin_bit_cast(float, a);
-    out[1] = __builtin_bit_cast(float, b);
-  } else {
-    uint32_t a2 = a, b2 = b;
-    swap16(a, a2);                           // a = r0 everywhere, a2 = r1
-    swap16(b, b2);                           // b = r2, b2 = r3
-    out[0] = __builtin_bit_cast(float, a);
-    out[1] = __builtin_bit_cast(float, a2);
-    out[2] = __builtin_bit_cast(float, b);
-    out[3] = __builtin_bit_cast(float, b2);
+  uint32_t x = (U * SPG) < 2 ? a : b;
+  if constexpr (SPG == 1) {
+    uint32_t y = x;
+    swap16(x, y);                            // x = [x0, x0, x0, x0], y = [x1, x1, x1, x1]
+    x = (U & 1) ? y : x;
   }
+  return __builtin_bit_cast(float, x);
 }
 
 template <int ACT, int CTW, int SPG>
 __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch<CTW>& b, const uint8_t* xs,
-                                          DecodeAcc<CTW, fold_units<SPG>()>& ma, f32x4 (&acc)[CTW]) {
+                                          DecodeAcc<CTW, acc_sets<SPG>()>& ma, f32x4 (&acc)[CTW]) {
   constexpr int U = fold_units<SPG>();
   const int lane = threadIdx.x & 63;
   const uint32_t one2 = pack2<ACT>(1.f, 1.f);
   const u32x4 ones = {one2, one2, one2, one2};
+  if constexpr (SPG == 4) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ma.rs[u][i] *= 0.f;
+    for (int i = 0; i < 4; ++i) ma.rs[0][i] *= 0.f;
 #pragma unroll
     for (int c = 0; c < CTW; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ma.part[u][c][i] *= 0.f;
-  }
-  u32x4 w[CTW];
+      for (int i = 0; i < 4; ++i) ma.part[0][c][i] *= 0.f;
 #pragma unroll
-  for (int c = 0; c < CTW; ++c) w[c] = SPG == 4 ? b.w[c] : transpose_rows(b.w[c]);
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
+      ma.rs[0] = mfma16<ACT>(av, ones, ma.rs[0]);
 #pragma unroll
-  for (int w4 = 0; w4 < 4; ++w4) {
-    const int u = w4 / SPG;
-    const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
-    ma.rs[u] = mfma16<ACT>(av, ones, ma.rs[u]);
+      for (int c = 0; c < CTW; ++c) ma.part[0][c] = mfma16<ACT>(av, unpack8_low<ACT>(b.w[c][w4]), ma.part[0][c]);
+      // one K step's operands at a time (bounds the live unpacked fragments)
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) ma.part[u][c] = mfma16<ACT>(av, unpack8_low<ACT>(w[c][w4]), ma.part[u][c]);
-    // one K step's operands at a time (bounds the live unpacked fragments)
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int c = 0; c < CTW; ++c) {
-    const float s = to_f32<ACT>((uint16_t)b.s[c]);
-    const float o = to_f32<ACT>((uint16_t)b.o[c]) * a.omul;
-    const float cc = o - UnpackLow<ACT>::bias * s;
-    if constexpr (SPG == 4) {
+    for (int c = 0; c < CTW; ++c) {
+      const float s = to_f32<ACT>((uint16_t)b.s[c]);
+      const float o = to_f32<ACT>((uint16_t)b.o[c]) * a.omul;
+      const float cc = o - UnpackLow<ACT>::bias * s;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[0][c][i], fmaf(cc, ma.rs[0][i], acc[c][i]));
-    } else {
-      float su[U], cu[U];
-      bcast_units<SPG>(s, su);
-      bcast_units<SPG>(cc, cu);
+    }
+  } else {
+    // lane row R holds the scale and folded offset of unit R / SPG
+    float sr[CTW], cr[CTW];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int c = 0; c < CTW; ++c) {
+      sr[c] = to_f32<ACT>((uint16_t)b.s[c]);
+      cr[c] = to_f32<ACT>((uint16_t)b.o[c]) * a.omul - UnpackLow<ACT>::bias * sr[c];
+    }
+    u32x4 w[CTW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[c][i] = fmaf(su[u], ma.part[u][c][i], fmaf(cu[u], ma.rs[u][i], acc[c][i]));
+    for (int c = 0; c < CTW; ++c) w[c] = transpose_rows(b.w[c]);
+    // unit u accumulates into set u % 2 and is folded after unit u + 1's
+    // MFMAs are issued, so the fold does not wait on its own MFMAs
+#pragma unroll
+    for (int u = 0; u <= U; ++u) {
+      if (u < U) {
+        const int st = u & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ma.rs[st][i] *= 0.f;
+#pragma unroll
+        for (int c = 0; c < CTW; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ma.part[st][c][i] *= 0.f;
+#pragma unroll
+        for (int w4 = u * SPG; w4 < (u + 1) * SPG; ++w4) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
+          ma.rs[st] = mfma16<ACT>(av, ones, ma.rs[st]);
+#pragma unroll
+          for (int c = 0; c < CTW; ++c)
+            ma.part[st][c] = mfma16<ACT>(av, unpack8_low<ACT>(w[c][w4]), ma.part[st][c]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (u > 0) {
+        const int ps = (u - 1) & 1;
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+          float su, cu;
+          switch (u - 1) {   // unrolled: a constant unit index
+            case 0: su = bcast_unit<SPG, 0>(sr[c]); cu = bcast_unit<SPG, 0>(cr[c]); break;
+            case 1: su = bcast_unit<SPG, 1>(sr[c]); cu = bcast_unit<SPG, 1>(cr[c]); break;
+            case 2: su = bcast_unit<SPG, 2>(sr[c]); cu = bcast_unit<SPG, 2>(cr[c]); break;
+            default: su = bcast_unit<SPG, 3>(sr[c]); cu = bcast_unit<SPG, 3>(cr[c]); break;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[c][i] = fmaf(su, ma.part[ps][c][i], fmaf(cu, ma.rs[ps][i], acc[c][i]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -308,9 +343,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const int kb0 = wave * a.kpw;
   const int kb1 = kb0 + a.kpw < kbs ? kb0 + a.kpw : kbs;
   f32x4 acc[CTW];
-  DecodeAcc<CTW, fold_units<SPG>()> ma;
+  DecodeAcc<CTW, acc_sets<SPG>()> ma;
 #pragma unroll
-  for (int u = 0; u < fold_units<SPG>(); ++u) {
+  for (int u = 0; u < acc_sets<SPG>(); ++u) {
     ma.rs[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < CTW; ++i) ma.part[u][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -401,7 +436,8 @@ void launch_act(const DecodeArgs& a, int spg, int ctw, unsigned grid, hipStream_
     if (ctw == 1) gemm_decode<ACT, 1, 2><<<dim3(grid), 1024, 0, s>>>(a);
     else gemm_decode<ACT, 2, 2><<<dim3(grid), 1024, 0, s>>>(a);
   } else {
-    gemm_decode<ACT, 1, 1><<<dim3(grid), 1024, 0, s>>>(a);
+    if (ctw == 1) gemm_decode<ACT, 1, 1><<<dim3(grid), 1024, 0, s>>>(a);
+    else gemm_decode<ACT, 2, 1><<<dim3(grid), 1024, 0, s>>>(a);
   }
   prof_end(s);
 }
@@ -414,12 +450,12 @@ int decode_spg(const WqProblem& p) {
 }
 
 // column tiles per workgroup: keep the grid within one workgroup per CU up to
-// 768 tiles (n = 12288); wider layers take more workgroups of 3. The per-unit
-// accumulators of short groups cap the tiles at 2 (SPG = 2) or 1 (SPG = 1)
-// within the register budget of 16 waves per CU.
+// 768 tiles (n = 12288); wider layers take more workgroups of 3. The second
+// accumulator set of short groups caps the tiles at 2 within the register
+// budget of 16 waves per CU.
 int decode_ctw(int64_t nct, int spg) {
   const int ctw = nct <= 256 ? 1 : nct <= 512 ? 2 : 3;
-  const int cap = spg == 4 ? 3 : spg == 2 ? 2 : 1;
+  const int cap = spg == 4 ? 3 : 2;
   return ctw < cap ? ctw : cap;
 }
 
