@@ -66,12 +66,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b_wide_prefill_traffic.md")
 
 
 def source_hash() -> str:
-    """Hash of the sources of the prefill call's kernels: traffic counters
-    taken on other sources do not describe this build."""
+    """Hash of the sources the prefill MFMA tile (gemm_b_wide) is compiled
+    from: traffic counters taken on other sources do not describe this
+    build."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_gemm_int4_amd", "csrc")
-    for f in ("wq_gemm_fast.hip", "wq_gemm.hip", "wq_unpack.h", "wq_device.h"):
+    for f in ("wq_gemm_fast.hip", "wq_unpack.h", "wq_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
