@@ -45,12 +45,14 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ s1,
                                                       const uint8_t* __restrict__ s2,
                                                       float* __restrict__ y, int64_t M, int64_t K,
-                                                      int64_t N, int64_t Np) {
+                                                      int64_t N, int64_t Np, int64_t mb, int64_t nb,
+                                                      int64_t ne) {
   __shared__ __attribute__((aligned(16))) uint8_t As[MX_BM][MX_LDS];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * MX_BM;
-  const int64_t n0 = (int64_t)blockIdx.x * MX_BN;
+  // the grid covers rows [mb, M) and columns [nb, ne) of the (M, N) output
+  const int64_t m0 = mb + (int64_t)blockIdx.y * MX_BM;
+  const int64_t n0 = nb + (int64_t)blockIdx.x * MX_BN;
   const int64_t KB = (K + 31) / 32;
   f32x4 acc[2][2] = {};
 
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict_
       u32x4 bv = {0, 0, 0, 0};
       if (col < Np) bv = *reinterpret_cast<const u32x4*>(x2 + ((kb / 4) * Np + col) * 64 + (kb % 4) * 16);
       bf[i] = (i32x8){(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
-      sb[i] = (col < N && kb < KB) ? (int)s2[kb * N + col] : 127;
+      sb[i] = (col < ne && kb < KB) ? (int)s2[kb * N + col] : 127;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = n0 + wc * 32 + j * 16 + (lane & 15);
-      if (col >= N) continue;
+      if (col >= ne) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + wr * 32 + i * 16 + 4 * (lane >> 4) + r;
@@ -129,20 +131,56 @@ struct MfBufs {
   uint8_t* s2;
 };
 
+// The tile's global inputs. With RG (a ragged shape: K not a multiple of 128,
+// or M, N not multiples of 256) every input goes through a buffer resource
+// (a read past the tensor returns zero).
+struct MfSrc {
+  const uint8_t* x1t;
+  const uint8_t* x2;
+  const uint8_t* s1;
+  const uint8_t* s2;
+  __amdgpu_buffer_rsrc_t rx, rw, rs1, rs2;
+};
+
+__device__ __forceinline__ void mf_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void mf_dma4(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, 0, 0, 0);
+}
+
 // DMA of one 128-deep step into the given buffers: 7 instructions per wave
 // (x1: 4 KiB in four 1 KiB pieces; weights: 2 KiB; one 256-byte scale row).
-__device__ __forceinline__ void mf_dma(const uint8_t* __restrict__ x1t, const uint8_t* __restrict__ x2,
-                                       const uint8_t* __restrict__ s1, const uint8_t* __restrict__ s2,
-                                       const MfBufs& bf, int64_t M, int64_t N, int64_t Np, int64_t KB,
-                                       int64_t m0, int64_t n0, int step, int wave, int lane) {
+// With RG, waves 0..3 read their scale1 bytes with byte loads instead (issued
+// first, so that their wait does not cover the DMA) and return them packed;
+// the caller writes them to LDS before the step's closing barrier.
+template <bool RG>
+__device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, int64_t M, int64_t N,
+                                           int64_t Np, int64_t KB, int64_t m0, int64_t n0, int step,
+                                           int wave, int lane) {
   const int64_t k0 = (int64_t)step * MF_BK;
+  uint32_t s1w = 0;
+  if constexpr (RG) {
+    if (wave < 4) {
+      const int64_t row = m0 + 64 * wave + lane;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t blk = 4 * (int64_t)step + b;
+        const uint32_t off = blk < KB ? (uint32_t)(row * KB + blk) : BUF_OOB;
+        s1w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(src.rs1, off, 0, 0) << (8 * b);
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = 4 * wave + i;                 // k-rows 4q .. 4q + 3
     const int r = 4 * q + (lane >> 4);
     const int c = (lane & 15) ^ mf_swz(r);      // logical chunk for this physical slot
-    __builtin_amdgcn_global_load_lds((glb_void*)(x1t + (k0 + r) * M + m0 + 16 * c),
-                                     (lds_void*)(bf.a + q * 1024), 16, 0, 0);
+    if constexpr (RG)
+      mf_dma16(src.rx, bf.a + q * 1024, (uint32_t)((k0 + r) * M + m0 + 16 * c));
+    else
+      __builtin_amdgcn_global_load_lds((glb_void*)(src.x1t + (k0 + r) * M + m0 + 16 * c),
+                                       (lds_void*)(bf.a + q * 1024), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -152,16 +190,24 @@ __device__ __forceinline__ void mf_dma(const uint8_t* __restrict__ x1t, const ui
     const int q = 2 * wave + i;
     const int sl = 16 * q + (lane >> 2);
     const int col = (sl & 128) + 8 * (sl & 15) + ((sl >> 4) & 7);
-    __builtin_amdgcn_global_load_lds((glb_void*)(x2 + ((int64_t)step * Np + n0 + col) * 64 + 16 * (lane & 3)),
-                                     (lds_void*)(bf.b + q * 1024), 16, 0, 0);
+    if constexpr (RG)
+      mf_dma16(src.rw, bf.b + q * 1024, (uint32_t)(((int64_t)step * Np + n0 + col) * 64 + 16 * (lane & 3)));
+    else
+      __builtin_amdgcn_global_load_lds((glb_void*)(src.x2 + ((int64_t)step * Np + n0 + col) * 64 + 16 * (lane & 3)),
+                                       (lds_void*)(bf.b + q * 1024), 16, 0, 0);
   }
   if (wave < 4) {   // scale1 rows m0 + 64 wave + lane, blocks 4 step .. 4 step + 3
-    __builtin_amdgcn_global_load_lds((glb_void*)(s1 + (m0 + 64 * wave + lane) * KB + 4 * step),
-                                     (lds_void*)(bf.s1 + wave * 256), 4, 0, 0);
+    if constexpr (!RG)
+      __builtin_amdgcn_global_load_lds((glb_void*)(src.s1 + (m0 + 64 * wave + lane) * KB + 4 * step),
+                                       (lds_void*)(bf.s1 + wave * 256), 4, 0, 0);
   } else {          // scale2 block row 4 step + (wave - 4), columns n0 .. n0 + 255
-    __builtin_amdgcn_global_load_lds((glb_void*)(s2 + (4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane),
-                                     (lds_void*)(bf.s2 + (wave - 4) * 256), 4, 0, 0);
+    if constexpr (RG)
+      mf_dma4(src.rs2, bf.s2 + (wave - 4) * 256, (uint32_t)((4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane));
+    else
+      __builtin_amdgcn_global_load_lds((glb_void*)(src.s2 + (4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane),
+                                       (lds_void*)(bf.s2 + (wave - 4) * 256), 4, 0, 0);
   }
+  return s1w;
 }
 
 // The eight MFMAs of one A fragment (row block i) against the weight
@@ -175,6 +221,8 @@ __device__ __forceinline__ void mf_row(f32x4 (&acc)[8], const i32x8& af, const u
         0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, sa, J & 3, (int)(J < 4 ? sbw.x : sbw.y))), ...);
 }
 
+// The tiles cover the (M, N) output, all of K.
+template <bool RG>
 __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict__ x1t,
                                                        const uint8_t* __restrict__ x2,
                                                        const uint8_t* __restrict__ s1,
@@ -196,8 +244,19 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   const int64_t T = tiles_m * tiles_n;
   if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
   const int64_t m0 = (id / tiles_n) * MF_BM, n0 = (id % tiles_n) * MF_BN;
-  const int64_t KB = K / 32;
-  const int steps = (int)(K / MF_BK);
+  const int64_t KB = (K + 31) / 32;
+  const int steps = (int)((K + MF_BK - 1) / MF_BK);
+  MfSrc src;
+  src.x1t = x1t;
+  src.x2 = x2;
+  src.s1 = s1;
+  src.s2 = s2;
+  if constexpr (RG) {
+    src.rx = buf_rsrc(x1t, (uint32_t)(K * M));
+    src.rw = buf_rsrc(x2, (uint32_t)((int64_t)steps * Np * 64));
+    src.rs1 = buf_rsrc(s1, (uint32_t)(M * KB));
+    src.rs2 = buf_rsrc(s2, (uint32_t)(KB * N));
+  }
   MfBufs buf0, buf1;
   buf0.a = a0; buf0.b = b0; buf0.s1 = s10; buf0.s2 = s20;
   buf1.a = a1; buf1.b = b1; buf1.s1 = s11; buf1.s2 = s21;
@@ -210,6 +269,11 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   const __amdgpu_buffer_rsrc_t ry = buf_rsrc(y, (uint32_t)(M * N * 4));
   const uint32_t yl = (uint32_t)((4 * (lane >> 4)) * N + 8 * (lane & 15)) * 4u;
   const uint32_t yw = (uint32_t)(((m0 + 64 * wm) * N + n0 + 128 * wn) * 4);
+  // with a ragged shape, rows past M and 4-column runs past N (N % 4 == 0)
+  // are neither read nor written: out-of-range offsets
+  auto y_ok = [&](int i, int r, int h) {
+    return m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r < M && n0 + 128 * wn + 8 * (lane & 15) + 4 * h < N;
+  };
   f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -218,7 +282,8 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
       const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, yl + 16u * h, so, 0));
+        const uint32_t vo = RG && !y_ok(i, r, h) ? BUF_OOB : yl + 16u * h;
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, vo, so, 0));
         acc[i][4 * h + 0][r] = __uint_as_float(v.x);
         acc[i][4 * h + 1][r] = __uint_as_float(v.y);
         acc[i][4 * h + 2][r] = __uint_as_float(v.z);
@@ -226,8 +291,11 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
       }
     }
 
-  mf_dma(x1t, x2, s1, s2, buf0, M, N, Np, KB, m0, n0, 0, wave, lane);
-  wait_vm<0>();
+  {
+    const uint32_t s1w = mf_dma<RG>(src, buf0, M, N, Np, KB, m0, n0, 0, wave, lane);
+    wait_vm<0>();
+    if (RG && wave < 4) *reinterpret_cast<uint32_t*>(buf0.s1 + wave * 256 + 4 * lane) = s1w;
+  }
   __syncthreads();
 
   // per-lane LDS read offsets (independent of the step)
@@ -246,7 +314,8 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   // `nxt`. The single barrier at the end both publishes every wave's DMA into
   // `nxt` and frees `cur`, which the next step's DMA refills.
   auto do_step = [&](int step, const MfBufs& cur, const MfBufs& nxt) {
-    if (step + 1 < steps) mf_dma(x1t, x2, s1, s2, nxt, M, N, Np, KB, m0, n0, step + 1, wave, lane);
+    uint32_t s1w = 0;
+    if (step + 1 < steps) s1w = mf_dma<RG>(src, nxt, M, N, Np, KB, m0, n0, step + 1, wave, lane);
     u32x4 bv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const u32x4*>(cur.b + boff + 1024 * j);
@@ -265,6 +334,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
       mf_row(acc[i], af, bv, sa, sbw, std::make_integer_sequence<int, 8>{});
     }
     wait_vm<0>();            // this wave's DMA into `nxt` has landed
+    if (RG && wave < 4 && step + 1 < steps) *reinterpret_cast<uint32_t*>(nxt.s1 + wave * 256 + 4 * lane) = s1w;
     __syncthreads();
   };
   for (int step = 0; step < steps; step += 2) {
@@ -284,7 +354,8 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
         v.y = __float_as_uint(acc[i][4 * h + 1][r]);
         v.z = __float_as_uint(acc[i][4 * h + 2][r]);
         v.w = __float_as_uint(acc[i][4 * h + 3][r]);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, yl + 16u * h, so, 0);
+        const uint32_t vo = RG && !y_ok(i, r, h) ? BUF_OOB : yl + 16u * h;
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, vo, so, 0);
       }
     }
 }
@@ -292,18 +363,28 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
 
 hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s) {
   const int64_t Np = 16 * ((p.n + 15) / 16);
-  // the tiled kernel addresses y through a buffer resource (32-bit offsets)
-  if (p.m % MF_BM == 0 && p.n % MF_BN == 0 && p.k % MF_BK == 0 && p.m * p.n * 4 < (int64_t(1) << 31)) {
-    const int64_t tm = p.m / MF_BM, tn = p.n / MF_BN;
-    prof_begin(s);
-    mx_gemm_tile<<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
-                                                         Np, tm, tn);
-    prof_end(s);
-    return hipGetLastError();
-  }
-  dim3 grid((unsigned)((p.n + MX_BN - 1) / MX_BN), (unsigned)((p.m + MX_BM - 1) / MX_BM));
+  const int64_t KB = (p.k + 31) / 32, steps = (p.k + MF_BK - 1) / MF_BK;
+  const int64_t tm = (p.m + MF_BM - 1) / MF_BM, tn = (p.n + MF_BN - 1) / MF_BN;
+  const bool aligned = p.m % MF_BM == 0 && p.n % MF_BN == 0 && p.k % MF_BK == 0;
+  // The 256 x 256 tile: x1 rows of 16-byte chunks (M % 16), 4-byte scale2
+  // pieces and 16-byte y runs (N % 4), y below 2 GiB (one buffer resource);
+  // a ragged shape also needs every input, and every offset its last step
+  // and its last tile row and column form past the inputs, below 2 GiB.
+  const int64_t lim = int64_t(1) << 31;
+  const bool tile = p.m % 16 == 0 && p.n % 4 == 0 && p.m * p.n * 4 < lim &&
+                    (aligned || ((steps + 1) * MF_BK * p.m < lim && (p.m + MF_BM) * KB < lim &&
+                                 (KB + 8) * p.n < lim && steps * Np * 64 < lim));
   prof_begin(s);
-  mx_gemm_kernel<<<grid, 256, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n, Np);
+  if (tile && aligned) {
+    mx_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
+                                                                Np, tm, tn);
+  } else if (tile) {
+    mx_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
+                                                               Np, tm, tn);
+  } else {
+    dim3 grid((unsigned)((p.n + MX_BN - 1) / MX_BN), (unsigned)((p.m + MX_BM - 1) / MX_BM));
+    mx_gemm_kernel<<<grid, 256, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n, Np, 0, 0, p.n);
+  }
   prof_end(s);
   return hipGetLastError();
 }
