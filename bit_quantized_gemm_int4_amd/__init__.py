@@ -317,9 +317,13 @@ def matmul_add_rmsnorm(x1: torch.Tensor, x2: torch.Tensor, k: int, n: int, w_dty
 def mx_matmul_inplace_add(x1_t: torch.Tensor, x2_packed: torch.Tensor, x1_scale: torch.Tensor,
                           x2_scale: torch.Tensor, y: torch.Tensor, m: int, k: int, n: int,
                           group_size: int = MX_GROUP_SIZE, stream=None) -> torch.Tensor:
-    """y += the MX block-32 product; x1_t is (k, m) E4M3, x2 GFX950_B E2M1."""
+    """y += the MX block-32 product; x1_t is (k, m) E4M3, x2 GFX950_B E2M1.
+    Allocates the optional workspace the size query asks for (m not a
+    multiple of 16: the large tile on a padded copy of x1)."""
+    wsn = mx_quant_matmul_inplace_add_workspace_size(m, k, n)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=y.device) if wsn else None
     mx_quant_matmul_inplace_add(x1_t, x2_packed, WQ_LAYOUT_GFX950_B, x1_scale, x2_scale, m, k, n,
-                                1, 0, group_size, y, None, 0, stream)
+                                1, 0, group_size, y, ws, wsn, stream)
     return y
 
 

@@ -155,7 +155,7 @@ __device__ __forceinline__ void mf_dma4(__amdgpu_buffer_rsrc_t r, uint8_t* dst, 
 // first, so that their wait does not cover the DMA) and return them packed;
 // the caller writes them to LDS before the step's closing barrier.
 template <bool RG>
-__device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, int64_t M, int64_t N,
+__device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, int64_t Mx, int64_t N,
                                            int64_t Np, int64_t KB, int64_t m0, int64_t n0, int step,
                                            int wave, int lane) {
   const int64_t k0 = (int64_t)step * MF_BK;
@@ -177,9 +177,9 @@ __device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, i
     const int r = 4 * q + (lane >> 4);
     const int c = (lane & 15) ^ mf_swz(r);      // logical chunk for this physical slot
     if constexpr (RG)
-      mf_dma16(src.rx, bf.a + q * 1024, (uint32_t)((k0 + r) * M + m0 + 16 * c));
+      mf_dma16(src.rx, bf.a + q * 1024, (uint32_t)((k0 + r) * Mx + m0 + 16 * c));
     else
-      __builtin_amdgcn_global_load_lds((glb_void*)(src.x1t + (k0 + r) * M + m0 + 16 * c),
+      __builtin_amdgcn_global_load_lds((glb_void*)(src.x1t + (k0 + r) * Mx + m0 + 16 * c),
                                        (lds_void*)(bf.a + q * 1024), 16, 0, 0);
   }
 #pragma unroll
@@ -221,14 +221,15 @@ __device__ __forceinline__ void mf_row(f32x4 (&acc)[8], const i32x8& af, const u
         0 /*A: E4M3*/, 4 /*B: E2M1*/, 0, sa, J & 3, (int)(J < 4 ? sbw.x : sbw.y))), ...);
 }
 
-// The tiles cover the (M, N) output, all of K.
+// The tiles cover the (M, N) output, all of K; x1's rows are Mx >= M bytes
+// apart (Mx = M, or M padded to 16 in a workspace copy).
 template <bool RG>
 __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict__ x1t,
                                                        const uint8_t* __restrict__ x2,
                                                        const uint8_t* __restrict__ s1,
                                                        const uint8_t* __restrict__ s2,
-                                                       float* __restrict__ y, int64_t M, int64_t K,
-                                                       int64_t N, int64_t Np, int64_t tiles_m,
+                                                       float* __restrict__ y, int64_t M, int64_t Mx,
+                                                       int64_t K, int64_t N, int64_t Np, int64_t tiles_m,
                                                        int64_t tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t a0[MF_ABYTES], a1[MF_ABYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[MF_BBYTES], b1[MF_BBYTES];
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   src.s1 = s1;
   src.s2 = s2;
   if constexpr (RG) {
-    src.rx = buf_rsrc(x1t, (uint32_t)(K * M));
+    src.rx = buf_rsrc(x1t, (uint32_t)(K * Mx));
     src.rw = buf_rsrc(x2, (uint32_t)((int64_t)steps * Np * 64));
     src.rs1 = buf_rsrc(s1, (uint32_t)(M * KB));
     src.rs2 = buf_rsrc(s2, (uint32_t)(KB * N));
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
     }
 
   {
-    const uint32_t s1w = mf_dma<RG>(src, buf0, M, N, Np, KB, m0, n0, 0, wave, lane);
+    const uint32_t s1w = mf_dma<RG>(src, buf0, Mx, N, Np, KB, m0, n0, 0, wave, lane);
     wait_vm<0>();
     if (RG && wave < 4) *reinterpret_cast<uint32_t*>(buf0.s1 + wave * 256 + 4 * lane) = s1w;
   }
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   // `nxt` and frees `cur`, which the next step's DMA refills.
   auto do_step = [&](int step, const MfBufs& cur, const MfBufs& nxt) {
     uint32_t s1w = 0;
-    if (step + 1 < steps) s1w = mf_dma<RG>(src, nxt, M, N, Np, KB, m0, n0, step + 1, wave, lane);
+    if (step + 1 < steps) s1w = mf_dma<RG>(src, nxt, Mx, N, Np, KB, m0, n0, step + 1, wave, lane);
     u32x4 bv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const u32x4*>(cur.b + boff + 1024 * j);
@@ -359,27 +360,66 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
       }
     }
 }
+
+// x1 (K, M) -> (K, Mx) with zero columns past M: one 16-byte output chunk per
+// thread (its source bytes read one by one: rows of x1 need not be aligned).
+__global__ __launch_bounds__(256) void mx_pad_x1(const uint8_t* __restrict__ x1t, uint8_t* __restrict__ out,
+                                                 int64_t K, int64_t M, int64_t Mx) {
+  const int64_t chunks = Mx / 16;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= K * chunks) return;
+  const int64_t k = i / chunks, c = i - k * chunks;
+  const uint8_t* src = x1t + k * M + 16 * c;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int b = 0; b < 16; ++b)
+    if (16 * c + b < M) w[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
+  *reinterpret_cast<u32x4*>(out + k * Mx + 16 * c) = (u32x4){w[0], w[1], w[2], w[3]};
+}
+
+// The 256 x 256 tile takes x1 rows of 16-byte chunks (Mx % 16), 4-byte
+// scale2 pieces and 16-byte y runs (N % 4), y below 2 GiB (one buffer
+// resource); a ragged shape also needs every input, and every offset its last
+// step and its last tile row and column form past the inputs, below 2 GiB.
+bool mx_tile_ok(int64_t m, int64_t mx, int64_t k, int64_t n) {
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t Np = 16 * ((n + 15) / 16);
+  const int64_t KB = (k + 31) / 32, steps = (k + MF_BK - 1) / MF_BK;
+  const bool aligned = m % MF_BM == 0 && n % MF_BN == 0 && k % MF_BK == 0 && mx == m;
+  return mx % 16 == 0 && n % 4 == 0 && m * n * 4 < lim &&
+         (aligned || ((steps + 1) * MF_BK * mx < lim && (m + MF_BM) * KB < lim && (KB + 8) * n < lim &&
+                      steps * Np * 64 < lim));
+}
+
 }  // namespace
+
+size_t mx_x1pad_bytes(int64_t m, int64_t k, int64_t n) {
+  if (m <= 0 || k <= 0 || n <= 0 || m % 16 == 0) return 0;
+  const int64_t mx = 16 * ((m + 15) / 16);
+  if (!mx_tile_ok(m, mx, k, n)) return 0;
+  return ((size_t)(k * mx) + 255) & ~(size_t)255;
+}
 
 hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s) {
   const int64_t Np = 16 * ((p.n + 15) / 16);
-  const int64_t KB = (p.k + 31) / 32, steps = (p.k + MF_BK - 1) / MF_BK;
   const int64_t tm = (p.m + MF_BM - 1) / MF_BM, tn = (p.n + MF_BN - 1) / MF_BN;
   const bool aligned = p.m % MF_BM == 0 && p.n % MF_BN == 0 && p.k % MF_BK == 0;
-  // The 256 x 256 tile: x1 rows of 16-byte chunks (M % 16), 4-byte scale2
-  // pieces and 16-byte y runs (N % 4), y below 2 GiB (one buffer resource);
-  // a ragged shape also needs every input, and every offset its last step
-  // and its last tile row and column form past the inputs, below 2 GiB.
-  const int64_t lim = int64_t(1) << 31;
-  const bool tile = p.m % 16 == 0 && p.n % 4 == 0 && p.m * p.n * 4 < lim &&
-                    (aligned || ((steps + 1) * MF_BK * p.m < lim && (p.m + MF_BM) * KB < lim &&
-                                 (KB + 8) * p.n < lim && steps * Np * 64 < lim));
+  // x1 rows not 16-byte aligned: with a workspace, the tile runs on a padded copy
+  const bool pad = p.m % 16 != 0 && p.x1pad != nullptr && mx_x1pad_bytes(p.m, p.k, p.n) > 0;
+  const int64_t mx = pad ? 16 * ((p.m + 15) / 16) : p.m;
+  const uint8_t* x1 = pad ? p.x1pad : p.x1;
   prof_begin(s);
-  if (tile && aligned) {
-    mx_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
+  if (pad) {
+    const int64_t threads = p.k * (mx / 16);
+    mx_pad_x1<<<dim3((unsigned)((threads + 255) / 256)), 256, 0, s>>>(p.x1, p.x1pad, p.k, p.m, mx);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (mx_tile_ok(p.m, mx, p.k, p.n) && aligned && !pad) {
+    mx_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx, p.k, p.n,
                                                                 Np, tm, tn);
-  } else if (tile) {
-    mx_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n,
+  } else if (mx_tile_ok(p.m, mx, p.k, p.n)) {
+    mx_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx, p.k, p.n,
                                                                Np, tm, tn);
   } else {
     dim3 grid((unsigned)((p.n + MX_BN - 1) / MX_BN), (unsigned)((p.m + MX_BM - 1) / MX_BM));

@@ -321,10 +321,7 @@ wq_status wq_add_rms_norm(const void* x, const void* residual, const void* gamma
 
 // ---------------------------------------------------------------------------
 size_t mx_quant_matmul_inplace_add_workspace_size(int64_t m, int64_t k, int64_t n) {
-  (void)m;
-  (void)k;
-  (void)n;
-  return 0;
+  return wq::mx_x1pad_bytes(m, k, n);
 }
 
 wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout x2_layout,
@@ -333,8 +330,6 @@ wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout 
                                       int transpose_x2, int64_t group_size, float* y,
                                       void* workspace, size_t workspace_size,
                                       hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_size;
   // Constraints: only transposeX1 = true, transposeX2 = false.
   if (transpose_x1 != 1 || transpose_x2 != 0) return WQ_ERR_UNSUPPORTED;
   if (x2_layout != WQ_LAYOUT_GFX950_B) return WQ_ERR_UNSUPPORTED;
@@ -359,8 +354,21 @@ wq_status mx_quant_matmul_inplace_add(const void* x1, const void* x2, wq_layout 
       overlap(y, ybytes, x2, wq_pack_int4_bytes(k, n, WQ_LAYOUT_GFX950_B)) ||
       overlap(y, ybytes, x1_scale, (size_t)(m * kb)) || overlap(y, ybytes, x2_scale, (size_t)(kb * n)))
     return WQ_ERR_ALIAS;
+  // the workspace is optional: with one of the queried size, shapes whose m
+  // is not a multiple of 16 run on the large tile over a padded copy of x1
+  const size_t need = wq::mx_x1pad_bytes(m, k, n);
+  uint8_t* pad = nullptr;
+  if (need > 0 && workspace && workspace_size >= need) {
+    if (!aligned16(workspace)) return WQ_ERR_SHAPE;
+    if (overlap(workspace, need, y, ybytes) || overlap(workspace, need, x1, (size_t)(k * m)) ||
+        overlap(workspace, need, x2, wq_pack_int4_bytes(k, n, WQ_LAYOUT_GFX950_B)) ||
+        overlap(workspace, need, x1_scale, (size_t)(m * kb)) ||
+        overlap(workspace, need, x2_scale, (size_t)(kb * n)))
+      return WQ_ERR_ALIAS;
+    pad = static_cast<uint8_t*>(workspace);
+  }
   wq::MxProblem p{static_cast<const uint8_t*>(x1), static_cast<const uint8_t*>(x2), x1_scale,
-                  x2_scale, y, m, k, n};
+                  x2_scale, y, m, k, n, pad};
   return from_hip(wq::launch_mx_matmul(p, stream));
 }
 

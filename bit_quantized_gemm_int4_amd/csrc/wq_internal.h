@@ -90,8 +90,13 @@ struct MxProblem {
   const uint8_t* s2;     // (kb, n)
   float* y;
   int64_t m, k, n;
+  uint8_t* x1pad;        // null, or mx_x1pad_bytes(m, k, n) bytes for x1 with rows padded to 16
 };
 
+// Workspace the MX GEMM can use when m is not a multiple of 16: x1 copied to
+// (k, 16 ceil(m / 16)) so that the 256 x 256 tile can take the shape; 0 when
+// the shape needs none (or cannot take the tile anyway).
+size_t mx_x1pad_bytes(int64_t m, int64_t k, int64_t n);
 hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s);
 
 struct I8Problem {

@@ -61,6 +61,11 @@ def test_size_queries():
     ws = wq.wq_matmul_add_rmsnorm_workspace_size(4096, 8192, 8192)
     assert ws >= 4096 * (8192 // 32) * 4
     assert wq.mx_quant_matmul_inplace_add_workspace_size(4096, 8192, 4096) == 0
+    # m % 16 != 0: room for x1 with rows padded to 16 bytes (k x 16 ceil(m/16)), 256-byte rounded
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(4100, 8192, 4100) == 8192 * 4112
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(33, 7, 17) == 0          # n % 4: small tile
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(33, 7, 16) == 512        # 7 x 48 = 336 -> 512
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(0, 7, 16) == 0
 
 
 def _pack(**kw):
@@ -196,11 +201,12 @@ def test_noalloc_validation_without_a_device():
 
 def _mx(**kw):
     a = dict(x1=FAKE, x2=FAKE2, layout=wq.WQ_LAYOUT_GFX950_B, s1=FAKE3, s2=FAKE3 + 0x10000,
-             m=64, k=256, n=64, t1=1, t2=0, group=wq.MX_GROUP_SIZE, y=FAKE3 + 0x100000)
+             m=64, k=256, n=64, t1=1, t2=0, group=wq.MX_GROUP_SIZE, y=FAKE3 + 0x100000, ws=None,
+             wsn=0)
     a.update(kw)
     return wq.lib().mx_quant_matmul_inplace_add(a["x1"], a["x2"], a["layout"], a["s1"], a["s2"],
                                                 a["m"], a["k"], a["n"], a["t1"], a["t2"],
-                                                a["group"], a["y"], None, 0, 0)
+                                                a["group"], a["y"], a["ws"], a["wsn"], 0)
 
 
 def test_mx_matmul_validation():
@@ -220,6 +226,12 @@ def test_mx_matmul_validation():
     assert _mx(s1=FAKE3 + 1) == wq.WQ_ERR_SHAPE
     assert _mx(s2=FAKE3 + 0x10002) == wq.WQ_ERR_SHAPE
     assert _mx(m=0) == wq.WQ_OK and _mx(k=0) == wq.WQ_OK
+    # the optional workspace (m % 16 != 0): checked only when it is large enough to be used
+    need = wq.mx_quant_matmul_inplace_add_workspace_size(60, 256, 64)
+    assert need == 256 * 64
+    assert _mx(m=60, ws=FAKE3 + 0x200008, wsn=need) == wq.WQ_ERR_SHAPE         # misaligned
+    assert _mx(m=60, ws=FAKE3 + 0x100000, wsn=need) == wq.WQ_ERR_ALIAS         # over y
+    assert _mx(m=60, ws=FAKE + 0x10, wsn=need) == wq.WQ_ERR_ALIAS              # over x1
 
 
 def _qmm(**kw):

@@ -88,8 +88,10 @@ def _codes(rng, k, m, n, s_lo=118, s_hi=134):
 # (256, 1024, 256) .. (768, 2048, 256) take the 256 x 256 tile with one, three
 # (odd) and many 128-deep steps; the next ones take its ragged variant: a K
 # tail (the last step reads past K: 7, 200, 1000 and 1056 deep), M and N not
-# multiples of 256 (a last tile row / column mostly outside the output); (300,
-# 256, 300) has M % 16 != 0 (the small tile)
+# multiples of 256 (a last tile row / column mostly outside the output); with
+# M % 16 != 0 ((70, 80, 20), (130, 416, 96), (300, 256, 300)) the binding
+# passes the queried workspace and the tile runs on a padded copy of x1; N % 4
+# != 0 ((33, 7, 17), (1, 32, 2)) takes the small tile
 @pytest.mark.parametrize("m,k,n", [(64, 128, 64), (16, 256, 16), (70, 80, 20), (130, 416, 96),
                                    (1, 32, 2), (33, 7, 17), (256, 1024, 256), (256, 128, 512),
                                    (512, 384, 768), (768, 2048, 256),
@@ -134,6 +136,30 @@ def test_codes_inside_the_alignment_windows_are_exact(m, k, n):
     want = oracle.mx_quant_matmul_inplace_add(x1, x2, s1, s2, y)
     assert np.all(want * 64 == np.round(want * 64)) and np.all(np.abs(want) < 2 ** 17)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("m,k,n", [(300, 256, 300), (70, 200, 20)])
+def test_without_workspace_the_small_tile_gives_the_same_y(m, k, n):
+    # m % 16 != 0 and no workspace: the small tile; with the queried workspace
+    # the large tile on a padded copy of x1. Both within the bound of the
+    # MFMA's accumulation against the oracle.
+    rng = np.random.default_rng(m + 7 * k + n)
+    x1, x2, s1, s2 = _codes(rng, k, m, n)
+    y = rng.standard_normal((m, n)).astype(np.float32)
+    want = oracle.mx_quant_matmul_inplace_add(x1, x2, s1, s2, y.astype(np.float64))
+    bound = _mfma_bound(x1, x2, s1, s2, y.astype(np.float64))
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(m, k, n) > 0
+    x2p = wq.pack_int4(torch.from_numpy(x2.astype(np.int32)).to(DEV), wq.WQ_LAYOUT_GFX950_B)
+    args = [torch.from_numpy(x1).to(DEV), x2p, torch.from_numpy(s1).to(DEV), torch.from_numpy(s2).to(DEV)]
+    note(f"mx without workspace {m}x{k}x{n}")
+    yd = torch.from_numpy(y).to(DEV)
+    wq.mx_quant_matmul_inplace_add(args[0], args[1], wq.WQ_LAYOUT_GFX950_B, args[2], args[3], m, k, n,
+                                   1, 0, wq.MX_GROUP_SIZE, yd, None, 0)
+    torch.cuda.synchronize()
+    got = yd.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - want) <= bound)
+    got_ws = _run(x1, x2, s1, s2, y)
+    assert np.all(np.abs(got_ws - want) <= bound)
 
 
 def test_group_size_zero_same_as_explicit():
