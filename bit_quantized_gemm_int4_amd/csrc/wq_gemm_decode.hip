@@ -1,6 +1,7 @@
 // Decode-shaped weight-quantized GEMM (m <= 32) for INT4 weights in the
-// GFX950_B layout, any group the pages allow (a multiple of 32 along K, or
-// per channel / per tensor), k a multiple of 128. Same operator as wq_gemm.hip
+// GFX950_B layout or INT8 weights stored transposed (n, k), any group the
+// pages allow (a multiple of 32 along K, or per channel / per tensor), k a
+// multiple of 128. Same operator as wq_gemm.hip
 // (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula); the RMSNorm
 // finish runs as the next launch (rmsnorm_finish), which on this GPU costs
 // less than any in-kernel grid synchronization: every cross-XCD handoff
@@ -42,6 +43,15 @@
 // accumulator sets and is folded while the next unit's MFMAs run; its scale
 // and offset, loaded by the lanes of one row, reach the other rows by the
 // same swaps.
+//
+// INT8 weights (W8, the transposed (n, k) layout: each column's K values
+// contiguous) take the same path with 32 bytes per lane and block: lane row
+// R loads K values 32 R .. + 31 of its column (two 16-byte loads), i.e. the
+// layout of a GFX950_B sub-block at one byte per code, and step j uses its
+// dwords 2 j and 2 j + 1. fp16 codes enter as q + 1152 (the byte with its
+// sign bit flipped under the exponent byte 0x64: 1024 + q + 128, exact), the
+// constant folded per block like the INT4 one; bf16 codes enter as q
+// (converted through float32, exact for |q| <= 128).
 //
 // Epilogue: y = acc + bias + residual (stored rounded to the activation
 // dtype) and, per (workgroup, row), the sum of the float32 y^2 over the
@@ -85,21 +95,50 @@ constexpr int acc_sets() { return SPG == 4 ? 1 : 2; }
 template <int CTW>
 struct DecodeLane {
   __amdgpu_buffer_rsrc_t w, x, s, o;
-  uint32_t woff[CTW];        // lane's 16 weight bytes in a K block, per column tile
+  uint32_t woff[CTW];        // lane's first weight byte in block 0, per column tile
   uint32_t xoff;             // x1 row l%16, first K fragment of the lane (BUF_OOB for rows >= m)
   uint32_t soff[CTW];        // lane's scale element per tile (columns clamped to n - 1)
 };
 
 // One 128-deep block's register loads (its x1 fragments go to LDS).
-template <int CTW>
+template <int CTW, bool W8>
 struct DecodeBatch {
-  u32x4 w[CTW];              // packed codes: dword w4 feeds K step w4
-  uint32_t s[CTW], o[CTW];   // raw 16-bit scale and offset
+  u32x4 w[W8 ? 2 * CTW : CTW];   // INT4: dword w4 of tile c feeds K step w4; INT8: tile c in w[2c], w[2c + 1]
+  uint32_t s[CTW], o[CTW];       // raw 16-bit scale and offset
 };
 
 // vector-memory instructions one batch issues
-template <int CTW>
-constexpr int batch_loads() { return CTW + 4 + 2 * CTW; }
+template <int CTW, bool W8>
+constexpr int batch_loads() { return (W8 ? 2 : 1) * CTW + 4 + 2 * CTW; }
+
+// The constant the 16-bit operand adds to a code: INT4 q + 136 / q + 1032
+// (unpack8_low), INT8 q + 1152 in fp16, q itself in bf16.
+template <int ACT, bool W8>
+constexpr float code_bias() {
+  return W8 ? (ACT == ACT_F16 ? 1152.f : 0.f) : UnpackLow<ACT>::bias;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight INT8 codes (lo: K 0..3, hi: K 4..7, K ascending from the low byte)
+// -> the MFMA operand of one step.
+template <int ACT>
+__device__ __forceinline__ u32x4 i8_operand(uint32_t lo, uint32_t hi) {
+  if constexpr (ACT == ACT_F16) {
+    const uint32_t ul = lo ^ 0x80808080u, uh = hi ^ 0x80808080u;
+    return (u32x4){__builtin_amdgcn_perm(0x64646464u, ul, 0x04010400u),
+                   __builtin_amdgcn_perm(0x64646464u, ul, 0x04030402u),
+                   __builtin_amdgcn_perm(0x64646464u, uh, 0x04010400u),
+                   __builtin_amdgcn_perm(0x64646464u, uh, 0x04030402u)};
+  } else {
+    auto pair = [](uint32_t w, int j) {
+      const f32x2 f = {(float)(int)(int8_t)(w >> (8 * j)), (float)(int)(int8_t)(w >> (8 * j + 8))};
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    };
+    return (u32x4){pair(lo, 0), pair(lo, 2), pair(hi, 0), pair(hi, 2)};
+  }
+}
 
 // Loop-carried MFMA accumulators of a wave: the block's partial sums per
 // column tile and the block's row sums of x. Every MFMA updates them in
@@ -129,13 +168,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, ui
 // loads the scale and offset of fold unit R / SPG: group
 // floor((unit + 1/2) / upg) with upg fold units per group, exact in float32
 // for every unit index below 2^11 (k < 2^16).
-template <int CTW, int SPG>
+template <int CTW, int SPG, bool W8>
 __device__ __forceinline__ void issue_batch(const DecodeArgs& a, const DecodeLane<CTW>& ln, int kb,
-                                            uint8_t* xs, DecodeBatch<CTW>& b) {
-  const uint32_t wso = (uint32_t)kb * (uint32_t)a.np * 64u;
+                                            uint8_t* xs, DecodeBatch<CTW, W8>& b) {
+  if constexpr (W8) {
+    const uint32_t wso = (uint32_t)kb * 128u;
 #pragma unroll
-  for (int c = 0; c < CTW; ++c)
-    b.w[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c], wso, 0));
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        b.w[2 * c + h] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c] + 16u * h, wso, 0));
+  } else {
+    const uint32_t wso = (uint32_t)kb * (uint32_t)a.np * 64u;
+#pragma unroll
+    for (int c = 0; c < CTW; ++c)
+      b.w[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c], wso, 0));
+  }
   constexpr uint32_t xstep = SPG == 4 ? 16u : 64u;
 #pragma unroll
   for (int w4 = 0; w4 < 4; ++w4)
@@ -196,13 +245,48 @@ __device__ __forceinline__ float bcast_unit(float v) {
   return __builtin_bit_cast(float, x);
 }
 
-template <int ACT, int CTW, int SPG>
-__device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch<CTW>& b, const uint8_t* xs,
+// The per-step weight words of one tile: INT4 one dword per step (src.x ..
+// src.w), INT8 two (lo[j], hi[j]); with short groups transposed across lane
+// rows so that step j holds 32-deep sub-block j in every row.
+template <bool W8>
+struct StepWords {
+  u32x4 lo, hi;    // hi unused for INT4
+};
+
+template <int SPG, bool W8>
+__device__ __forceinline__ StepWords<W8> step_words(const u32x4* w) {
+  StepWords<W8> r;
+  if constexpr (W8) {
+    r.lo = (u32x4){w[0].x, w[0].z, w[1].x, w[1].z};
+    r.hi = (u32x4){w[0].y, w[0].w, w[1].y, w[1].w};
+    if constexpr (SPG < 4) {
+      r.lo = transpose_rows(r.lo);
+      r.hi = transpose_rows(r.hi);
+    }
+  } else {
+    r.lo = SPG == 4 ? w[0] : transpose_rows(w[0]);
+  }
+  return r;
+}
+
+template <int ACT, bool W8>
+__device__ __forceinline__ u32x4 step_operand(const StepWords<W8>& sw, int j) {
+  if constexpr (W8) return i8_operand<ACT>(sw.lo[j], sw.hi[j]);
+  else return unpack8_low<ACT>(sw.lo[j]);
+}
+
+template <int ACT, int CTW, int SPG, bool W8>
+__device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch<CTW, W8>& b, const uint8_t* xs,
                                           DecodeAcc<CTW, acc_sets<SPG>()>& ma, f32x4 (&acc)[CTW]) {
   constexpr int U = fold_units<SPG>();
+  constexpr int WPT = W8 ? 2 : 1;            // weight registers per tile
+  constexpr float BIAS = code_bias<ACT, W8>();
   const int lane = threadIdx.x & 63;
   const uint32_t one2 = pack2<ACT>(1.f, 1.f);
   const u32x4 ones = {one2, one2, one2, one2};
+  StepWords<W8> w[CTW];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) w[c] = step_words<SPG, W8>(&b.w[WPT * c]);
   if constexpr (SPG == 4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ma.rs[0][i] *= 0.f;
@@ -215,7 +299,7 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
       const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
       ma.rs[0] = mfma16<ACT>(av, ones, ma.rs[0]);
 #pragma unroll
-      for (int c = 0; c < CTW; ++c) ma.part[0][c] = mfma16<ACT>(av, unpack8_low<ACT>(b.w[c][w4]), ma.part[0][c]);
+      for (int c = 0; c < CTW; ++c) ma.part[0][c] = mfma16<ACT>(av, step_operand<ACT, W8>(w[c], w4), ma.part[0][c]);
       // one K step's operands at a time (bounds the live unpacked fragments)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -223,7 +307,7 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
     for (int c = 0; c < CTW; ++c) {
       const float s = to_f32<ACT>((uint16_t)b.s[c]);
       const float o = to_f32<ACT>((uint16_t)b.o[c]) * a.omul;
-      const float cc = o - UnpackLow<ACT>::bias * s;
+      const float cc = o - BIAS * s;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[0][c][i], fmaf(cc, ma.rs[0][i], acc[c][i]));
     }
@@ -233,11 +317,8 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
       sr[c] = to_f32<ACT>((uint16_t)b.s[c]);
-      cr[c] = to_f32<ACT>((uint16_t)b.o[c]) * a.omul - UnpackLow<ACT>::bias * sr[c];
+      cr[c] = to_f32<ACT>((uint16_t)b.o[c]) * a.omul - BIAS * sr[c];
     }
-    u32x4 w[CTW];
-#pragma unroll
-    for (int c = 0; c < CTW; ++c) w[c] = transpose_rows(b.w[c]);
     // unit u accumulates into set u % 2 and is folded after unit u + 1's
     // MFMAs are issued, so the fold does not wait on its own MFMAs
 #pragma unroll
@@ -256,7 +337,7 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
           ma.rs[st] = mfma16<ACT>(av, ones, ma.rs[st]);
 #pragma unroll
           for (int c = 0; c < CTW; ++c)
-            ma.part[st][c] = mfma16<ACT>(av, unpack8_low<ACT>(w[c][w4]), ma.part[st][c]);
+            ma.part[st][c] = mfma16<ACT>(av, step_operand<ACT, W8>(w[c], w4), ma.part[st][c]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -281,7 +362,7 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
   }
 }
 
-template <int ACT, int CTW, int SPG>
+template <int ACT, int CTW, int SPG, bool W8>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_decode(DecodeArgs a) {
   constexpr int RS = CTW * 16 + 4;                  // reduction row stride (floats)
   // per wave: two 4 KiB x1 slots, reused after the K loop for the wave's
@@ -310,7 +391,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
     const int64_t ct = ct0 + c < a.nct ? ct0 + c : a.nct - 1;
-    ln.woff[c] = (uint32_t)((ct * 16 + col) * 64 + kq * 16);
+    // INT4: the GFX950_B record's sub-block kq; INT8: 32 bytes of column
+    // row (n, k), past n out of the weight (reads zeros)
+    ln.woff[c] = W8 ? (uint32_t)((ct * 16 + col) * a.k + kq * 32) : (uint32_t)((ct * 16 + col) * 64 + kq * 16);
     const int64_t sc = n0 + 16 * c + col < a.n ? n0 + 16 * c + col : a.n - 1;
     ln.soff[c] = (uint32_t)(sc * a.s_col * 2);
   }
@@ -359,23 +442,23 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   // ahead of the first use.
   uint8_t* xa = xlds[wave][0];
   uint8_t* xb = xlds[wave][1];
-  DecodeBatch<CTW> ba, bb;
-  if (kb0 < kb1) issue_batch<CTW, SPG>(a, ln, kb0, xa, ba);
+  DecodeBatch<CTW, W8> ba, bb;
+  if (kb0 < kb1) issue_batch<CTW, SPG, W8>(a, ln, kb0, xa, ba);
   for (int kb = kb0; kb < kb1; kb += 2) {
-    if (kb + 1 < kb1) issue_batch<CTW, SPG>(a, ln, kb + 1, xb, bb);
+    if (kb + 1 < kb1) issue_batch<CTW, SPG, W8>(a, ln, kb + 1, xb, bb);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 1 < kb1) wait_vm<batch_loads<CTW>()>();
+    if (kb + 1 < kb1) wait_vm<batch_loads<CTW, W8>()>();
     else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
-    mma_batch<ACT, CTW, SPG>(a, ba, xa, ma, acc);
+    mma_batch<ACT, CTW, SPG, W8>(a, ba, xa, ma, acc);
     __builtin_amdgcn_sched_barrier(0);
     if (kb + 1 >= kb1) break;
-    if (kb + 2 < kb1) issue_batch<CTW, SPG>(a, ln, kb + 2, xa, ba);
+    if (kb + 2 < kb1) issue_batch<CTW, SPG, W8>(a, ln, kb + 2, xa, ba);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 2 < kb1) wait_vm<batch_loads<CTW>()>();
+    if (kb + 2 < kb1) wait_vm<batch_loads<CTW, W8>()>();
     else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
-    mma_batch<ACT, CTW, SPG>(a, bb, xb, ma, acc);
+    mma_batch<ACT, CTW, SPG, W8>(a, bb, xb, ma, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -423,22 +506,30 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   }
 }
 
-template <int ACT>
-void launch_act(const DecodeArgs& a, int spg, int ctw, unsigned grid, hipStream_t s) {
-  prof_begin(s);
+template <int ACT, bool W8>
+void launch_fmt(const DecodeArgs& a, int spg, int ctw, unsigned grid, hipStream_t s) {
   if (spg == 4) {
     switch (ctw) {
-      case 1: gemm_decode<ACT, 1, 4><<<dim3(grid), 1024, 0, s>>>(a); break;
-      case 2: gemm_decode<ACT, 2, 4><<<dim3(grid), 1024, 0, s>>>(a); break;
-      default: gemm_decode<ACT, 3, 4><<<dim3(grid), 1024, 0, s>>>(a); break;
+      case 1: gemm_decode<ACT, 1, 4, W8><<<dim3(grid), 1024, 0, s>>>(a); break;
+      case 2: gemm_decode<ACT, 2, 4, W8><<<dim3(grid), 1024, 0, s>>>(a); break;
+      default:
+        if constexpr (!W8) gemm_decode<ACT, 3, 4, W8><<<dim3(grid), 1024, 0, s>>>(a);
+        break;
     }
   } else if (spg == 2) {
-    if (ctw == 1) gemm_decode<ACT, 1, 2><<<dim3(grid), 1024, 0, s>>>(a);
-    else gemm_decode<ACT, 2, 2><<<dim3(grid), 1024, 0, s>>>(a);
+    if (W8 || ctw == 1) gemm_decode<ACT, 1, 2, W8><<<dim3(grid), 1024, 0, s>>>(a);
+    else if constexpr (!W8) gemm_decode<ACT, 2, 2, W8><<<dim3(grid), 1024, 0, s>>>(a);
   } else {
-    if (ctw == 1) gemm_decode<ACT, 1, 1><<<dim3(grid), 1024, 0, s>>>(a);
-    else gemm_decode<ACT, 2, 1><<<dim3(grid), 1024, 0, s>>>(a);
+    if (W8 || ctw == 1) gemm_decode<ACT, 1, 1, W8><<<dim3(grid), 1024, 0, s>>>(a);
+    else if constexpr (!W8) gemm_decode<ACT, 2, 1, W8><<<dim3(grid), 1024, 0, s>>>(a);
   }
+}
+
+template <int ACT>
+void launch_act(const DecodeArgs& a, bool w8, int spg, int ctw, unsigned grid, hipStream_t s) {
+  prof_begin(s);
+  if (w8) launch_fmt<ACT, true>(a, spg, ctw, grid, s);
+  else launch_fmt<ACT, false>(a, spg, ctw, grid, s);
   prof_end(s);
 }
 
@@ -450,41 +541,49 @@ int decode_spg(const WqProblem& p) {
 }
 
 // column tiles per workgroup: keep the grid within one workgroup per CU up to
-// 768 tiles (n = 12288); wider layers take more workgroups of 3. The second
-// accumulator set of short groups caps the tiles at 2 within the register
-// budget of 16 waves per CU.
-int decode_ctw(int64_t nct, int spg) {
+// 768 tiles (n = 12288); wider layers take more workgroups of 3. Within the
+// register budget of 16 waves per CU, the second accumulator set of short
+// groups caps the tiles at 2, the INT8 weights' doubled registers at 2, both
+// together at 1.
+int decode_ctw(int64_t nct, int spg, bool w8) {
   const int ctw = nct <= 256 ? 1 : nct <= 512 ? 2 : 3;
-  const int cap = spg == 4 ? 3 : 2;
+  const int cap = spg == 4 ? (w8 ? 2 : 3) : (w8 ? 1 : 2);
   return ctw < cap ? ctw : cap;
 }
 
+bool decode_w8(const WqProblem& p) { return p.w_bits == 8; }
+
 }  // namespace
 
-// INT4 in the GFX950_B layout, k a multiple of 128, m <= 32. The weight
-// stream addresses the packed weight through one buffer resource whose
-// out-of-range offset is 2^31: the weight must stay below 2 GiB.
+// INT4 in the GFX950_B layout or INT8 stored (n, k), k a multiple of 128,
+// m <= 32. The weight stream addresses the weight through one buffer
+// resource whose out-of-range offset is 2^31: the weight (with the INT8
+// columns of a partial last tile) must stay below 2 GiB.
 bool decode_ok(const WqProblem& p) {
-  if (p.w_bits != 4 || p.layout != WQ_LAYOUT_GFX950_B || p.k % 128 != 0 || p.m > 32) return false;
+  if (p.k % 128 != 0 || p.m > 32) return false;
   if (p.group < p.k && p.group % 32 != 0) return false;
-  return (p.k / 128) * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
+  const int64_t np = 16 * ((p.n + 15) / 16);
+  if (p.w_bits == 4 && p.layout == WQ_LAYOUT_GFX950_B) return (p.k / 128) * np * 64 < (int64_t(1) << 31);
+  if (p.w_bits == 8 && p.transpose_x2) return np * p.k < (int64_t(1) << 31);
+  return false;
 }
 
 // Per-(row, workgroup) sums of y^2 of the decode kernel: [32][grid] at most.
 int64_t decode_grid(const WqProblem& p) {
   const int64_t nct = (p.n + 15) / 16;
-  const int ctw = decode_ctw(nct, decode_spg(p));
+  const int ctw = decode_ctw(nct, decode_spg(p), decode_w8(p));
   return (nct + ctw - 1) / ctw;
 }
 size_t decode_partial_bytes(int64_t n) {
-  // the largest grid over the fold shapes
+  // the largest grid over the fold shapes and weight formats
   const int64_t nct = (n + 15) / 16;
   int64_t grid = 0;
-  for (int spg = 1; spg <= 4; spg *= 2) {
-    const int ctw = decode_ctw(nct, spg);
-    const int64_t g = (nct + ctw - 1) / ctw;
-    grid = g > grid ? g : grid;
-  }
+  for (int w8 = 0; w8 < 2; ++w8)
+    for (int spg = 1; spg <= 4; spg *= 2) {
+      const int ctw = decode_ctw(nct, spg, w8 != 0);
+      const int64_t g = (nct + ctw - 1) / ctw;
+      grid = g > grid ? g : grid;
+    }
   return (size_t)(grid * 32 * 4);
 }
 
@@ -512,18 +611,19 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   a.s_row = p.s_row;
   a.s_col = p.s_col;
   a.x1_bytes = (uint32_t)(p.m * p.k * 2);
-  a.x2_bytes = (uint32_t)(p.k / 128 * a.np * 64);
+  const bool w8 = decode_w8(p);
+  a.x2_bytes = w8 ? (uint32_t)(p.n * p.k) : (uint32_t)(p.k / 128 * a.np * 64);
   a.s_bytes = (uint32_t)(((groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
   a.res_bytes = (uint32_t)(p.m * p.n * 2);
   const int64_t kbs = p.k / 128;
   a.kpw = (int32_t)((kbs + DC_WAVES - 1) / DC_WAVES);
-  const int ctw = decode_ctw(a.nct, spg);
+  const int ctw = decode_ctw(a.nct, spg, w8);
   const unsigned grid = (unsigned)decode_grid(p);
   // one launch per 16 rows (m <= 32: at most two; the second finds the
   // weights in the last-level cache)
   for (a.row0 = 0; a.row0 < p.m; a.row0 += 16) {
-    if (p.bf16) launch_act<ACT_BF16>(a, spg, ctw, grid, s);
-    else launch_act<ACT_F16>(a, spg, ctw, grid, s);
+    if (p.bf16) launch_act<ACT_BF16>(a, w8, spg, ctw, grid, s);
+    else launch_act<ACT_F16>(a, w8, spg, ctw, grid, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

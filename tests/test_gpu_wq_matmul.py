@@ -122,6 +122,31 @@ W8 = [  # m, k, n, granularity, group, offset, bias, act: the INT8 64 x 64 tile
 ]
 
 
+W8_DECODE = [  # m <= 32, INT8 stored (n, k), k % 128 == 0: the weight stream
+    (1, 4096, 11008, "channel", 0, (-0.5, 0.5), 0.1, torch.bfloat16),
+    (16, 1024, 520, "group", 128, (-1.0, 1.0), 0.1, torch.float16),
+    (5, 2048, 300, "group", 64, (-1.0, 1.0), None, torch.bfloat16),
+    (9, 512, 777, "group", 32, (-0.5, 0.5), 0.1, torch.bfloat16),
+    (32, 768, 1000, "group", 96, "none", 0.1, torch.float16),
+    (3, 1152, 130, "group", 384, (-1.0, 1.0), 0.1, torch.float16),
+    (21, 256, 16, "tensor", 0, (-0.5, 0.5), 0.1, torch.bfloat16),
+    (2, 4096, 9000, "group", 128, None, 0.1, torch.float16),
+]
+
+
+@pytest.mark.parametrize("shape", W8_DECODE, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in W8_DECODE])
+def test_int8_decode_shapes(shape):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"w8dec{m}x{k}x{n}", m, k, n, act=act, w_bits=8, granularity=gran,
+                          group_size=g, scale_range=(0.001, 0.01), offset_range=off,
+                          bias_std=bias, seed=11 * m + k + n)
+    note(f"wq int8 decode {c.name} {gran} g={g} {act}")
+    y, nrm = wq_on_gpu(c, transpose_x2=True)
+    check_wq(c, y, nrm)
+    y2, n2 = wq_on_gpu(c, transpose_x2=True, inplace=True)
+    assert torch.equal(y, y2) and torch.equal(nrm, n2)
+
+
 @pytest.mark.parametrize("shape", W8, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in W8])
 @pytest.mark.parametrize("transpose", [False, True])
 def test_int8_tile_shapes(shape, transpose):
@@ -138,14 +163,16 @@ def test_int8_tile_shapes(shape, transpose):
 
 @pytest.mark.parametrize("act", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("transpose", [False, True])
-@pytest.mark.parametrize("k,G", [(256, 32), (320, 64), (512, 0)])
-def test_int8_integer_valued_y_is_bit_exact(act, transpose, k, G):
+@pytest.mark.parametrize("k,G,m", [(256, 32, 36), (320, 64, 36), (512, 0, 36), (256, 32, 20), (512, 0, 20),
+                                   (384, 64, 20)])
+def test_int8_integer_valued_y_is_bit_exact(act, transpose, k, G, m):
     # x1 rows one-hot with sign +-1 (rows 0..3 on K = 0 and 1, where the
     # codes are -128 and 127), INT8 codes over the whole range, scale 1, no
     # offset, zero bias, integer residual: y = +-q[p, :] + residual, integers
-    # with |y| <= 132, exact in fp16 and bf16
-    m, n = 36, 72
-    rng = np.random.default_rng(7 * k + G + transpose)
+    # with |y| <= 132, exact in fp16 and bf16. m = 20 with a transposed weight
+    # and k % 128 == 0 takes the weight stream (codes as q + 1152 in fp16)
+    n = 72
+    rng = np.random.default_rng(7 * k + G + transpose + m)
     pos = rng.integers(0, k, m)
     pos[:4] = [0, 1, 0, 1]
     sign = rng.choice([-1.0, 1.0], m)
@@ -404,9 +431,12 @@ ONE_SIGN = [  # m, k, n, granularity, group, offset, act
     (1, 8192, 1024, "channel", 0, (-0.1, 0.1), torch.float16),
     (40, 8192, 256, "group", 64, None, torch.float16),          # generic tile (group 64)
 ]
-ONE_SIGN_W8 = [  # the INT8 tile: one group over all of K, and group 64
+ONE_SIGN_W8 = [  # the INT8 tile: one group over all of K, and group 64; m <= 32 the
+    # weight stream when transposed
     (130, 8192, 520, "channel", 0, None, torch.float16),
     (64, 8192, 256, "group", 64, (-0.1, 0.1), torch.bfloat16),
+    (16, 8192, 1024, "channel", 0, None, torch.float16),
+    (16, 8192, 1024, "group", 128, (-0.1, 0.1), torch.bfloat16),
 ]
 
 
