@@ -18,10 +18,10 @@
 // K; CTW grows with n so that up to n = 12288 the grid stays within one
 // workgroup per CU. Its waves split K: wave w takes 128-deep blocks
 // [w*kpw, (w+1)*kpw), two blocks in flight: the loads of block b + 1
-// (weights first, then the x1 fragments by buffer -> LDS DMA into one of the
-// wave's two LDS slots, then one scale / offset pair per column) are issued
-// before block b is multiplied. The waves' sums meet in LDS and are added in
-// a fixed wave order.
+// (weights first, then the x1 rows by buffer -> LDS DMA into one of the
+// wave's two LDS slots, one instruction per four rows of the launch, then
+// the scales and offsets) are issued before block b is multiplied. The
+// waves' sums meet in LDS and are added in a fixed wave order.
 //
 // Arithmetic per 128-deep block: the codes enter the MFMA as 16-bit
 // B = q + 136 (fp16: q + 1032; wq_unpack.h, unpack8_low), one more MFMA
@@ -92,12 +92,12 @@ constexpr int fold_units() { return 4 / SPG; }
 template <int SPG>
 constexpr int acc_sets() { return SPG == 4 ? 1 : 2; }
 
-template <int CTW>
+template <int CTW, int XD>
 struct DecodeLane {
   __amdgpu_buffer_rsrc_t w, x, s, o;
   uint32_t woff[CTW];        // lane's first weight byte in block 0, per column tile
-  uint32_t xoff;             // x1 row l%16, first K fragment of the lane (BUF_OOB for rows >= m)
-  uint32_t soff[CTW];        // lane's scale element per tile (columns clamped to n - 1)
+  uint32_t xoff[XD];         // x1 bytes the lane fetches in DMA d of a block (BUF_OOB past m)
+  uint32_t soff[CTW];        // scale element per tile (SPG = 4: [0] only, tile of the lane row)
 };
 
 // One 128-deep block's register loads (its x1 fragments go to LDS).
@@ -107,9 +107,10 @@ struct DecodeBatch {
   uint32_t s[CTW], o[CTW];       // raw 16-bit scale and offset
 };
 
-// vector-memory instructions one batch issues
-template <int CTW, bool W8>
-constexpr int batch_loads() { return (W8 ? 2 : 1) * CTW + 4 + 2 * CTW; }
+// vector-memory instructions one batch issues: weights, XD x1 DMAs, scales
+// and offsets (SPG = 4: one of each, lane row R holding tile R's)
+template <int CTW, int SPG, bool W8, int XD>
+constexpr int batch_loads() { return (W8 ? 2 : 1) * CTW + XD + (SPG == 4 ? 2 : 2 * CTW); }
 
 // The constant the 16-bit operand adds to a code: INT4 q + 136 / q + 1032
 // (unpack8_low), INT8 q + 1152 in fp16, q itself in bf16.
@@ -157,19 +158,26 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
+// x1 staging. A block's x1 slot holds row r's 128 K values (sixteen 16-byte
+// chunks, chunk j = K values 8 j .. + 7) at xs + 256 r, chunk j in slot
+// j ^ r, so the sixteen rows of one MFMA operand read hit distinct banks.
+// DMA d fetches rows 4 d .. 4 d + 3 (a DMA instruction writes its 64 lanes'
+// 16 bytes in lane order: lane i lands in row 4 d + i/16, slot i%16, so it
+// fetches chunk (i%16) ^ row). XD = ceil(rows / 4) DMAs: rows past the
+// launch's last are not fetched, and their MFMA output rows are discarded.
+//
 // K step w4 pairs the weight dword w4 of lane l (K values 32 (l/16) + 8 w4
 // .. + 7 of its column: the lane's GFX950_B sub-block) with the same eight K
-// values of x1 row l%16. That fragment sits at xs + 1024 w4 + 16 l: each DMA
-// instruction writes its 64 lanes' 16 bytes in lane order, so a lane reads
-// back exactly what it fetched.
+// values of x1 row l%16: chunk 4 (l/16) + w4. With SPG < 4 the weights are
+// transposed across lane rows and step w4 takes chunk 4 w4 + l/16.
 //
-// With SPG < 4 the fragment of step w4 is x1 K values 32 w4 + 8 (l/16) ..
-// + 7 (the transposed weights), i.e. offset xoff + 64 w4, and lane row R
-// loads the scale and offset of fold unit R / SPG: group
+// Scales: with SPG = 4 lane row R loads tile min(R, CTW - 1)'s scale and
+// offset, broadcast to the other rows at the fold. With SPG < 4 lane row R
+// loads the scale and offset of fold unit R / SPG for every tile: group
 // floor((unit + 1/2) / upg) with upg fold units per group, exact in float32
 // for every unit index below 2^11 (k < 2^16).
-template <int CTW, int SPG, bool W8>
-__device__ __forceinline__ void issue_batch(const DecodeArgs& a, const DecodeLane<CTW>& ln, int kb,
+template <int CTW, int SPG, bool W8, int XD>
+__device__ __forceinline__ void issue_batch(const DecodeArgs& a, const DecodeLane<CTW, XD>& ln, int kb,
                                             uint8_t* xs, DecodeBatch<CTW, W8>& b) {
   if constexpr (W8) {
     const uint32_t wso = (uint32_t)kb * 128u;
@@ -185,23 +193,30 @@ __device__ __forceinline__ void issue_batch(const DecodeArgs& a, const DecodeLan
     for (int c = 0; c < CTW; ++c)
       b.w[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, ln.woff[c], wso, 0));
   }
-  constexpr uint32_t xstep = SPG == 4 ? 16u : 64u;
 #pragma unroll
-  for (int w4 = 0; w4 < 4; ++w4)
-    dma16(ln.x, xs + 1024 * w4, ln.xoff + xstep * w4, (uint32_t)kb * 256u);
-  uint32_t vso = 0u, sso = 0u;
+  for (int d = 0; d < XD; ++d) dma16(ln.x, xs + 1024 * d, ln.xoff[d], (uint32_t)kb * 256u);
   if constexpr (SPG == 4) {
-    sso = (uint32_t)((kb / a.bpg) * a.s_row) * 2u;
+    const uint32_t sso = (uint32_t)((kb / a.bpg) * a.s_row) * 2u;
+    b.s[0] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[0], sso, 0);
+    b.o[0] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[0], sso, 0);
   } else {
     const int unit = kb * fold_units<SPG>() + (int)((threadIdx.x & 63) >> 4) / SPG;
     const uint32_t g = (uint32_t)(((float)unit + 0.5f) * a.upg_rcp);
-    vso = g * (uint32_t)a.s_row * 2u;
-  }
+    const uint32_t vso = g * (uint32_t)a.s_row * 2u;
 #pragma unroll
-  for (int c = 0; c < CTW; ++c) {
-    b.s[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[c] + vso, sso, 0);
-    b.o[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[c] + vso, sso, 0);
+    for (int c = 0; c < CTW; ++c) {
+      b.s[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.s, ln.soff[c] + vso, 0u, 0);
+      b.o[c] = __builtin_amdgcn_raw_buffer_load_b16(ln.o, ln.soff[c] + vso, 0u, 0);
+    }
   }
+}
+
+// Byte offset of lane l's x1 fragment for K step w4 in a block's slot.
+template <int SPG>
+__device__ __forceinline__ uint32_t x1_frag(int lane, int w4) {
+  const int r = lane & 15, kq = lane >> 4;
+  const int j = SPG == 4 ? 4 * kq + w4 : 4 * w4 + kq;
+  return (uint32_t)(256 * r + 16 * (j ^ r));
 }
 
 // Cross-row lane swaps (rows of 16 lanes, r0 .. r3), in the layout of the
@@ -296,17 +311,26 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
       for (int i = 0; i < 4; ++i) ma.part[0][c][i] *= 0.f;
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + x1_frag<SPG>(lane, w4));
       ma.rs[0] = mfma16<ACT>(av, ones, ma.rs[0]);
 #pragma unroll
       for (int c = 0; c < CTW; ++c) ma.part[0][c] = mfma16<ACT>(av, step_operand<ACT, W8>(w[c], w4), ma.part[0][c]);
       // one K step's operands at a time (bounds the live unpacked fragments)
       __builtin_amdgcn_sched_barrier(0);
     }
+    // lane row R loaded tile min(R, CTW - 1)'s scale and offset
+    const float s_r = to_f32<ACT>((uint16_t)b.s[0]);
+    const float o_r = to_f32<ACT>((uint16_t)b.o[0]) * a.omul;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
-      const float s = to_f32<ACT>((uint16_t)b.s[c]);
-      const float o = to_f32<ACT>((uint16_t)b.o[c]) * a.omul;
+      float s = s_r, o = o_r;
+      if constexpr (CTW > 1) {
+        switch (c) {   // unrolled: a constant row index
+          case 0: s = bcast_unit<1, 0>(s_r); o = bcast_unit<1, 0>(o_r); break;
+          case 1: s = bcast_unit<1, 1>(s_r); o = bcast_unit<1, 1>(o_r); break;
+          default: s = bcast_unit<1, 2>(s_r); o = bcast_unit<1, 2>(o_r); break;
+        }
+      }
       const float cc = o - BIAS * s;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[c][i] = fmaf(s, ma.part[0][c][i], fmaf(cc, ma.rs[0][i], acc[c][i]));
@@ -333,7 +357,7 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
           for (int i = 0; i < 4; ++i) ma.part[st][c][i] *= 0.f;
 #pragma unroll
         for (int w4 = u * SPG; w4 < (u + 1) * SPG; ++w4) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(xs + 1024 * w4 + 16 * lane);
+          const u32x4 av = *reinterpret_cast<const u32x4*>(xs + x1_frag<SPG>(lane, w4));
           ma.rs[st] = mfma16<ACT>(av, ones, ma.rs[st]);
 #pragma unroll
           for (int c = 0; c < CTW; ++c)
@@ -362,7 +386,7 @@ __device__ __forceinline__ void mma_batch(const DecodeArgs& a, const DecodeBatch
   }
 }
 
-template <int ACT, int CTW, int SPG, bool W8>
+template <int ACT, int CTW, int SPG, bool W8, int XD>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_decode(DecodeArgs a) {
   constexpr int RS = CTW * 16 + 4;                  // reduction row stride (floats)
   // per wave: two 4 KiB x1 slots, reused after the K loop for the wave's
@@ -379,24 +403,30 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 
   // Lane offsets: weight column 16 * tile + l%16 (tile clamped to the last
   // one; a partial last workgroup discards the repeats), 32-deep sub-block
-  // l/16; x1 row row0 + l%16 (rows >= m read zeros); scale column clamped to
-  // n - 1. Every offset a valid lane uses stays inside its buffer.
-  DecodeLane<CTW> ln;
+  // l/16; x1 row row0 + 4 d + l/16 of DMA d, chunk (l%16) ^ that local row
+  // (rows >= m read zeros); scale column clamped to n - 1. Every offset a
+  // valid lane uses stays inside its buffer.
+  DecodeLane<CTW, XD> ln;
   ln.w = buf_rsrc(a.x2, a.x2_bytes);
   ln.x = buf_rsrc(a.x1, a.x1_bytes);
   ln.s = buf_rsrc(a.scale, a.s_bytes);
   ln.o = buf_rsrc(a.offset, a.s_bytes);
-  const int64_t xrow = a.row0 + col;
-  ln.xoff = xrow < a.m ? (uint32_t)(xrow * a.k * 2 + kq * (SPG == 4 ? 64 : 16)) : BUF_OOB;
+#pragma unroll
+  for (int d = 0; d < XD; ++d) {
+    const int q = 4 * d + kq;                       // local row 0..15
+    const int64_t xrow = a.row0 + q;
+    ln.xoff[d] = xrow < a.m ? (uint32_t)(xrow * a.k * 2 + 16 * (col ^ q)) : BUF_OOB;
+  }
+  auto scol = [&](int c) { return n0 + 16 * c + col < a.n ? n0 + 16 * c + col : a.n - 1; };
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
     const int64_t ct = ct0 + c < a.nct ? ct0 + c : a.nct - 1;
     // INT4: the GFX950_B record's sub-block kq; INT8: 32 bytes of column
     // row (n, k), past n out of the weight (reads zeros)
     ln.woff[c] = W8 ? (uint32_t)((ct * 16 + col) * a.k + kq * 32) : (uint32_t)((ct * 16 + col) * 64 + kq * 16);
-    const int64_t sc = n0 + 16 * c + col < a.n ? n0 + 16 * c + col : a.n - 1;
-    ln.soff[c] = (uint32_t)(sc * a.s_col * 2);
+    ln.soff[c] = (uint32_t)(scol(c) * a.s_col * 2);
   }
+  if constexpr (SPG == 4) ln.soff[0] = (uint32_t)(scol(kq < CTW ? kq : CTW - 1) * a.s_col * 2);
 
   // Epilogue mapping (two adjacent columns of one row per thread, TPR threads
   // per row); its residual and bias values are fetched before the K loop so
@@ -443,19 +473,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   uint8_t* xa = xlds[wave][0];
   uint8_t* xb = xlds[wave][1];
   DecodeBatch<CTW, W8> ba, bb;
-  if (kb0 < kb1) issue_batch<CTW, SPG, W8>(a, ln, kb0, xa, ba);
+  if (kb0 < kb1) issue_batch<CTW, SPG, W8, XD>(a, ln, kb0, xa, ba);
   for (int kb = kb0; kb < kb1; kb += 2) {
-    if (kb + 1 < kb1) issue_batch<CTW, SPG, W8>(a, ln, kb + 1, xb, bb);
+    if (kb + 1 < kb1) issue_batch<CTW, SPG, W8, XD>(a, ln, kb + 1, xb, bb);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 1 < kb1) wait_vm<batch_loads<CTW, W8>()>();
+    if (kb + 1 < kb1) wait_vm<batch_loads<CTW, SPG, W8, XD>()>();
     else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
     mma_batch<ACT, CTW, SPG, W8>(a, ba, xa, ma, acc);
     __builtin_amdgcn_sched_barrier(0);
     if (kb + 1 >= kb1) break;
-    if (kb + 2 < kb1) issue_batch<CTW, SPG, W8>(a, ln, kb + 2, xa, ba);
+    if (kb + 2 < kb1) issue_batch<CTW, SPG, W8, XD>(a, ln, kb + 2, xa, ba);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 2 < kb1) wait_vm<batch_loads<CTW, W8>()>();
+    if (kb + 2 < kb1) wait_vm<batch_loads<CTW, SPG, W8, XD>()>();
     else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
     mma_batch<ACT, CTW, SPG, W8>(a, bb, xb, ma, acc);
@@ -506,30 +536,39 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   }
 }
 
+template <int ACT, bool W8, int XD>
+void launch_spg4(const DecodeArgs& a, int ctw, unsigned grid, hipStream_t s) {
+  switch (ctw) {
+    case 1: gemm_decode<ACT, 1, 4, W8, XD><<<dim3(grid), 1024, 0, s>>>(a); break;
+    case 2: gemm_decode<ACT, 2, 4, W8, XD><<<dim3(grid), 1024, 0, s>>>(a); break;
+    default:
+      if constexpr (!W8) gemm_decode<ACT, 3, 4, W8, XD><<<dim3(grid), 1024, 0, s>>>(a);
+      break;
+  }
+}
+
+// xd: x1 DMAs per block, 1, 2 or 4 for at most 4, 8 or 16 rows in the launch
+// (short groups always take 4)
 template <int ACT, bool W8>
-void launch_fmt(const DecodeArgs& a, int spg, int ctw, unsigned grid, hipStream_t s) {
+void launch_fmt(const DecodeArgs& a, int spg, int ctw, int xd, unsigned grid, hipStream_t s) {
   if (spg == 4) {
-    switch (ctw) {
-      case 1: gemm_decode<ACT, 1, 4, W8><<<dim3(grid), 1024, 0, s>>>(a); break;
-      case 2: gemm_decode<ACT, 2, 4, W8><<<dim3(grid), 1024, 0, s>>>(a); break;
-      default:
-        if constexpr (!W8) gemm_decode<ACT, 3, 4, W8><<<dim3(grid), 1024, 0, s>>>(a);
-        break;
-    }
+    if (xd == 1) launch_spg4<ACT, W8, 1>(a, ctw, grid, s);
+    else if (xd == 2) launch_spg4<ACT, W8, 2>(a, ctw, grid, s);
+    else launch_spg4<ACT, W8, 4>(a, ctw, grid, s);
   } else if (spg == 2) {
-    if (W8 || ctw == 1) gemm_decode<ACT, 1, 2, W8><<<dim3(grid), 1024, 0, s>>>(a);
-    else if constexpr (!W8) gemm_decode<ACT, 2, 2, W8><<<dim3(grid), 1024, 0, s>>>(a);
+    if (W8 || ctw == 1) gemm_decode<ACT, 1, 2, W8, 4><<<dim3(grid), 1024, 0, s>>>(a);
+    else if constexpr (!W8) gemm_decode<ACT, 2, 2, W8, 4><<<dim3(grid), 1024, 0, s>>>(a);
   } else {
-    if (W8 || ctw == 1) gemm_decode<ACT, 1, 1, W8><<<dim3(grid), 1024, 0, s>>>(a);
-    else if constexpr (!W8) gemm_decode<ACT, 2, 1, W8><<<dim3(grid), 1024, 0, s>>>(a);
+    if (W8 || ctw == 1) gemm_decode<ACT, 1, 1, W8, 4><<<dim3(grid), 1024, 0, s>>>(a);
+    else if constexpr (!W8) gemm_decode<ACT, 2, 1, W8, 4><<<dim3(grid), 1024, 0, s>>>(a);
   }
 }
 
 template <int ACT>
-void launch_act(const DecodeArgs& a, bool w8, int spg, int ctw, unsigned grid, hipStream_t s) {
+void launch_act(const DecodeArgs& a, bool w8, int spg, int ctw, int xd, unsigned grid, hipStream_t s) {
   prof_begin(s);
-  if (w8) launch_fmt<ACT, true>(a, spg, ctw, grid, s);
-  else launch_fmt<ACT, false>(a, spg, ctw, grid, s);
+  if (w8) launch_fmt<ACT, true>(a, spg, ctw, xd, grid, s);
+  else launch_fmt<ACT, false>(a, spg, ctw, xd, grid, s);
   prof_end(s);
 }
 
@@ -622,8 +661,10 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s) {
   // one launch per 16 rows (m <= 32: at most two; the second finds the
   // weights in the last-level cache)
   for (a.row0 = 0; a.row0 < p.m; a.row0 += 16) {
-    if (p.bf16) launch_act<ACT_BF16>(a, w8, spg, ctw, grid, s);
-    else launch_act<ACT_F16>(a, w8, spg, ctw, grid, s);
+    const int64_t rows = p.m - a.row0;
+    const int xd = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;
+    if (p.bf16) launch_act<ACT_BF16>(a, w8, spg, ctw, xd, grid, s);
+    else launch_act<ACT_F16>(a, w8, spg, ctw, xd, grid, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
