@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
                                                     int64_t np, int64_t s_row, int64_t s_col, int ngb,
                                                     uint16_t* __restrict__ corr,
                                                     uint32_t* __restrict__ zflag) {
-  extern __shared__ float sh[];               // max(k / 8, 32 * 65) floats
+  extern __shared__ float sh[];               // max(k / 8 + k / 128, 32 * 65) floats
   const int t = threadIdx.x;
   const int64_t b = blockIdx.x;
   if (b < m) {
@@ -117,16 +117,19 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
         s += lo_f32<ACT>(v[i].y) + hi_f32<ACT>(v[i].y);
         s += lo_f32<ACT>(v[i].z) + hi_f32<ACT>(v[i].z);
         s += lo_f32<ACT>(v[i].w) + hi_f32<ACT>(v[i].w);
-        if (c < chunks) sh[c] = s;
+        if (c < chunks) sh[c + (c >> 4)] = s;   // one pad float per 16 chunks
       }
     }
     __syncthreads();
-    const int64_t per = group / 8;             // chunks per group
+    // chunks per group: a multiple of 16, so with the padding thread g's
+    // reads start 17 * per / 16 floats after thread g - 1's (an odd stride
+    // for groups of 128: the 64 lanes read 64 distinct banks)
+    const int64_t per = group / 8;
     for (int64_t g = t; g < gp; g += 256) {
       float s = 0.f;
       if (g < groups) {
         const int64_t c1 = (g + 1) * per < chunks ? (g + 1) * per : chunks;
-        for (int64_t c = g * per; c < c1; ++c) s += sh[c];
+        for (int64_t c = g * per; c < c1; ++c) s += sh[c + (c >> 4)];
       }
       uint16_t hi, mid, lo;
       split3_bf16(s, hi, mid, lo);
@@ -656,7 +659,8 @@ hipError_t launch_wide_t(const WqProblem& p, float* partial, uint16_t* rs, uint1
   const int64_t ncb = (a.np + PC_COLS - 1) / PC_COLS;
   const int64_t blocks = p.m + ncb * a.ngb;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const int64_t sh_floats = p.k / 8 > PC_GROUPS * (PC_COLS + 1) ? p.k / 8 : PC_GROUPS * (PC_COLS + 1);
+  const int64_t row_floats = p.k / 8 + p.k / 128;    // chunk sums, one pad float per 16
+  const int64_t sh_floats = row_floats > PC_GROUPS * (PC_COLS + 1) ? row_floats : PC_GROUPS * (PC_COLS + 1);
   prefill_prep<ACT><<<dim3((unsigned)blocks), 256, (size_t)sh_floats * sizeof(float), s>>>(
       a.x1, p.m, p.k, a.group, a.groups, a.gp, rs, a.scale, static_cast<const uint16_t*>(p.offset),
       p.n, a.np, p.s_row, p.s_col, a.ngb, corr, zflag);
