@@ -187,19 +187,27 @@ static_assert(32 * WD_EROW <= 16384, "epilogue staging must fit a wave's 16 KiB 
 // x1 slab (128 rows x 128 K) -> LDS: 32 DMA instructions of 1 KiB (4 rows);
 // wave w issues 4w + j: rows 16w + 4j + lane/16. LDS rows are 256 bytes; the
 // 16-byte chunk of row r at position p holds logical chunk p ^ h(r & 15),
-// h(r) = (r mod 4) * 4 + r / 4: the 16-byte A-fragment reads (16 rows, one
-// K chunk per lane group) then run at the rate of linear reads, measured
-// with an LDS probe on gfx950 (p ^ r, whose 16 positions are distinct in
-// every group of 16 lanes, ran 1.38x slower). With r & 15 = 4j + lane/16,
-// h(r) = 4 (lane/16) + j, so the lane's source chunk is c0 ^ j, c0 =
-// (lane & 15) ^ 4 (lane / 16), and its byte offset is (v0 ^ 16j) + 8jk with
-// v0 = (16w + lane/16) * 2k + 16 c0 (2k is a multiple of 256, so the XOR only
-// touches the chunk bits). The buffer resource starts at the slab and ends
-// after the tile's last row: rows past m read 0.
+// with h linear over the bits of r: h(1) = 8, h(2) = 3, h(4) = 0, h(8) = 1.
+// The 16-byte A-fragment reads (16 rows; in lane group g, K chunk 4g + d)
+// then take no bank-conflict cycles: this map was picked from 200 random
+// linear maps by the SQ_LDS_BANK_CONFLICT counter of an LDS probe on
+// gfx950 that reads exactly these fragments (the earlier (r mod 4) * 4 +
+// r / 4, like most maps tried, cost 2 cycles per read; the read cost does
+// not follow a plain bank-count model). With r & 15 = 4j + lane/16 and h
+// linear, h(r) = h(lane/16) ^ h(4j), so the lane's source chunk is
+// c0 ^ h(4j), c0 = (lane & 15) ^ h(lane / 16), and its byte offset is
+// (v0 ^ 16 h(4j)) + 8jk with v0 = (16w + lane/16) * 2k + 16 c0 (2k is a
+// multiple of 256, so the XOR only touches the chunk bits). The buffer
+// resource starts at the slab and ends after the tile's last row: rows past
+// m read 0.
+__host__ __device__ constexpr int wd_swz(int r) {
+  return ((r & 1) ? 8 : 0) ^ ((r & 2) ? 3 : 0) ^ ((r & 8) ? 1 : 0);
+}
+
 __device__ __forceinline__ void wd_dma_a1(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf,
                                           int j) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (4 * wave_id() + j) * 4 * WD_LROW), 16,
-                                           (v0 ^ (16u * j)) + 8u * j * k, 0, 0, 0);
+                                           (v0 ^ (16u * (uint32_t)wd_swz(4 * j))) + 8u * j * k, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wd_dma_a(__amdgpu_buffer_rsrc_t ra, uint32_t v0, uint32_t k, uint8_t* buf) {
@@ -262,7 +270,7 @@ __device__ __forceinline__ void wd_slab(const uint8_t* abuf, const uint8_t* wbuf
   // makes the weight reads conflict-free; each group still covers its block
   // once over the four steps.
   const int g = lane >> 4, cl = lane & 15;
-  const int hcl = ((cl & 3) << 2) | (cl >> 2);           // the row swizzle h(cl)
+  const int hcl = wd_swz(cl);                             // the row swizzle h(cl)
   const uint8_t* arow = abuf + cl * WD_LROW;
   const uint8_t* brow = wbuf + wave * 4096 + 16 * (4 * cl + (g ^ (cl >> 2)));
   auto a_at = [&](int i, int c) {
@@ -348,7 +356,7 @@ __device__ __forceinline__ void wide_body(const FastArgs& a, int64_t m0, int64_t
   //      resources are rebuilt per slab in scalar registers ----
   const int rows_left = (int)(a.m - m0 < WD_BM ? a.m - m0 : WD_BM);
   const uint32_t a_v0 = (uint32_t)(16 * wave + (lane >> 4)) * 2u * k +
-                        16u * (uint32_t)((lane & 15) ^ ((lane >> 4) << 2));
+                        16u * (uint32_t)((lane & 15) ^ wd_swz(lane >> 4));
   const uint32_t b_v0 = wd_b_v0(wave, lane);
   const int64_t slab_bytes = a.np * 64;
   // (the slab after the last one gets empty resources: its DMA, issued
