@@ -124,6 +124,9 @@ constexpr int MF_SBYTES = 1024;            // 256 x 4 scale bytes
 // multiple of 8 below 128, hit each value of (r & 7) | ((r & 16) >> 1) twice.
 __device__ __forceinline__ int mf_swz(int r) { return (r & 7) | ((r & 16) >> 1); }
 
+// position of 32-deep block g inside weight record slot jl (mod 16): g ^ mf_bswz(jl)
+__device__ __forceinline__ int mf_bswz(int jl) { return (jl >> 1) & 2; }
+
 struct MfBufs {
   uint8_t* a;
   uint8_t* b;
@@ -186,14 +189,19 @@ __device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, i
   for (int i = 0; i < 2; ++i) {
     // 64-byte record slot sl = 128 wn + 16 j + jl holds the tile's column
     // 128 wn + 8 jl + j, so that a lane's eight columns (j = 0..7) are
-    // consecutive: their scales are one 8-byte read and their y one 32-byte run
+    // consecutive: their scales are one 8-byte read and their y one 32-byte run.
+    // Inside slot jl (mod 16) the 16-byte 32-deep blocks sit at position
+    // g ^ mf_bswz(jl): the fragment reads then take no bank-conflict cycles
+    // (unswizzled: 4 per read; picked with the SQ_LDS_BANK_CONFLICT counter
+    // of an LDS probe of these reads). Four lanes still fetch one record.
     const int q = 2 * wave + i;
     const int sl = 16 * q + (lane >> 2);
     const int col = (sl & 128) + 8 * (sl & 15) + ((sl >> 4) & 7);
+    const int blk = (lane & 3) ^ mf_bswz(lane >> 2);
     if constexpr (RG)
-      mf_dma16(src.rw, bf.b + q * 1024, (uint32_t)(((int64_t)step * Np + n0 + col) * 64 + 16 * (lane & 3)));
+      mf_dma16(src.rw, bf.b + q * 1024, (uint32_t)(((int64_t)step * Np + n0 + col) * 64 + 16 * blk));
     else
-      __builtin_amdgcn_global_load_lds((glb_void*)(src.x2 + ((int64_t)step * Np + n0 + col) * 64 + 16 * (lane & 3)),
+      __builtin_amdgcn_global_load_lds((glb_void*)(src.x2 + ((int64_t)step * Np + n0 + col) * 64 + 16 * blk),
                                        (lds_void*)(bf.b + q * 1024), 16, 0, 0);
   }
   if (wave < 4) {   // scale1 rows m0 + 64 wave + lane, blocks 4 step .. 4 step + 3
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   const int r0 = 16 * g + (jl >> 1);
   const int swz = mf_swz(r0);
   const int abase = r0 * 256 + 8 * (jl & 1);
-  const int boff = (128 * wn + jl) * 64 + g * 16;       // + 1024 j
+  const int boff = (128 * wn + jl) * 64 + 16 * (g ^ mf_bswz(jl));   // + 1024 j
   const int s1off = (64 * wm + jl) * 4 + g;             // + 64 i
   const int s2off = g * 256 + 128 * wn + 8 * jl;        // columns 8 jl .. 8 jl + 7
 
