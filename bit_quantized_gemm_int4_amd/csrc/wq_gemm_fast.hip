@@ -76,14 +76,14 @@ struct FastArgs {
 // ---------------------------------------------------------------------------
 // Pre-pass (one launch): the per-group row sums of x1 and the per-group
 // column corrections, both written as bf16 hi/lo in MFMA operand order.
-//   blocks [0, m): row b's sums, [m][3][gp] (zero padded to gp groups): eight-
-//     element chunk sums in LDS (each thread's loads issued together), then
-//     each group summed in a fixed order;
-//   blocks [m, m + ncb * ngb): a tile of 64 columns x 32 groups of
+//   blocks [0, nct), nct = ncb * ngb: a tile of 64 columns x 32 groups of
 //     o[g][n] - bias * s[g][n] (zero for padding), [np][2][gp]: read along the
 //     columns (coalesced), transposed through LDS, written along the groups.
 //     The tile also writes one word, nonzero when one of its scales is zero
-//     (zflag[ci * ngb + gi]); the main tile ORs the words of its strip.
+//     (zflag[ci * ngb + gi]); the main tile ORs the words of its strip;
+//   blocks [nct, nct + m): row b - nct's sums, [m][3][gp] (zero padded to gp
+//     groups): eight-element chunk sums in LDS (each thread's loads issued
+//     together), then each group summed in a fixed order.
 // ---------------------------------------------------------------------------
 constexpr int PC_COLS = 64, PC_GROUPS = 32;
 
@@ -98,9 +98,12 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
                                                     uint32_t* __restrict__ zflag) {
   extern __shared__ float sh[];               // max(k / 8 + k / 128, 32 * 65) floats
   const int t = threadIdx.x;
+  // the correction tiles take the first blocks, so that the row blocks,
+  // which only stream x1, make up the last round of workgroups
+  const int64_t nct = ((np + PC_COLS - 1) / PC_COLS) * ngb;
   const int64_t b = blockIdx.x;
-  if (b < m) {
-    const int64_t row = b;
+  if (b >= nct) {
+    const int64_t row = b - nct;
     const uint16_t* xr = x1 + row * k;
     const int64_t chunks = k / 8;
     for (int64_t c0 = 0; c0 < chunks; c0 += 1024) {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256) void prefill_prep(const uint16_t* __restrict__
     }
     return;
   }
-  const int64_t cb = b - m;
+  const int64_t cb = b;
   const int64_t ci = cb / ngb, gi = cb % ngb;
   float (*tile)[PC_COLS + 1] = reinterpret_cast<float (*)[PC_COLS + 1]>(sh);
   int zero = 0;
