@@ -614,6 +614,95 @@ def main():
         ceilings["hbm_copy"] = {"what": "device copy of 512 MiB (read + write)", "ms": round(cp_ms, 5),
                                 "GB/s": round(2 * cb / cp_ms / 1e6, 1)}
         del src, dst
+        # the stream-read microkernel (the library's wq_ceiling_stream_read:
+        # every 16-byte chunk loaded once, nothing else) at the decode
+        # weight's size, over 24 rotated copies (past the last-level cache),
+        # timed per call like the decode rows: eagerly with events, and the
+        # 24 calls replayed as one HIP graph; then over 512 MiB
+        rb = wq.wq_pack_int4_bytes(4096, 11008, wq.WQ_LAYOUT_GFX950_B)   # decode x2 (4096, 11008)
+        rcopies = 24
+        rbufs = [torch.ones(rb // 4, dtype=torch.int32, device=dev) for _ in range(rcopies)]
+        rout = torch.empty(wq.wq_ceiling_stream_read_words(rb), dtype=torch.int32, device=dev)
+        rd = lambda i: wq.wq_ceiling_stream_read(rbufs[i % rcopies], rb, rout)
+        for i in range(2 * rcopies):
+            rd(i)
+        evs = []
+        for i in range(200):
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            rd(i)
+            b0.record(stream)
+            evs.append((a0, b0))
+        torch.cuda.synchronize()
+        rd_ms = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            for i in range(rcopies):
+                rd(i)
+        stream.wait_stream(gs)
+        torch.cuda.synchronize()
+        rgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rgraph):
+            for i in range(rcopies):
+                rd(i)
+        for _ in range(3):
+            rgraph.replay()
+        torch.cuda.synchronize()
+        gts = []
+        for _ in range(8):
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            rgraph.replay()
+            b0.record(stream)
+            gts.append((a0, b0))
+        torch.cuda.synchronize()
+        rg_ms = statistics.median(a0.elapsed_time(b0) for a0, b0 in gts) / rcopies
+        del rgraph, rbufs, rout
+        ceilings["hbm_stream_read_decode_weight"] = {
+            "what": f"wq_ceiling_stream_read of {rb} B (the decode weight's bytes), 24 rotated copies",
+            "us": round(rd_ms * 1e3, 3), "GB/s": round(rb / rd_ms / 1e6, 1),
+            "graph_us": round(rg_ms * 1e3, 3), "graph_GB/s": round(rb / rg_ms / 1e6, 1)}
+        big = 512 << 20
+        bsrc = torch.ones(big // 4, dtype=torch.int32, device=dev)
+        bout = torch.empty(wq.wq_ceiling_stream_read_words(big), dtype=torch.int32, device=dev)
+        for _ in range(3):
+            wq.wq_ceiling_stream_read(bsrc, big, bout)
+        evs = []
+        for _ in range(10):
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            wq.wq_ceiling_stream_read(bsrc, big, bout)
+            b0.record(stream)
+            evs.append((a0, b0))
+        torch.cuda.synchronize()
+        br_ms = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+        ceilings["hbm_stream_read_512MiB"] = {"what": "wq_ceiling_stream_read of 512 MiB",
+                                              "ms": round(br_ms, 5), "GB/s": round(big / br_ms / 1e6, 1)}
+        del bsrc, bout
+        # the MFMA-loop microkernel (wq_ceiling_mfma_loop: bf16 16x16x32 on
+        # register operands): 512 workgroups of four waves (two waves per
+        # SIMD, as the prefill tile runs) and 2048 (eight per SIMD)
+        mloop = {}
+        for wgs in (512, 2048):
+            iters = 16384 if wgs == 512 else 4096
+            mout = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+            for _ in range(2):
+                wq.wq_ceiling_mfma_loop(wgs, iters, mout)
+            evs = []
+            for _ in range(5):
+                a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                wq.wq_ceiling_mfma_loop(wgs, iters, mout)
+                b0.record(stream)
+                evs.append((a0, b0))
+            torch.cuda.synchronize()
+            ml_ms = statistics.median(a0.elapsed_time(b0) for a0, b0 in evs)
+            mflop = 2 * 16 * 16 * 32 * 8 * 4 * iters * wgs
+            mloop[f"wg{wgs}"] = {"ms": round(ml_ms, 5), "TFLOP/s": round(mflop / ml_ms / 1e9, 1)}
+            del mout
+        ceilings["mfma_loop_bf16"] = {"what": "wq_ceiling_mfma_loop: v_mfma_f32_16x16x32_bf16 on register "
+                                              "operands, 2 and 8 waves per SIMD", **mloop}
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     cpu = None

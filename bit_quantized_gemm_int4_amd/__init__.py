@@ -47,6 +47,7 @@ EXPORTS = (
     "mx_fp4_quant_matmul_inplace_add_workspace_size", "mx_fp4_quant_matmul_inplace_add",
     "wq_weight_quant_matmul_workspace_size", "wq_weight_quant_matmul", "wq_add_rms_norm",
     "wq_profile_enable", "wq_profile_read",
+    "wq_ceiling_stream_read_words", "wq_ceiling_stream_read", "wq_ceiling_mfma_loop",
 )
 
 _lib = None
@@ -91,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "wq_add_rms_norm": (I, [P, P, P, I64, I64, I, D, P, P, P]),
             "wq_profile_enable": (I, [I]),
             "wq_profile_read": (I, [P, I64, ctypes.POINTER(I64)]),
+            "wq_ceiling_stream_read_words": (S, [S]),
+            "wq_ceiling_stream_read": (I, [P, S, P, P]),
+            "wq_ceiling_mfma_loop": (I, [I64, ctypes.c_int32, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -174,6 +178,20 @@ def wq_profile_read(capacity: int = 4096, check=True):
     _check(lib().wq_profile_read(ctypes.addressof(buf), capacity, ctypes.byref(n)),
            "wq_profile_read", check)
     return [buf[i] for i in range(min(n.value, capacity))]
+
+
+def wq_ceiling_stream_read_words(nbytes: int) -> int:
+    return lib().wq_ceiling_stream_read_words(nbytes)
+
+
+def wq_ceiling_stream_read(src, nbytes, out, stream=None, check=True) -> int:
+    st = lib().wq_ceiling_stream_read(_ptr(src), nbytes, _ptr(out), _stream(stream))
+    return _check(st, "wq_ceiling_stream_read", check)
+
+
+def wq_ceiling_mfma_loop(workgroups, iters, out, stream=None, check=True) -> int:
+    st = lib().wq_ceiling_mfma_loop(workgroups, iters, _ptr(out), _stream(stream))
+    return _check(st, "wq_ceiling_mfma_loop", check)
 
 
 def wq_matmul_add_rmsnorm_workspace_size(m: int, k: int, n: int) -> int:

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libwq.so")
 
 SOURCES = ["wq_api.cpp", "wq_profile.cpp", "wq_pack.hip", "wq_quant.hip", "wq_gemm.hip", "wq_gemm_fast.hip",
            "wq_gemm_decode.hip", "wq_gemm_w8.hip", "mx_gemm.hip", "i8_gemm.hip", "add_rmsnorm.hip",
-           "mx4_gemm.hip", "a8w4_gemm.hip", "wq_noalloc.hip"]
+           "mx4_gemm.hip", "a8w4_gemm.hip", "wq_noalloc.hip", "wq_ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -37,6 +37,9 @@ FLAGS = [
 # MFMAs keep accumulators in ordinary VGPRs (no AGPR copies). Its accumulators are long-lived and updated in place; the decode
 # kernel, whose per-block partial sums are short-lived, keeps them in AGPRs.
 FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              # the MFMA-loop microkernel: with AGPR accumulators the
+              # allocator rotated them into partially overlapping MFMAs
+              "wq_ceiling.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "wq_gemm_w8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               # the INT8 epilogue rounds each float step on its own, as its
               # reading of the formula fixes: no fused multiply-add
@@ -47,7 +50,7 @@ FILE_FLAGS = {"wq_gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 # destinations that partially overlap a source operand (codegen_check).
 MFMA_SOURCES = ["wq_gemm.hip", "wq_gemm_fast.hip", "wq_gemm_decode.hip", "wq_gemm_w8.hip", "mx_gemm.hip",
                 "i8_gemm.hip",
-                "mx4_gemm.hip", "a8w4_gemm.hip"]
+                "mx4_gemm.hip", "a8w4_gemm.hip", "wq_ceiling.hip"]
 
 
 def _compile(src: str) -> str:

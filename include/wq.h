@@ -444,6 +444,37 @@ wq_status wq_quant_matmul_inplace_add_w4(const void* x1, wq_dtype x1_dtype,
 wq_status wq_profile_enable(int enable);
 wq_status wq_profile_read(float* times_ms, int64_t capacity, int64_t* launches);
 
+/* ------------------------------------------------------------------------
+ * Achievable ceilings (measurement aids, not operators of any page): two
+ * microkernels that the measurement times next to the published MI355X
+ * peaks, so that a kernel's fraction of peak can be read against what this
+ * GPU reaches on the same resource with nothing else in the way.
+ *
+ * wq_ceiling_stream_read loads each 16-byte chunk of `bytes` bytes at src
+ * once (one 16-byte load per lane, four per thread issued before any use)
+ * and writes, per wave, the XOR of the 32-bit words it read:
+ * wq_ceiling_stream_read_words(bytes) words to out. The XOR of all of them
+ * is the XOR of every word of the input. src: device memory, 16-byte
+ * aligned, bytes a positive multiple of 16 below 2^40 (otherwise
+ * wq_ceiling_stream_read_words returns 0); out: device memory,
+ * caller-owned, 4-byte aligned.
+ *
+ * wq_ceiling_mfma_loop runs `workgroups` workgroups of four waves; each
+ * wave issues `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16
+ * on register operands, i.e. 2 * 16 * 16 * 32 * 8 * 4 * iters * workgroups
+ * flops in all. The operands are random bf16 values of magnitude in
+ * [0.5, 2), four A and four B fragments per lane (accumulator j multiplies
+ * A set j % 4 by B set j / 2), fixed functions of the lane index; each lane
+ * writes the sum of its accumulators to out[workgroups * 256] (device
+ * memory, caller-owned, floats), the same for every workgroup.
+ *
+ * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (sizes or alignment as above;
+ * workgroups outside [1, 2^20], iters outside [1, 16384]); WQ_ERR_LAUNCH.
+ * ---------------------------------------------------------------------- */
+size_t wq_ceiling_stream_read_words(size_t bytes);
+wq_status wq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* out, hipStream_t stream);
+wq_status wq_ceiling_mfma_loop(int64_t workgroups, int32_t iters, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

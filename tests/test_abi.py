@@ -29,7 +29,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     L = wq.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -384,3 +384,23 @@ def test_mx_fp4_matmul_validation():
     assert _mx4(x1=FAKE + 8) == wq.WQ_ERR_SHAPE                       # misaligned
     assert _mx4(y=FAKE + 0x100000) == wq.WQ_ERR_ALIAS                 # y over x2
     assert _mx4(ws=FAKE + 0x200000) == wq.WQ_ERR_ALIAS                # workspace over x1's scales
+
+
+def test_ceiling_microkernels_validate_on_the_host():
+    L = wq.lib()
+    assert L.wq_ceiling_stream_read_words(0) == 0
+    assert L.wq_ceiling_stream_read_words(24) == 0                # not a multiple of 16
+    assert L.wq_ceiling_stream_read_words(16) == 4                # one workgroup, four waves
+    assert L.wq_ceiling_stream_read_words(16384) == 4
+    assert L.wq_ceiling_stream_read_words(16400) == 8
+    assert L.wq_ceiling_stream_read_words(1 << 40) == 0
+    assert L.wq_ceiling_stream_read(None, 16, FAKE, None) == wq.WQ_ERR_NULLPTR
+    assert L.wq_ceiling_stream_read(FAKE, 16, None, None) == wq.WQ_ERR_NULLPTR
+    assert L.wq_ceiling_stream_read(FAKE, 24, FAKE2, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_stream_read(FAKE + 8, 16, FAKE2, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_stream_read(FAKE, 16, FAKE2 + 2, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_mfma_loop(1, 1, None, None) == wq.WQ_ERR_NULLPTR
+    assert L.wq_ceiling_mfma_loop(0, 1, FAKE, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_mfma_loop((1 << 20) + 1, 1, FAKE, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_mfma_loop(1, 0, FAKE, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_mfma_loop(1, 16385, FAKE, None) == wq.WQ_ERR_SHAPE
