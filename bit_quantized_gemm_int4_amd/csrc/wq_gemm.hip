@@ -15,7 +15,8 @@
 //   - gemm_b_wide (wq_gemm_fast.hip): the same weights at larger m, the
 //     MFMA-bound tile;
 //   - gemm_w8 (wq_gemm_w8.hip): INT8 weights, row-major or transposed, k a
-//     multiple of 16: a 64 x 64 tile with loads two K steps ahead;
+//     multiple of 16: a 64 x 64 tile with loads two K steps ahead; also
+//     INT4 GFX950_B weights where the two kernels above do not apply;
 //   - gemm_generic: any weight layout (INT4 ND / ND transposed / GFX950_B,
 //     INT8 ND / transposed), any group size, 64x64x32 tiles with both operands staged
 //     in LDS; integer codes go to the MFMA and each group's scale and

@@ -1,6 +1,8 @@
 // INT8-weight tile of the weight-quantized matmul + AddRmsNorm
 // (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula; x2 int8 (k, n)
-// or its transpose (n, k), Constraints section). Same operator and numerics
+// or its transpose (n, k), Constraints section), also run on INT4 weights
+// in the GFX950_B layout (B4) for the groups and K the prefill tile does not
+// take. Same operator and numerics
 // as wq_gemm.hip: the codes enter the MFMA as exact 16-bit values q, each
 // group's scale and offset are applied to its float32 partial sums, the
 // epilogue writes y = acc + bias + residual and per-(row, 32-column tile)
@@ -42,7 +44,7 @@ constexpr int W8_LDS = W8_BK + 8;   // halves per LDS row: 144 bytes, conflict-f
 
 struct W8Args {
   const uint16_t* x1;
-  const uint8_t* x2;
+  const uint8_t* x2;        // INT8 (k, n) or (n, k); or INT4 GFX950_B (B4)
   const uint16_t* scale;
   const uint16_t* offset;   // may be null
   const uint16_t* bias;     // may be null
@@ -50,6 +52,7 @@ struct W8Args {
   uint16_t* y;
   float* partial;           // [m][ceil(n / 32)]
   int64_t m, k, n, s_row, s_col;
+  int64_t np;               // B4: the padded width of the GFX950_B layout
   int upg;                  // 32-deep units per group; INT32_MAX: one group over all of K
   uint32_t s_bytes;
 };
@@ -94,6 +97,44 @@ __device__ __forceinline__ void convert_k16(const u32x4& w, u32x4& lo, u32x4& hi
   }
   lo = (u32x4){o[0], o[1], o[2], o[3]};
   hi = (u32x4){o[4], o[5], o[6], o[7]};
+}
+
+// 16 consecutive K codes of one column as INT4 nibbles (w0: K 0..7, w1:
+// K 8..15, low nibble first; the GFX950_B byte order) -> eight dwords of
+// 16-bit q, K ascending. u = n ^ 8 = q + 8 in [0, 15]: fp16 places u under
+// the exponent byte 0x64 (1024 + u) and subtracts 1032 with one packed half
+// subtraction per pair; bf16 converts each byte to float32 and subtracts 8
+// (exact), two per packed bf16 conversion.
+template <int ACT>
+__device__ __forceinline__ void convert_n16(uint32_t w0, uint32_t w1, u32x4& lo4, u32x4& hi4) {
+  uint32_t o[8];
+  const uint32_t w[2] = {w0, w1};
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const uint32_t u = w[d] ^ 0x88888888u;
+    const uint32_t ev = u & 0x0F0F0F0Fu, od = (u >> 4) & 0x0F0F0F0Fu;   // K 0, 2, 4, 6 / K 1, 3, 5, 7
+    const uint32_t p0 = __builtin_amdgcn_perm(od, ev, 0x05010400u);    // K 0..3 as bytes
+    const uint32_t p1 = __builtin_amdgcn_perm(od, ev, 0x07030602u);    // K 4..7
+    if constexpr (ACT == ACT_F16) {
+      const f16x2 bias = {(_Float16)1032.f, (_Float16)1032.f};
+      auto pair = [&](uint32_t b, uint32_t sel) {
+        const uint32_t h = __builtin_amdgcn_perm(0x64646464u, b, sel);
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) - bias);
+      };
+      o[4 * d] = pair(p0, 0x04010400u);
+      o[4 * d + 1] = pair(p0, 0x04030402u);
+      o[4 * d + 2] = pair(p1, 0x04010400u);
+      o[4 * d + 3] = pair(p1, 0x04030402u);
+    } else {
+      auto q = [](uint32_t b, int j) { return (float)((b >> (8 * j)) & 0xFFu) - 8.f; };
+      o[4 * d] = bf16_pair(q(p0, 0), q(p0, 1));
+      o[4 * d + 1] = bf16_pair(q(p0, 2), q(p0, 3));
+      o[4 * d + 2] = bf16_pair(q(p1, 0), q(p1, 1));
+      o[4 * d + 3] = bf16_pair(q(p1, 2), q(p1, 3));
+    }
+  }
+  lo4 = (u32x4){o[0], o[1], o[2], o[3]};
+  hi4 = (u32x4){o[4], o[5], o[6], o[7]};
 }
 
 // Four K rows of four columns (r[i] = row i, byte j = column j) -> per
@@ -156,7 +197,7 @@ __device__ __forceinline__ bool closes_group(const W8Args& a, int kend, int kh, 
 }
 
 // The loads of one step of one slice: K values [k0, k0 + 64) below kend.
-template <bool ND>
+template <bool ND, bool B4>
 __device__ __forceinline__ void load_stage(const W8Args& a, const W8Lane& ln, int64_t n0, int kend, int k0,
                                            FoldPos& fp, W8Stage& st) {
   const int t = threadIdx.x & 255, lane = t & 63;
@@ -166,7 +207,17 @@ __device__ __forceinline__ void load_stage(const W8Args& a, const W8Lane& ln, in
     st.a0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.x, v, 0, 0));
     st.a1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.x, v + 16u, 0, 0));
   }
-  if constexpr (!ND) {
+  if constexpr (B4) {
+    // column c's K values kk .. kk + 15: 8 bytes of its GFX950_B record
+    // (the 32-deep block kk / 32 of 128-deep block kk / 128), the resource
+    // starting at the workgroup's first column
+    const int c = t >> 2, kk = k0 + (t & 3) * 16;
+    const uint32_t v = (c < ln.cols) & (kk < kend)
+                           ? (uint32_t)((((int64_t)(kk >> 7) * a.np + c) * 64) + ((kk >> 5) & 3) * 16 + ((kk & 31) >> 1))
+                           : BUF_OOB;
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ln.w, v, 0, 0));
+    st.b = (u32x4){w.x, w.y, 0u, 0u};
+  } else if constexpr (!ND) {
     const int c = t >> 2, kc = (t & 3) * 16;
     const uint32_t v = (c < ln.cols) & (k0 + kc < kend) ? (uint32_t)(c * (int)a.k + k0 + kc) : BUF_OOB;
     st.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, v, 0, 0));
@@ -203,7 +254,7 @@ struct W8Scales {
   uint16_t s[2][W8_BN], o[2][W8_BN];
 };
 
-template <int ACT, bool ND>
+template <int ACT, bool ND, bool B4>
 __device__ __forceinline__ void store_stage(const W8Stage& st, uint16_t* As, uint16_t* Bs, W8Scales& ss) {
   const int t = threadIdx.x & 255;
   if (t < 128) {
@@ -218,7 +269,8 @@ __device__ __forceinline__ void store_stage(const W8Stage& st, uint16_t* As, uin
   if constexpr (!ND) {
     const int c = t >> 2, kc = (t & 3) * 16;
     u32x4 lo, hi;
-    convert_k16<ACT>(st.b, lo, hi);
+    if constexpr (B4) convert_n16<ACT>(st.b.x, st.b.y, lo, hi);
+    else convert_k16<ACT>(st.b, lo, hi);
     *reinterpret_cast<u32x4*>(Bs + c * W8_LDS + kc) = lo;
     *reinterpret_cast<u32x4*>(Bs + c * W8_LDS + kc + 8) = hi;
   } else {
@@ -284,7 +336,7 @@ __device__ __forceinline__ void compute_stage(const W8Args& a, const uint16_t* A
   }
 }
 
-template <int ACT, bool ND>
+template <int ACT, bool ND, bool B4>
 __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   // per slice: x1 and weight tiles, double-buffered, and the fold scales;
   // after the K loop the tiles hold the slices' sums
@@ -304,7 +356,8 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   ln.rows = (int)(a.m - m0 < W8_BM ? a.m - m0 : W8_BM);
   ln.cols = (int)(a.n - n0 < W8_BN ? a.n - n0 : W8_BN);
   ln.x = buf_rsrc(a.x1 + m0 * a.k, (uint32_t)(ln.rows * a.k * 2));
-  if constexpr (ND) ln.w = buf_rsrc(a.x2 + n0, (uint32_t)((a.k - 1) * a.n + ln.cols));
+  if constexpr (B4) ln.w = buf_rsrc(a.x2 + n0 * 64, (uint32_t)(((a.k + 127) / 128 * a.np - n0) * 64));
+  else if constexpr (ND) ln.w = buf_rsrc(a.x2 + n0, (uint32_t)((a.k - 1) * a.n + ln.cols));
   else ln.w = buf_rsrc(a.x2 + n0 * a.k, (uint32_t)(ln.cols * a.k));
   ln.s = buf_rsrc(a.scale, a.s_bytes);
   ln.o = buf_rsrc(a.offset ? a.offset : a.scale, a.s_bytes);
@@ -339,19 +392,19 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   FoldPos fl = {u0 % a.upg, u0 / a.upg};
   FoldPos fc = fl;
   W8Stage sa, sb;
-  load_stage<ND>(a, ln, n0, kend, kb, fl, sa);
-  load_stage<ND>(a, ln, n0, kend, kb + W8_BK, fl, sb);
-  store_stage<ACT, ND>(sa, A0, B0, Ss[q][0]);
+  load_stage<ND, B4>(a, ln, n0, kend, kb, fl, sa);
+  load_stage<ND, B4>(a, ln, n0, kend, kb + W8_BK, fl, sb);
+  store_stage<ACT, ND, B4>(sa, A0, B0, Ss[q][0]);
   __syncthreads();
   for (int s = 0; s < sps; s += 2) {
     const int k0 = kb + s * W8_BK;
-    load_stage<ND>(a, ln, n0, kend, k0 + 2 * W8_BK, fl, sa);
+    load_stage<ND, B4>(a, ln, n0, kend, k0 + 2 * W8_BK, fl, sa);
     compute_stage<ACT>(a, A0, B0, Ss[q][0], kend, k0, fc, z);
-    store_stage<ACT, ND>(sb, A1, B1, Ss[q][1]);
+    store_stage<ACT, ND, B4>(sb, A1, B1, Ss[q][1]);
     __syncthreads();
-    load_stage<ND>(a, ln, n0, kend, k0 + 3 * W8_BK, fl, sb);
+    load_stage<ND, B4>(a, ln, n0, kend, k0 + 3 * W8_BK, fl, sb);
     compute_stage<ACT>(a, A1, B1, Ss[q][1], kend, k0 + W8_BK, fc, z);
-    store_stage<ACT, ND>(sa, A0, B0, Ss[q][0]);
+    store_stage<ACT, ND, B4>(sa, A0, B0, Ss[q][0]);
     __syncthreads();
   }
 
@@ -432,6 +485,7 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
   a.m = p.m;
   a.k = p.k;
   a.n = p.n;
+  a.np = 16 * ((p.n + 15) / 16);
   const int64_t group = p.group >= p.k ? p.k : p.group;
   a.upg = p.group >= p.k ? INT32_MAX : (int)(group / 32);
   a.s_row = p.s_row;
@@ -440,8 +494,9 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
   a.s_bytes = (uint32_t)(((groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
   const dim3 grid((unsigned)((p.n + W8_BN - 1) / W8_BN), (unsigned)((p.m + W8_BM - 1) / W8_BM));
   prof_begin(s);
-  if (p.transpose_x2) gemm_w8<ACT, false><<<grid, 256 * W8_KS, 0, s>>>(a);
-  else gemm_w8<ACT, true><<<grid, 256 * W8_KS, 0, s>>>(a);
+  if (p.w_bits == 4) gemm_w8<ACT, false, true><<<grid, 256 * W8_KS, 0, s>>>(a);
+  else if (p.transpose_x2) gemm_w8<ACT, false, false><<<grid, 256 * W8_KS, 0, s>>>(a);
+  else gemm_w8<ACT, true, false><<<grid, 256 * W8_KS, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError();
 }
@@ -451,7 +506,13 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
 // INT8 weights, k a multiple of 16 (16-byte loads never straddle a row of
 // x1 or of the transposed weight); row-major weights with n a multiple of 4
 // (4-byte column groups) and below 2 GiB (one buffer resource).
+// INT4 GFX950_B weights (the shapes the prefill tile does not take: groups
+// of 32, 64 or any multiple of 32 not dividing 128, or k not a multiple of
+// 128): k a multiple of 16, the packed weight below 2 GiB.
 bool w8_ok(const WqProblem& p) {
+  if (p.w_bits == 4)
+    return p.layout == WQ_LAYOUT_GFX950_B && p.k % 16 == 0 &&
+           (p.k + 127) / 128 * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
   if (p.w_bits != 8 || p.k % 16 != 0) return false;
   if (p.transpose_x2) return true;
   return p.n % 4 == 0 && p.k * p.n < (int64_t(1) << 31);

@@ -133,7 +133,7 @@ def test_decode_graph_of_rotating_weights():
 
 
 @pytest.mark.parametrize("shape", [(256, 1024, 1024, 128), (96, 512, 640, 32)],
-                         ids=["prefill-tile-g128", "generic-g32"])
+                         ids=["prefill-tile-g128", "int8-tile-int4-g32"])
 def test_prefill_and_generic_call_replays(shape):
     m, k, n, g = shape
     note(f"graph: wq {m}x{k}x{n} g={g}")

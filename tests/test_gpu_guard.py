@@ -52,12 +52,13 @@ class Guarded:
 
 
 WQ_CASES = [  # m, k, n, act, granularity, group, layout, transpose, inplace
-    (17, 256, 40, torch.float16, "group", 32, wq.WQ_LAYOUT_GFX950_B, False, False),   # generic tile
+    (17, 256, 40, torch.float16, "group", 32, wq.WQ_LAYOUT_GFX950_B, False, False),   # decode kernel, group 32
     (5, 384, 130, torch.bfloat16, "group", 128, wq.WQ_LAYOUT_GFX950_B, False, True),  # decode kernel
     (21, 512, 200, torch.float16, "channel", 0, wq.WQ_LAYOUT_GFX950_B, False, False), # decode, 2 launches
     (130, 512, 520, torch.bfloat16, "group", 128, wq.WQ_LAYOUT_GFX950_B, False, True),  # prefill, masked strip
     (33, 256, 90, torch.bfloat16, "group", 64, wq.WQ_LAYOUT_ND, False, False),        # ND
     (70, 256, 48, torch.float16, "channel", 0, wq.WQ_LAYOUT_ND, True, False),          # INT4 ND transposed
+    (70, 336, 132, torch.bfloat16, "group", 32, wq.WQ_LAYOUT_GFX950_B, False, True),   # INT8 tile, INT4 weight
 ]
 
 

@@ -134,6 +134,58 @@ W8_DECODE = [  # m <= 32, INT8 stored (n, k), k % 128 == 0: the weight stream
 ]
 
 
+W4_TILE = [  # m, k, n, granularity, group, offset, bias, act: INT4 GFX950_B weights on the
+    # INT8 tile's structure (groups of 32 / 64 / odd multiples of 32 with m > 32, and
+    # k not a multiple of 128 at any m)
+    (300, 1024, 200, "group", 32, (-0.5, 0.5), 0.1, torch.bfloat16),
+    (130, 2048, 520, "group", 64, (-1.0, 1.0), None, torch.float16),
+    (65, 768, 1000, "group", 96, "none", 0.1, torch.bfloat16),        # folds mid-step
+    (513, 512, 136, "group", 32, None, 0.1, torch.float16),
+    (40, 208, 132, "group", 32, (-1.0, 1.0), 0.1, torch.bfloat16),    # k % 128 != 0, last step 16 deep
+    (7, 336, 70, "channel", 0, (-0.5, 0.5), 0.1, torch.float16),      # decode-sized m, k % 128 != 0
+    (96, 4096, 512, "group", 160, (-1.0, 1.0), 0.1, torch.float16),
+    (200, 80, 48, "tensor", 0, "none", None, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", W4_TILE, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in W4_TILE])
+def test_int4_on_the_int8_tile(shape):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"w4tile{m}x{k}x{n}", m, k, n, act=act, w_bits=4, granularity=gran,
+                          group_size=g, offset_range=off, bias_std=bias, seed=7 * m + k + n)
+    note(f"wq int4 on the INT8 tile {c.name} {gran} g={g} {act}")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
+    y2, n2 = wq_on_gpu(c, inplace=True)
+    assert torch.equal(y, y2) and torch.equal(nrm, n2)
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_int4_short_group_zero_scales(G):
+    # a zero group scale leaves only the offset for that group and column
+    m, k, n = 100, 1024, 300
+    c = workloads.wq_case(f"w4tile_zero_g{G}", m, k, n, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=G, scale_range=(0.002, 0.02),
+                          offset_range=(-1.0, 1.0), bias_std=0.1, seed=19 + G)
+    c.scale[1, :] = 0
+    c.scale[:, 5] = 0
+    c.scale[c.scale.shape[0] - 1, 77] = 0
+    note(f"wq int4 INT8-tile zero scales g={G}")
+    y, nrm = wq_on_gpu(c)
+    check_wq(c, y, nrm)
+
+
+def test_int4_short_group_prefill_rows_sampled():
+    # the prefill shape at group 64 (4096 x 8192 x 8192, bf16): 24 sampled rows
+    c = workloads.wq_case("w4tile prefill g64", 4096, 8192, 8192, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=64, scale_range=(0.002, 0.02),
+                          offset_range=(-0.5, 0.5), bias_std=0.1, seed=5)
+    note("wq int4 INT8-tile prefill 4096x8192x8192 g64")
+    y, nrm = wq_on_gpu(c)
+    rows = np.random.default_rng(9).choice(4096, size=24, replace=False)
+    check_wq(c, y, nrm, rows=rows)
+
+
 @pytest.mark.parametrize("shape", W8_DECODE, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in W8_DECODE])
 def test_int8_decode_shapes(shape):
     m, k, n, gran, g, off, bias, act = shape
@@ -429,7 +481,8 @@ ONE_SIGN = [  # m, k, n, granularity, group, offset, act
     (16, 8192, 1024, "group", 128, None, torch.float16),        # decode kernel
     (16, 8192, 1024, "group", 128, None, torch.bfloat16),
     (1, 8192, 1024, "channel", 0, (-0.1, 0.1), torch.float16),
-    (40, 8192, 256, "group", 64, None, torch.float16),          # generic tile (group 64)
+    (40, 8192, 256, "group", 64, None, torch.float16),          # INT8 tile, INT4 weights (group 64)
+    (40, 8192, 256, "group", 32, (-0.1, 0.1), torch.bfloat16),  # INT8 tile, INT4 weights (group 32)
 ]
 ONE_SIGN_W8 = [  # the INT8 tile: one group over all of K, and group 64; m <= 32 the
     # weight stream when transposed
