@@ -539,7 +539,7 @@ def main():
 
     # ---------------- achievable ceilings on this GPU (context, not targets) -------------
     ceilings = None
-    if not args.no_ceilings and not only:
+    if not args.no_ceilings and (not only or "ceilings" in only):
         ceilings = {}
         # vendor dense bf16 GEMM (hipBLASLt via torch.matmul) at the prefill shape
         xa = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
