@@ -92,6 +92,8 @@ extern "C" wq_status wq_ceiling_stream_read(const void* src, size_t bytes, uint3
   const size_t words = wq_ceiling_stream_read_words(bytes);
   if (words == 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 3) != 0)
     return WQ_ERR_SHAPE;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), o0 = reinterpret_cast<uintptr_t>(out);
+  if (o0 < s0 + bytes && s0 < o0 + words * 4) return WQ_ERR_ALIAS;
   const size_t grid = words / (wq::SR_THREADS / 64);
   if (grid > 0xFFFFFFFFull) return WQ_ERR_SHAPE;
   wq::stream_read_kernel<<<dim3((unsigned)grid), wq::SR_THREADS, 0, stream>>>(

@@ -469,7 +469,8 @@ wq_status wq_profile_read(float* times_ms, int64_t capacity, int64_t* launches);
  * memory, caller-owned, floats), the same for every workgroup.
  *
  * Errors: WQ_ERR_NULLPTR; WQ_ERR_SHAPE (sizes or alignment as above;
- * workgroups outside [1, 2^20], iters outside [1, 16384]); WQ_ERR_LAUNCH.
+ * workgroups outside [1, 2^20], iters outside [1, 16384]); WQ_ERR_ALIAS
+ * (the stream read's out overlapping src); WQ_ERR_LAUNCH.
  * ---------------------------------------------------------------------- */
 size_t wq_ceiling_stream_read_words(size_t bytes);
 wq_status wq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* out, hipStream_t stream);

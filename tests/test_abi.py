@@ -399,6 +399,7 @@ def test_ceiling_microkernels_validate_on_the_host():
     assert L.wq_ceiling_stream_read(FAKE, 24, FAKE2, None) == wq.WQ_ERR_SHAPE
     assert L.wq_ceiling_stream_read(FAKE + 8, 16, FAKE2, None) == wq.WQ_ERR_SHAPE
     assert L.wq_ceiling_stream_read(FAKE, 16, FAKE2 + 2, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_ceiling_stream_read(FAKE, 1 << 20, FAKE + 4096, None) == wq.WQ_ERR_ALIAS
     assert L.wq_ceiling_mfma_loop(1, 1, None, None) == wq.WQ_ERR_NULLPTR
     assert L.wq_ceiling_mfma_loop(0, 1, FAKE, None) == wq.WQ_ERR_SHAPE
     assert L.wq_ceiling_mfma_loop((1 << 20) + 1, 1, FAKE, None) == wq.WQ_ERR_SHAPE
