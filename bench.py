@@ -13,6 +13,8 @@ The operators built on the path run after the steps, in a loop of their
 own with the same warm-up and step counts, reported under ``extras``:
   wq_weight_quant_matmul + wq_add_rms_norm   the unfused chain on row 2's
                            inputs: matmul (4096, 8192) bf16, then AddRmsNorm
+  wq_matmul_add_rmsnorm    row 2's call with 64-deep groups (the short-group
+                           path)
   wq_quant_matmul_inplace_add  y (4096, 4096) fp32 += INT8 (row 3's output)
                            x INT8 weight (4096, 8192), per-token x per-channel
   wq_quant_matmul_inplace_add_w4  the same with an INT4 weight: row 5's packed
@@ -56,6 +58,7 @@ PEAK_FP4_TFLOPS = 10066.3      # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rows whose call launches one contraction kernel that the library times
 CONTRACTION_ROWS = {"wq_matmul_add_rmsnorm": "gemm_b_wide", "weight_quant_matmul": "gemm_b_wide",
+                    "wq_matmul_add_rmsnorm_g64": "gemm_w8",
                     "mx_matmul_inplace_add": "mx_gemm_tile",
                     "quant_matmul_inplace_add_int8": "i8_gemm_tile",
                     "mxfp4_matmul_inplace_add": "mx4_gemm_tile",
@@ -208,6 +211,17 @@ def main():
     def op_arn():
         wq.wq_add_rms_norm(mm_out, residual, gamma, M, N, wq.WQ_BF16, pf.eps, y2, norm2)
 
+    # the fused call on the same inputs with 64-deep groups (the short-group
+    # path: INT4 weights on the INT8 tile), scales drawn like the prefill's
+    scale64 = torch.from_numpy(np.random.default_rng(64).uniform(0.002, 0.02, (K // 64, N)).astype(np.float32)
+                               ).to(torch.bfloat16).to(dev)
+    y64, norm64 = torch.empty_like(residual), torch.empty_like(residual)
+
+    def op_wq64():
+        wq.wq_matmul_add_rmsnorm(x1, M, K, wq.WQ_BF16, x2, N, wq.WQ_INT4, wq.WQ_LAYOUT_GFX950_B, 0,
+                                 scale64, scale64.shape[0], scale64.shape[1], None, 64, bias, residual,
+                                 gamma, pf.eps, y64, norm64, ws, ws_n)
+
     def op_quant_tok():
         wq.wq_dynamic_quant(xq_in, wq.WQ_F16, MM, MK, smooth, wq.WQ_INT8, 0, 0, q8, q8s)
 
@@ -262,6 +276,8 @@ def main():
         ("weight_quant_matmul", op_wqbmm, 2 * M * N * K,
          x1.numel() * 2 + x2.numel() + 2 * scale.numel() * 2 + N * 2 + M * N * 2, "mfma"),
         ("add_rms_norm", op_arn, 0, 4 * M * N * 2 + N * 2, "hbm"),
+        ("wq_matmul_add_rmsnorm_g64", op_wq64, 2 * M * N * K,
+         x1.numel() * 2 + x2.numel() + scale64.numel() * 2 + N * 2 * 2 + 3 * M * N * 2, "mfma"),
         ("dynamic_quant_int8", op_quant_tok, 0, MM * MK * 2 + MK * 2 + MM * MK + MM * 4, "hbm"),
         ("dynamic_quant_mx", op_quant_mx, 0, MM * MK * 2 + MK * 2 + MM * MK + s1.numel(), "hbm"),
         ("mx_matmul_inplace_add", op_mx, 2 * MM * MN * MK,
@@ -280,7 +296,7 @@ def main():
     # quants, the MX GEMM); the rows built on it (the unfused chain, the INT8
     # and MXFP4 paths) run as extras in a loop of their own, so that their
     # dense GEMMs do not heat the GPU under the step's rows
-    EXTRA = {"weight_quant_matmul", "add_rms_norm", "quant_matmul_inplace_add_int8",
+    EXTRA = {"weight_quant_matmul", "add_rms_norm", "wq_matmul_add_rmsnorm_g64", "quant_matmul_inplace_add_int8",
              "quant_matmul_inplace_add_w4", "quant_matmul_inplace_add_a4w4", "dynamic_quant_mx_e2m1",
              "mxfp4_matmul_inplace_add"}
     core = [r for r in rows if want(r[0]) and r[0] not in EXTRA]
@@ -349,6 +365,7 @@ def main():
                 d["kernel_ms"] = round(km, 5)
                 d["kernel_TFLOP/s"] = round(flop / km / 1e9, 2)
             peak = {"wq_matmul_add_rmsnorm": PEAK_BF16_TFLOPS, "weight_quant_matmul": PEAK_BF16_TFLOPS,
+                    "wq_matmul_add_rmsnorm_g64": PEAK_BF16_TFLOPS,
                     "quant_matmul_inplace_add_int8": PEAK_INT8_TOPS,
                     "quant_matmul_inplace_add_w4": PEAK_INT8_TOPS,
                     "quant_matmul_inplace_add_a4w4": PEAK_INT8_TOPS,
