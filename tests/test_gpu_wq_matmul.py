@@ -145,6 +145,7 @@ W4_TILE = [  # m, k, n, granularity, group, offset, bias, act: INT4 GFX950_B wei
     (7, 336, 70, "channel", 0, (-0.5, 0.5), 0.1, torch.float16),      # decode-sized m, k % 128 != 0
     (96, 4096, 512, "group", 160, (-1.0, 1.0), 0.1, torch.float16),
     (200, 80, 48, "tensor", 0, "none", None, torch.bfloat16),
+    (40, 65520, 64, "group", 32, (-0.5, 0.5), 0.1, torch.float16),    # the largest k: 2048 groups
 ]
 
 
