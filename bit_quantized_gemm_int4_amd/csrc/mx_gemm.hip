@@ -16,7 +16,8 @@
 // a B fragment is one 16-byte load. A arrives K-major.
 //
 // Two kernels:
-//   - mx_gemm_tile: M, N multiples of 256 and K a multiple of 128. A
+//   - mx_gemm_tile: M, N multiples of 256 and K a multiple of 128 (RG: any
+//     M a multiple of 16, N and K, through bounded buffer resources). A
 //     256 x 256 workgroup tile, 8 waves of 64 (m) x 128 (n). Per 128-deep
 //     step the x1 tile (128 k-rows x 256 m bytes), the weight slab (256
 //     columns x 64 bytes) and both scale tiles move by direct global->LDS DMA,
@@ -28,8 +29,9 @@
 //     m0 + i. The x1 rows' 16-byte chunks are XOR-swizzled by k so that the
 //     32 rows one such read touches spread over all LDS banks. The
 //     accumulators start as y, so the in-place add costs no extra pass.
-//   - mx_gemm_kernel: any shape (partial K blocks, ragged M and N); a small
-//     64 x 64 tile that transposes A byte-wise.
+//   - mx_gemm_kernel: the shapes the tile does not take (M not a multiple of
+//     16 without a workspace for a padded x1 copy, offsets past 2 GiB); a
+//     small 64 x 64 tile that transposes A byte-wise.
 #include <utility>
 
 #include "wq_device.h"
@@ -156,8 +158,10 @@ __device__ __forceinline__ void mf_dma4(__amdgpu_buffer_rsrc_t r, uint8_t* dst, 
 // (x1: 4 KiB in four 1 KiB pieces; weights: 2 KiB; one 256-byte scale row).
 // With RG, waves 0..3 read their scale1 bytes with byte loads instead (issued
 // first, so that their wait does not cover the DMA) and return them packed;
-// the caller writes them to LDS before the step's closing barrier.
-template <bool RG>
+// the caller writes them to LDS before the step's closing barrier. With ON
+// (N not a multiple of 4: scale2 rows not 4-byte aligned) waves 4..7 do the
+// same for their scale2 bytes.
+template <bool RG, bool ON>
 __device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, int64_t Mx, int64_t N,
                                            int64_t Np, int64_t KB, int64_t m0, int64_t n0, int step,
                                            int wave, int lane) {
@@ -171,6 +175,14 @@ __device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, i
         const int64_t blk = 4 * (int64_t)step + b;
         const uint32_t off = blk < KB ? (uint32_t)(row * KB + blk) : BUF_OOB;
         s1w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(src.rs1, off, 0, 0) << (8 * b);
+      }
+    } else if (ON) {
+      const int64_t blk = 4 * (int64_t)step + (wave - 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t col = n0 + 4 * lane + b;
+        const uint32_t off = blk < KB && col < N ? (uint32_t)(blk * N + col) : BUF_OOB;
+        s1w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(src.rs2, off, 0, 0) << (8 * b);
       }
     }
   }
@@ -209,7 +221,9 @@ __device__ __forceinline__ uint32_t mf_dma(const MfSrc& src, const MfBufs& bf, i
       __builtin_amdgcn_global_load_lds((glb_void*)(src.s1 + (m0 + 64 * wave + lane) * KB + 4 * step),
                                        (lds_void*)(bf.s1 + wave * 256), 4, 0, 0);
   } else {          // scale2 block row 4 step + (wave - 4), columns n0 .. n0 + 255
-    if constexpr (RG)
+    if constexpr (ON)
+      ;                // byte loads above
+    else if constexpr (RG)
       mf_dma4(src.rs2, bf.s2 + (wave - 4) * 256, (uint32_t)((4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane));
     else
       __builtin_amdgcn_global_load_lds((glb_void*)(src.s2 + (4 * (int64_t)step + (wave - 4)) * N + n0 + 4 * lane),
@@ -231,7 +245,7 @@ __device__ __forceinline__ void mf_row(f32x4 (&acc)[8], const i32x8& af, const u
 
 // The tiles cover the (M, N) output, all of K; x1's rows are Mx >= M bytes
 // apart (Mx = M, or M padded to 16 in a workspace copy).
-template <bool RG>
+template <bool RG, bool ON>
 __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict__ x1t,
                                                        const uint8_t* __restrict__ x2,
                                                        const uint8_t* __restrict__ s1,
@@ -278,10 +292,18 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   const __amdgpu_buffer_rsrc_t ry = buf_rsrc(y, (uint32_t)(M * N * 4));
   const uint32_t yl = (uint32_t)((4 * (lane >> 4)) * N + 8 * (lane & 15)) * 4u;
   const uint32_t yw = (uint32_t)(((m0 + 64 * wm) * N + n0 + 128 * wn) * 4);
-  // with a ragged shape, rows past M and 4-column runs past N (N % 4 == 0)
-  // are neither read nor written: out-of-range offsets
+  // with a ragged shape, rows past M and 4-column runs past N (N % 4 == 0;
+  // otherwise ON, below) are neither read nor written: out-of-range offsets
   auto y_ok = [&](int i, int r, int h) {
     return m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r < M && n0 + 128 * wn + 8 * (lane & 15) + 4 * h < N;
+  };
+  // ON: y rows are only 4-byte aligned. A 4-column run inside the row still
+  // moves as one 16-byte access (dword-aligned multi-dword buffer accesses
+  // are supported on this target); the run that crosses N moves element by
+  // element. Every access is issued, the ones not taken with an
+  // out-of-range offset (no traffic), so no lane branches.
+  auto y_el_ok = [&](int i, int r, int c) {
+    return m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r < M && n0 + 128 * wn + 8 * (lane & 15) + c < N;
   };
   f32x4 acc[4][8];
 #pragma unroll
@@ -289,21 +311,42 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
+      if constexpr (ON) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t vo = RG && !y_ok(i, r, h) ? BUF_OOB : yl + 16u * h;
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, vo, so, 0));
-        acc[i][4 * h + 0][r] = __uint_as_float(v.x);
-        acc[i][4 * h + 1][r] = __uint_as_float(v.y);
-        acc[i][4 * h + 2][r] = __uint_as_float(v.z);
-        acc[i][4 * h + 3][r] = __uint_as_float(v.w);
+        for (int h = 0; h < 2; ++h) {
+          const bool full = y_el_ok(i, r, 4 * h + 3);
+          const u32x4 v = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, full ? yl + 16u * h : BUF_OOB, so, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t vo = !full && y_el_ok(i, r, 4 * h + e) ? yl + 16u * h + 4u * e : BUF_OOB;
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(ry, vo, so, 0);
+            acc[i][4 * h + e][r] = __uint_as_float(full ? v[e] : w);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t vo = RG && !y_ok(i, r, h) ? BUF_OOB : yl + 16u * h;
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, vo, so, 0));
+          acc[i][4 * h + 0][r] = __uint_as_float(v.x);
+          acc[i][4 * h + 1][r] = __uint_as_float(v.y);
+          acc[i][4 * h + 2][r] = __uint_as_float(v.z);
+          acc[i][4 * h + 3][r] = __uint_as_float(v.w);
+        }
       }
     }
 
+  // (the byte-loaded scale words go to LDS: scale1 rows for waves 0..3, with
+  // ON the scale2 rows for waves 4..7)
+  auto put_sw = [&](const MfBufs& b, uint32_t w) {
+    if (RG && wave < 4) *reinterpret_cast<uint32_t*>(b.s1 + wave * 256 + 4 * lane) = w;
+    if (ON && wave >= 4) *reinterpret_cast<uint32_t*>(b.s2 + (wave - 4) * 256 + 4 * lane) = w;
+  };
   {
-    const uint32_t s1w = mf_dma<RG>(src, buf0, Mx, N, Np, KB, m0, n0, 0, wave, lane);
+    const uint32_t s1w = mf_dma<RG, ON>(src, buf0, Mx, N, Np, KB, m0, n0, 0, wave, lane);
     wait_vm<0>();
-    if (RG && wave < 4) *reinterpret_cast<uint32_t*>(buf0.s1 + wave * 256 + 4 * lane) = s1w;
+    put_sw(buf0, s1w);
   }
   __syncthreads();
 
@@ -324,7 +367,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
   // `nxt` and frees `cur`, which the next step's DMA refills.
   auto do_step = [&](int step, const MfBufs& cur, const MfBufs& nxt) {
     uint32_t s1w = 0;
-    if (step + 1 < steps) s1w = mf_dma<RG>(src, nxt, Mx, N, Np, KB, m0, n0, step + 1, wave, lane);
+    if (step + 1 < steps) s1w = mf_dma<RG, ON>(src, nxt, Mx, N, Np, KB, m0, n0, step + 1, wave, lane);
     u32x4 bv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const u32x4*>(cur.b + boff + 1024 * j);
@@ -343,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
       mf_row(acc[i], af, bv, sa, sbw, std::make_integer_sequence<int, 8>{});
     }
     wait_vm<0>();            // this wave's DMA into `nxt` has landed
-    if (RG && wave < 4 && step + 1 < steps) *reinterpret_cast<uint32_t*>(nxt.s1 + wave * 256 + 4 * lane) = s1w;
+    if (step + 1 < steps) put_sw(nxt, s1w);
     __syncthreads();
   };
   for (int step = 0; step < steps; step += 2) {
@@ -356,6 +399,24 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_tile(const uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t so = yw + (uint32_t)((16 * i + r) * N * 4);
+      if constexpr (ON) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool full = y_el_ok(i, r, 4 * h + 3);
+          u32x4 v;
+          v.x = __float_as_uint(acc[i][4 * h + 0][r]);
+          v.y = __float_as_uint(acc[i][4 * h + 1][r]);
+          v.z = __float_as_uint(acc[i][4 * h + 2][r]);
+          v.w = __float_as_uint(acc[i][4 * h + 3][r]);
+          __builtin_amdgcn_raw_buffer_store_b128(v, ry, full ? yl + 16u * h : BUF_OOB, so, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t vo = !full && y_el_ok(i, r, 4 * h + e) ? yl + 16u * h + 4u * e : BUF_OOB;
+            __builtin_amdgcn_raw_buffer_store_b32(v[e], ry, vo, so, 0);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         u32x4 v;
@@ -385,16 +446,18 @@ __global__ __launch_bounds__(256) void mx_pad_x1(const uint8_t* __restrict__ x1t
   *reinterpret_cast<u32x4*>(out + k * Mx + 16 * c) = (u32x4){w[0], w[1], w[2], w[3]};
 }
 
-// The 256 x 256 tile takes x1 rows of 16-byte chunks (Mx % 16), 4-byte
-// scale2 pieces and 16-byte y runs (N % 4), y below 2 GiB (one buffer
-// resource); a ragged shape also needs every input, and every offset its last
-// step and its last tile row and column form past the inputs, below 2 GiB.
+// The 256 x 256 tile takes x1 rows of 16-byte chunks (Mx % 16) and y below
+// 2 GiB (one buffer resource); a ragged shape also needs every input, and
+// every offset its last step and its last tile row and column form past the
+// inputs, below 2 GiB. N not a multiple of 4 (scale2 and y rows not 4- and
+// 16-byte aligned) runs the ragged tile's ON form: scale2 by byte loads, y
+// in dword-aligned 16-byte runs and element by element where a run crosses N.
 bool mx_tile_ok(int64_t m, int64_t mx, int64_t k, int64_t n) {
   const int64_t lim = int64_t(1) << 31;
   const int64_t Np = 16 * ((n + 15) / 16);
   const int64_t KB = (k + 31) / 32, steps = (k + MF_BK - 1) / MF_BK;
   const bool aligned = m % MF_BM == 0 && n % MF_BN == 0 && k % MF_BK == 0 && mx == m;
-  return mx % 16 == 0 && n % 4 == 0 && m * n * 4 < lim &&
+  return mx % 16 == 0 && m * n * 4 < lim &&
          (aligned || ((steps + 1) * MF_BK * mx < lim && (m + MF_BM) * KB < lim && (KB + 8) * n < lim &&
                       steps * Np * 64 < lim));
 }
@@ -424,11 +487,14 @@ hipError_t launch_mx_matmul(const MxProblem& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (mx_tile_ok(p.m, mx, p.k, p.n) && aligned && !pad) {
-    mx_gemm_tile<false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx, p.k, p.n,
-                                                                Np, tm, tn);
+    mx_gemm_tile<false, false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx,
+                                                                       p.k, p.n, Np, tm, tn);
+  } else if (mx_tile_ok(p.m, mx, p.k, p.n) && p.n % 4 == 0) {
+    mx_gemm_tile<true, false><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx,
+                                                                      p.k, p.n, Np, tm, tn);
   } else if (mx_tile_ok(p.m, mx, p.k, p.n)) {
-    mx_gemm_tile<true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx, p.k, p.n,
-                                                               Np, tm, tn);
+    mx_gemm_tile<true, true><<<dim3((unsigned)(tm * tn)), 512, 0, s>>>(x1, p.x2, p.s1, p.s2, p.y, p.m, mx,
+                                                                     p.k, p.n, Np, tm, tn);
   } else {
     dim3 grid((unsigned)((p.n + MX_BN - 1) / MX_BN), (unsigned)((p.m + MX_BM - 1) / MX_BM));
     mx_gemm_kernel<<<grid, 256, 0, s>>>(p.x1, p.x2, p.s1, p.s2, p.y, p.m, p.k, p.n, Np, 0, 0, p.n);

@@ -120,7 +120,7 @@ def _e4m3_codes(shape, gen):
     return c.to(torch.uint8)
 
 
-@pytest.mark.parametrize("m,k,n", [(80, 80, 48), (256, 128, 256)])
+@pytest.mark.parametrize("m,k,n", [(80, 80, 48), (256, 128, 256), (80, 80, 50), (272, 200, 263)])
 def test_mx_gemm_guards(m, k, n):
     gen = torch.Generator().manual_seed(7)
     kb = (k + 31) // 32

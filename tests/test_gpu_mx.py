@@ -91,12 +91,14 @@ def _codes(rng, k, m, n, s_lo=118, s_hi=134):
 # multiples of 256 (a last tile row / column mostly outside the output); with
 # M % 16 != 0 ((70, 80, 20), (130, 416, 96), (300, 256, 300)) the binding
 # passes the queried workspace and the tile runs on a padded copy of x1; N % 4
-# != 0 ((33, 7, 17), (1, 32, 2)) takes the small tile
+# != 0 ((33, 7, 17), (1, 32, 2), (272, 384, 262), (48, 2080, 517),
+# (300, 256, 301)) moves y one element at a time and scale2 by byte loads
 @pytest.mark.parametrize("m,k,n", [(64, 128, 64), (16, 256, 16), (70, 80, 20), (130, 416, 96),
                                    (1, 32, 2), (33, 7, 17), (256, 1024, 256), (256, 128, 512),
                                    (512, 384, 768), (768, 2048, 256),
                                    (256, 7, 256), (256, 200, 256), (512, 1000, 256), (272, 384, 260),
-                                   (528, 1056, 772), (16, 128, 4), (48, 2080, 516), (300, 256, 300)])
+                                   (528, 1056, 772), (16, 128, 4), (48, 2080, 516), (300, 256, 300),
+                                   (272, 384, 262), (48, 2080, 517), (300, 256, 301)])
 def test_random_codes(m, k, n):
     note(f"mx random codes {m}x{k}x{n}")
     rng = np.random.default_rng(m * k + n)
@@ -114,7 +116,7 @@ def test_random_codes(m, k, n):
 
 
 @pytest.mark.parametrize("m,k,n", [(64, 256, 64), (70, 80, 20), (256, 1024, 256), (512, 384, 768),
-                                   (256, 200, 256), (528, 1000, 772)])
+                                   (256, 200, 256), (528, 1000, 772), (272, 384, 262), (80, 96, 41)])
 def test_codes_inside_the_alignment_windows_are_exact(m, k, n):
     # Random codes at unit scale with E4M3 exponent field 5..9 (|a| in
     # [0.25, 7.5], multiples of 2^-5, exponents -2..2) and nonzero E2M1 codes
