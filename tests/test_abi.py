@@ -63,7 +63,8 @@ def test_size_queries():
     assert wq.mx_quant_matmul_inplace_add_workspace_size(4096, 8192, 4096) == 0
     # m % 16 != 0: room for x1 with rows padded to 16 bytes (k x 16 ceil(m/16)), 256-byte rounded
     assert wq.mx_quant_matmul_inplace_add_workspace_size(4100, 8192, 4100) == 8192 * 4112
-    assert wq.mx_quant_matmul_inplace_add_workspace_size(33, 7, 17) == 0          # n % 4: small tile
+    # m % 16 != 0 with n % 4 != 0: the tile on a padded x1 copy, 7 x 48 bytes rounded to 256
+    assert wq.mx_quant_matmul_inplace_add_workspace_size(33, 7, 17) == 512
     assert wq.mx_quant_matmul_inplace_add_workspace_size(33, 7, 16) == 512        # 7 x 48 = 336 -> 512
     assert wq.mx_quant_matmul_inplace_add_workspace_size(0, 7, 16) == 0
 
