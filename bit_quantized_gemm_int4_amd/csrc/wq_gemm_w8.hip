@@ -1,8 +1,9 @@
 // INT8-weight tile of the weight-quantized matmul + AddRmsNorm
 // (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula; x2 int8 (k, n)
 // or its transpose (n, k), Constraints section), also run on INT4 weights
-// in the GFX950_B layout (B4) for the groups and K the prefill tile does not
-// take. Same operator and numerics
+// (B4) stored with each column's K codes contiguous: the GFX950_B layout,
+// for the groups and K the prefill tile does not take, and the transposed
+// ND layout ((n, k / 2) bytes). Same operator and numerics
 // as wq_gemm.hip: the codes enter the MFMA as exact 16-bit values q, each
 // group's scale and offset are applied to its float32 partial sums, the
 // epilogue writes y = acc + bias + residual and per-(row, 32-column tile)
@@ -44,7 +45,7 @@ constexpr int W8_LDS = W8_BK + 8;   // halves per LDS row: 144 bytes, conflict-f
 
 struct W8Args {
   const uint16_t* x1;
-  const uint8_t* x2;        // INT8 (k, n) or (n, k); or INT4 GFX950_B (B4)
+  const uint8_t* x2;        // INT8 (k, n) or (n, k); or INT4 (B4): GFX950_B, or ND transposed (n, k / 2)
   const uint16_t* scale;
   const uint16_t* offset;   // may be null
   const uint16_t* bias;     // may be null
@@ -52,7 +53,7 @@ struct W8Args {
   uint16_t* y;
   float* partial;           // [m][ceil(n / 32)]
   int64_t m, k, n, s_row, s_col;
-  int64_t np;               // B4: the padded width of the GFX950_B layout
+  int64_t np;               // B4: the padded width of the GFX950_B layout; 0 for ND transposed
   int upg;                  // 32-deep units per group; INT32_MAX: one group over all of K
   uint32_t s_bytes;
 };
@@ -209,12 +210,12 @@ __device__ __forceinline__ void load_stage(const W8Args& a, const W8Lane& ln, in
   }
   if constexpr (B4) {
     // column c's K values kk .. kk + 15: 8 bytes of its GFX950_B record
-    // (the 32-deep block kk / 32 of 128-deep block kk / 128), the resource
-    // starting at the workgroup's first column
+    // (the 32-deep block kk / 32 of 128-deep block kk / 128), or of its ND
+    // row of k / 2 bytes; the resource starts at the workgroup's first column
     const int c = t >> 2, kk = k0 + (t & 3) * 16;
-    const uint32_t v = (c < ln.cols) & (kk < kend)
-                           ? (uint32_t)((((int64_t)(kk >> 7) * a.np + c) * 64) + ((kk >> 5) & 3) * 16 + ((kk & 31) >> 1))
-                           : BUF_OOB;
+    const uint32_t at = a.np ? (uint32_t)((((int64_t)(kk >> 7) * a.np + c) * 64) + ((kk >> 5) & 3) * 16 + ((kk & 31) >> 1))
+                             : (uint32_t)(c * (a.k >> 1) + (kk >> 1));
+    const uint32_t v = (c < ln.cols) & (kk < kend) ? at : BUF_OOB;
     const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ln.w, v, 0, 0));
     st.b = (u32x4){w.x, w.y, 0u, 0u};
   } else if constexpr (!ND) {
@@ -356,7 +357,9 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   ln.rows = (int)(a.m - m0 < W8_BM ? a.m - m0 : W8_BM);
   ln.cols = (int)(a.n - n0 < W8_BN ? a.n - n0 : W8_BN);
   ln.x = buf_rsrc(a.x1 + m0 * a.k, (uint32_t)(ln.rows * a.k * 2));
-  if constexpr (B4) ln.w = buf_rsrc(a.x2 + n0 * 64, (uint32_t)(((a.k + 127) / 128 * a.np - n0) * 64));
+  if constexpr (B4)
+    ln.w = a.np ? buf_rsrc(a.x2 + n0 * 64, (uint32_t)(((a.k + 127) / 128 * a.np - n0) * 64))
+                : buf_rsrc(a.x2 + n0 * (a.k / 2), (uint32_t)(ln.cols * (a.k / 2)));
   else if constexpr (ND) ln.w = buf_rsrc(a.x2 + n0, (uint32_t)((a.k - 1) * a.n + ln.cols));
   else ln.w = buf_rsrc(a.x2 + n0 * a.k, (uint32_t)(ln.cols * a.k));
   ln.s = buf_rsrc(a.scale, a.s_bytes);
@@ -485,7 +488,7 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
   a.m = p.m;
   a.k = p.k;
   a.n = p.n;
-  a.np = 16 * ((p.n + 15) / 16);
+  a.np = p.layout == WQ_LAYOUT_GFX950_B ? 16 * ((p.n + 15) / 16) : 0;
   const int64_t group = p.group >= p.k ? p.k : p.group;
   a.upg = p.group >= p.k ? INT32_MAX : (int)(group / 32);
   a.s_row = p.s_row;
@@ -508,11 +511,14 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
 // (4-byte column groups) and below 2 GiB (one buffer resource).
 // INT4 GFX950_B weights (the shapes the prefill tile does not take: groups
 // of 32, 64 or any multiple of 32 not dividing 128, or k not a multiple of
-// 128): k a multiple of 16, the packed weight below 2 GiB.
+// 128) and transposed ND INT4 weights: k a multiple of 16, the packed weight
+// below 2 GiB.
 bool w8_ok(const WqProblem& p) {
-  if (p.w_bits == 4)
-    return p.layout == WQ_LAYOUT_GFX950_B && p.k % 16 == 0 &&
-           (p.k + 127) / 128 * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
+  if (p.w_bits == 4) {
+    if (p.k % 16 != 0) return false;
+    if (p.layout == WQ_LAYOUT_GFX950_B) return (p.k + 127) / 128 * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
+    return p.transpose_x2 && p.n * (p.k / 2) < (int64_t(1) << 31);
+  }
   if (p.w_bits != 8 || p.k % 16 != 0) return false;
   if (p.transpose_x2) return true;
   return p.n % 4 == 0 && p.k * p.n < (int64_t(1) << 31);
