@@ -1,9 +1,10 @@
 // INT8-weight tile of the weight-quantized matmul + AddRmsNorm
 // (aclnnWeightQuantMatmulAllReduceAddRmsNorm page, Formula; x2 int8 (k, n)
 // or its transpose (n, k), Constraints section), also run on INT4 weights
-// (B4) stored with each column's K codes contiguous: the GFX950_B layout,
-// for the groups and K the prefill tile does not take, and the transposed
-// ND layout ((n, k / 2) bytes). Same operator and numerics
+// (B4): the GFX950_B layout, for the groups and K the prefill tile does not
+// take, and the ND layout, transposed ((n, k / 2) bytes, each column's K
+// codes contiguous) or row-major ((k, n / 2) bytes, staged like a row-major
+// INT8 weight). Same operator and numerics
 // as wq_gemm.hip: the codes enter the MFMA as exact 16-bit values q, each
 // group's scale and offset are applied to its float32 partial sums, the
 // epilogue writes y = acc + bias + residual and per-(row, 32-column tile)
@@ -138,6 +139,31 @@ __device__ __forceinline__ void convert_n16(uint32_t w0, uint32_t w1, u32x4& lo4
   hi4 = (u32x4){o[4], o[5], o[6], o[7]};
 }
 
+// Four K rows of four INT4 columns (r[i] = row i, nibble j = column j, the
+// ND byte order) -> per column j the four K values as 16-bit q:
+// out[j] = {rows 0-1, rows 2-3}; u = n ^ 8 = q + 8 as in convert_n16.
+template <int ACT>
+__device__ __forceinline__ void convert_rows4_n(const uint32_t (&r)[4], u32x2 (&out)[4]) {
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = r[i] ^ 0x8888u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    auto nib = [&](int i) { return (u[i] >> (4 * j)) & 0xFu; };
+    if constexpr (ACT == ACT_F16) {
+      const f16x2 bias = {(_Float16)1032.f, (_Float16)1032.f};
+      auto pair = [&](int i0, int i1) {
+        const uint32_t h = (0x6400u | nib(i0)) | ((0x6400u | nib(i1)) << 16);   // 1024 + u, two halves
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) - bias);
+      };
+      out[j] = (u32x2){pair(0, 1), pair(2, 3)};
+    } else {
+      auto q = [&](int i) { return (float)nib(i) - 8.f; };
+      out[j] = (u32x2){bf16_pair(q(0), q(1)), bf16_pair(q(2), q(3))};
+    }
+  }
+}
+
 // Four K rows of four columns (r[i] = row i, byte j = column j) -> per
 // column j the four K values as 16-bit q: out[j] = {rows 0-1, rows 2-3}.
 template <int ACT>
@@ -208,7 +234,7 @@ __device__ __forceinline__ void load_stage(const W8Args& a, const W8Lane& ln, in
     st.a0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.x, v, 0, 0));
     st.a1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.x, v + 16u, 0, 0));
   }
-  if constexpr (B4) {
+  if constexpr (B4 && !ND) {
     // column c's K values kk .. kk + 15: 8 bytes of its GFX950_B record
     // (the 32-deep block kk / 32 of 128-deep block kk / 128), or of its ND
     // row of k / 2 bytes; the resource starts at the workgroup's first column
@@ -222,6 +248,15 @@ __device__ __forceinline__ void load_stage(const W8Args& a, const W8Lane& ln, in
     const int c = t >> 2, kc = (t & 3) * 16;
     const uint32_t v = (c < ln.cols) & (k0 + kc < kend) ? (uint32_t)(c * (int)a.k + k0 + kc) : BUF_OOB;
     st.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ln.w, v, 0, 0));
+  } else if constexpr (B4) {
+    // INT4 ND (k, n / 2) bytes: K row kk's columns c4 .. c4 + 3 are 2 bytes
+    const int rg = t >> 4, c4 = (t & 15) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t kk = k0 + 4 * rg + i;
+      const uint32_t v = (c4 < ln.cols) & (kk < kend) ? (uint32_t)(kk * (a.n >> 1) + (c4 >> 1)) : BUF_OOB;
+      st.b[i] = __builtin_amdgcn_raw_buffer_load_b16(ln.w, v, 0, 0);
+    }
   } else {
     const int rg = t >> 4, c4 = (t & 15) * 4;
 #pragma unroll
@@ -278,7 +313,8 @@ __device__ __forceinline__ void store_stage(const W8Stage& st, uint16_t* As, uin
     const int rg = t >> 4, c4 = (t & 15) * 4;
     const uint32_t r[4] = {st.b[0], st.b[1], st.b[2], st.b[3]};
     u32x2 out[4];
-    convert_rows4<ACT>(r, out);
+    if constexpr (B4) convert_rows4_n<ACT>(r, out);
+    else convert_rows4<ACT>(r, out);
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Bs + (c4 + j) * W8_LDS + 4 * rg) = out[j];
   }
@@ -357,7 +393,8 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   ln.rows = (int)(a.m - m0 < W8_BM ? a.m - m0 : W8_BM);
   ln.cols = (int)(a.n - n0 < W8_BN ? a.n - n0 : W8_BN);
   ln.x = buf_rsrc(a.x1 + m0 * a.k, (uint32_t)(ln.rows * a.k * 2));
-  if constexpr (B4)
+  if constexpr (B4 && ND) ln.w = buf_rsrc(a.x2 + n0 / 2, (uint32_t)((a.k - 1) * (a.n / 2) + ln.cols / 2));
+  else if constexpr (B4)
     ln.w = a.np ? buf_rsrc(a.x2 + n0 * 64, (uint32_t)(((a.k + 127) / 128 * a.np - n0) * 64))
                 : buf_rsrc(a.x2 + n0 * (a.k / 2), (uint32_t)(ln.cols * (a.k / 2)));
   else if constexpr (ND) ln.w = buf_rsrc(a.x2 + n0, (uint32_t)((a.k - 1) * a.n + ln.cols));
@@ -497,7 +534,8 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
   a.s_bytes = (uint32_t)(((groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
   const dim3 grid((unsigned)((p.n + W8_BN - 1) / W8_BN), (unsigned)((p.m + W8_BM - 1) / W8_BM));
   prof_begin(s);
-  if (p.w_bits == 4) gemm_w8<ACT, false, true><<<grid, 256 * W8_KS, 0, s>>>(a);
+  if (p.w_bits == 4 && p.layout == WQ_LAYOUT_ND && !p.transpose_x2) gemm_w8<ACT, true, true><<<grid, 256 * W8_KS, 0, s>>>(a);
+  else if (p.w_bits == 4) gemm_w8<ACT, false, true><<<grid, 256 * W8_KS, 0, s>>>(a);
   else if (p.transpose_x2) gemm_w8<ACT, false, false><<<grid, 256 * W8_KS, 0, s>>>(a);
   else gemm_w8<ACT, true, false><<<grid, 256 * W8_KS, 0, s>>>(a);
   prof_end(s);
@@ -511,13 +549,14 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
 // (4-byte column groups) and below 2 GiB (one buffer resource).
 // INT4 GFX950_B weights (the shapes the prefill tile does not take: groups
 // of 32, 64 or any multiple of 32 not dividing 128, or k not a multiple of
-// 128) and transposed ND INT4 weights: k a multiple of 16, the packed weight
-// below 2 GiB.
+// 128) and ND INT4 weights (transposed, or row-major with n a multiple of
+// 4): k a multiple of 16, the packed weight below 2 GiB.
 bool w8_ok(const WqProblem& p) {
   if (p.w_bits == 4) {
     if (p.k % 16 != 0) return false;
     if (p.layout == WQ_LAYOUT_GFX950_B) return (p.k + 127) / 128 * (16 * ((p.n + 15) / 16)) * 64 < (int64_t(1) << 31);
-    return p.transpose_x2 && p.n * (p.k / 2) < (int64_t(1) << 31);
+    if (p.transpose_x2) return p.n * (p.k / 2) < (int64_t(1) << 31);
+    return p.n % 4 == 0 && p.k * (p.n / 2) < (int64_t(1) << 31);
   }
   if (p.w_bits != 8 || p.k % 16 != 0) return false;
   if (p.transpose_x2) return true;

@@ -56,9 +56,10 @@ WQ_CASES = [  # m, k, n, act, granularity, group, layout, transpose, inplace
     (5, 384, 130, torch.bfloat16, "group", 128, wq.WQ_LAYOUT_GFX950_B, False, True),  # decode kernel
     (21, 512, 200, torch.float16, "channel", 0, wq.WQ_LAYOUT_GFX950_B, False, False), # decode, 2 launches
     (130, 512, 520, torch.bfloat16, "group", 128, wq.WQ_LAYOUT_GFX950_B, False, True),  # prefill, masked strip
-    (33, 256, 90, torch.bfloat16, "group", 64, wq.WQ_LAYOUT_ND, False, False),        # ND
+    (33, 256, 90, torch.bfloat16, "group", 64, wq.WQ_LAYOUT_ND, False, False),        # ND, n % 4 != 0: generic
     (70, 256, 48, torch.float16, "channel", 0, wq.WQ_LAYOUT_ND, True, False),          # INT4 ND transposed
     (70, 336, 132, torch.bfloat16, "group", 32, wq.WQ_LAYOUT_GFX950_B, False, True),   # INT8 tile, INT4 weight
+    (70, 512, 132, torch.float16, "group", 64, wq.WQ_LAYOUT_ND, False, True),          # INT8 tile, INT4 ND
 ]
 
 

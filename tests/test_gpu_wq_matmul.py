@@ -161,6 +161,25 @@ def test_int4_on_the_int8_tile(shape):
     assert torch.equal(y, y2) and torch.equal(nrm, n2)
 
 
+W4_ND = [  # m, k, n, granularity, group, offset, bias, act: row-major ND INT4 weights ((k, n / 2)
+    # bytes, n % 4 == 0) on the INT8 tile
+    (300, 1024, 200, "group", 32, (-0.5, 0.5), 0.1, torch.bfloat16),
+    (64, 2048, 516, "channel", 0, (-1.0, 1.0), None, torch.float16),
+    (7, 336, 68, "group", 96, "none", 0.1, torch.float16),
+    (129, 4096, 260, "group", 128, None, 0.1, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", W4_ND, ids=[f"{s[0]}x{s[1]}x{s[2]}-{s[3]}{s[4]}" for s in W4_ND])
+def test_int4_nd_on_the_int8_tile(shape):
+    m, k, n, gran, g, off, bias, act = shape
+    c = workloads.wq_case(f"w4nd{m}x{k}x{n}", m, k, n, act=act, w_bits=4, granularity=gran,
+                          group_size=g, offset_range=off, bias_std=bias, seed=3 * m + k + n)
+    note(f"wq int4 ND row-major on the INT8 tile {c.name} {gran} g={g} {act}")
+    y, nrm = wq_on_gpu(c, ND)
+    check_wq(c, y, nrm)
+
+
 @pytest.mark.parametrize("G", [32, 64])
 def test_int4_short_group_zero_scales(G):
     # a zero group scale leaves only the offset for that group and column

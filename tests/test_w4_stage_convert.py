@@ -74,3 +74,34 @@ def test_random_dwords():
         w0, w1 = int(w0), int(w1)
         assert convert_f16(w0, w1) == codes_of(w0, w1)
         assert convert_bf16(w0, w1) == codes_of(w0, w1)
+
+
+# Row-major ND INT4 (convert_rows4_n): four K rows of four columns, each row
+# 16 bits (nibble j = column j) -> per column the four K values as 16-bit q,
+# {rows 0-1, rows 2-3}.
+def convert_rows_f16(r):
+    u = [x ^ 0x8888 for x in r]
+    out = []
+    for j in range(4):
+        col = []
+        for a, b in ((0, 1), (2, 3)):
+            h = (0x6400 | ((u[a] >> (4 * j)) & 0xF)) | ((0x6400 | ((u[b] >> (4 * j)) & 0xF)) << 16)
+            col += list((halves(h) - np.float16(1032.0)).astype(np.float64))
+        out.append(col)
+    return out
+
+
+def convert_rows_bf16(r):
+    u = [x ^ 0x8888 for x in r]
+    return [[float(np.float32((u[i] >> (4 * j)) & 0xF) - np.float32(8.0)) for i in range(4)] for j in range(4)]
+
+
+def test_row_major_nibbles_every_code_in_every_position():
+    for pos in range(16):
+        for c in range(-8, 8):
+            codes = [[(3 * i + 5 * j + 1) % 16 - 8 for j in range(4)] for i in range(4)]   # [row][col]
+            codes[pos // 4][pos % 4] = c
+            r = [sum((codes[i][j] & 0xF) << (4 * j) for j in range(4)) for i in range(4)]
+            want = [[codes[i][j] for i in range(4)] for j in range(4)]
+            assert convert_rows_f16(r) == want
+            assert convert_rows_bf16(r) == want
