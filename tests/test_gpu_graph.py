@@ -242,6 +242,36 @@ def test_inplace_accumulators_replay():
         assert torch.equal(y_f4, seq[r + 1][3]), f"mxfp4 replay {r}"
 
 
+def test_mx_misaligned_n_replays():
+    # the MX tile's form for N not a multiple of 4 (scale2 by byte loads, y in
+    # unaligned 16-byte runs and element-wise across N) accumulates replay by
+    # replay exactly as eager calls do
+    note("graph: MX in-place add, n % 4 != 0")
+    rng = np.random.default_rng(11)
+    m, k, n = 272, 200, 262
+    x1 = torch.from_numpy(rng.integers(0, 256, (k, m), dtype=np.uint8))
+    x1[(x1 & 0x7F) == 0x7F] = 0
+    x1 = x1.to(DEV)
+    x2 = wq.pack_int4(torch.from_numpy(rng.integers(0, 16, (k, n), dtype=np.int32)).to(DEV), B)
+    kb = -(-k // 32)
+    s1 = torch.from_numpy(rng.integers(120, 128, (m, kb), dtype=np.uint8)).to(DEV)
+    s2 = torch.from_numpy(rng.integers(120, 128, (kb, n), dtype=np.uint8)).to(DEV)
+    y0 = torch.from_numpy(rng.standard_normal((m, n)).astype(np.float32)).to(DEV)
+    y = y0.clone()
+    e = y0.clone()
+    seq = []
+    for _ in range(4):
+        wq.mx_matmul_inplace_add(x1, x2, s1, s2, e, m, k, n)
+        seq.append(e.clone())
+    torch.cuda.synchronize()
+    g = _capture(lambda: wq.mx_matmul_inplace_add(x1, x2, s1, s2, y, m, k, n))
+    for r in range(3):
+        _eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, seq[r + 1]), f"replay {r}"
+
+
 def test_unfused_chain_replays():
     note("graph: standalone matmul -> add_rms_norm (decode m=4)")
     c = workloads.decode(4)

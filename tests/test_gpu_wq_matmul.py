@@ -180,6 +180,30 @@ def test_int4_nd_on_the_int8_tile(shape):
     check_wq(c, y, nrm)
 
 
+def test_int4_on_the_int8_tile_deterministic():
+    # the INT8 tile's fixed slice order and fold order: two runs bit for bit
+    c = workloads.wq_case("w4tile determinism", 513, 2048, 1000, act=torch.bfloat16, w_bits=4,
+                          granularity="group", group_size=32, offset_range=(-0.5, 0.5), bias_std=0.1, seed=4)
+    note("wq int4 INT8-tile determinism 513x2048x1000 g32")
+    y0, n0 = wq_on_gpu(c)
+    y1, n1 = wq_on_gpu(c)
+    assert torch.equal(y0, y1) and torch.equal(n0, n1)
+
+
+@pytest.mark.parametrize("act", [torch.float16, torch.bfloat16])
+def test_int4_nd_one_sign_activations(act):
+    # one-sign activations over a long K on the row-major ND INT4 staging
+    m, k, n = 40, 8192, 256
+    c = workloads.wq_case(f"w4nd one-sign {act}", m, k, n, act=act, w_bits=4, granularity="group",
+                          group_size=64, scale_range=(0.002, 0.02), offset_range=(-0.1, 0.1),
+                          x1_abs=True, w_range=(-7, 7))
+    note(f"wq int4 ND one-sign {act}")
+    y, nrm = wq_on_gpu(c, ND)
+    ey, en = check_wq(c, y, nrm)
+    if act == torch.float16:
+        assert ey <= 2e-3 and en <= 3e-3, (ey, en)      # the tight fp16 gate of the one-sign tests
+
+
 @pytest.mark.parametrize("G", [32, 64])
 def test_int4_short_group_zero_scales(G):
     # a zero group scale leaves only the offset for that group and column
