@@ -328,10 +328,17 @@ size_t partial_bytes(int64_t m, int64_t n) {
 // chunks of kRowChunk, so the workspace covers one chunk. No call needs
 // initial contents: each writes what it reads.
 size_t wq_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  // the last chunk's rows, which may take the INT8 tile's K split where a
+  // full chunk does not
+  const int64_t tail = m > kRowChunk && m % kRowChunk ? m % kRowChunk : 0;
   if (m > kRowChunk) m = kRowChunk;
-  const size_t tiled = partial_bytes(m, n) + fast_rowsum_bytes(m, k) + fast_corr_bytes(n, k);
+  size_t tiled = partial_bytes(m, n) + fast_rowsum_bytes(m, k) + fast_corr_bytes(n, k);
   const size_t dec = decode_partial_bytes(n);
-  return (tiled > dec ? tiled : dec) + 256;
+  const size_t split = w8_split_bytes(m, k, n), split_tail = w8_split_bytes(tail, k, n);
+  if (dec > tiled) tiled = dec;
+  if (split > tiled) tiled = split;
+  if (split_tail > tiled) tiled = split_tail;
+  return tiled + 256;
 }
 
 namespace {
@@ -368,7 +375,9 @@ hipError_t wq_rows(const WqProblem& p, hipStream_t s) {
                                                  fast_rowsum_bytes(p.m, p.k));
     e = launch_prefill(p, a.partial, rs, corr, s);
   } else if (w8_ok(p)) {
-    e = launch_w8(p, a.partial, s);
+    bool finished = false;
+    e = launch_w8(p, a.partial, s, finished);
+    if (e != hipSuccess || finished) return e;
   } else {
     e = p.bf16 ? launch_generic<ACT_BF16>(p, a, s) : launch_generic<ACT_F16>(p, a, s);
   }

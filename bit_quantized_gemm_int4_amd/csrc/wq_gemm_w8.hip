@@ -27,6 +27,10 @@
 // Loads run two K steps ahead of the MFMAs (two register stages, LDS double
 // buffer, one barrier per step): at small m the tile is latency-bound, and
 // two steps in flight halve the exposed load latency.
+// A small grid over a long K also splits K across workgroups (up to four
+// per output tile, within one workgroup per CU): each writes its float32
+// sums to the workspace, and w8_split_finish adds them per row and forms y
+// and normOut in place of the tile's epilogue and the norm finish.
 //
 // Conversion to exact 16-bit values:
 //   fp16: u = q + 128 (sign bit flipped) placed under the exponent byte 0x64
@@ -57,6 +61,12 @@ struct W8Args {
   int64_t np;               // B4: the padded width of the GFX950_B layout; 0 for ND transposed
   int upg;                  // 32-deep units per group; INT32_MAX: one group over all of K
   uint32_t s_bytes;
+  // K split across workgroups: workgroup z takes K values [z kz, (z + 1) kz)
+  // (kz a multiple of the step) and writes its float32 sums to ypart[z]
+  // ((m, n) row-major) for w8_split_finish; ypart null: one workgroup over
+  // all of K (kz >= k) and the epilogue in the tile.
+  float* ypart;
+  int64_t kz;
 };
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -419,10 +429,12 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   // same even number of steps with every load unconditional (a step past its
   // slice reads zeros through out-of-range offsets and multiplies nothing),
   // so the barriers match and the waits see one straight sequence of loads.
-  const int steps = (int)((a.k + W8_BK - 1) / W8_BK);
+  const int kz0 = (int)(blockIdx.z * a.kz);
+  const int kz1 = kz0 + a.kz < a.k ? kz0 + (int)a.kz : (int)a.k;
+  const int steps = (kz1 - kz0 + W8_BK - 1) / W8_BK;
   const int sps = (steps + W8_KS - 1) / W8_KS;
-  const int kb = q * sps * W8_BK;
-  const int kend = (q + 1) * sps * W8_BK < (int)a.k ? (q + 1) * sps * W8_BK : (int)a.k;
+  const int kb = kz0 + q * sps * W8_BK;
+  const int kend = kb + sps * W8_BK < kz1 ? kb + sps * W8_BK : kz1;
   uint16_t* A0 = As[q][0];
   uint16_t* A1 = As[q][1];
   uint16_t* B0 = Bs[q][0];
@@ -479,6 +491,21 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
     for (int e = 0; e < 4; ++e) v[e] += w[e];
   }
   const int64_t row = m0 + er, col = n0 + ec;
+  if (a.ypart) {
+    // K split: this workgroup's sums only (bias, residual and the norm are
+    // the split finish's)
+    if (row < a.m) {
+      float* pz = a.ypart + blockIdx.z * a.m * a.n + row * a.n + col;
+      if ((a.n & 3) == 0 && col + 3 < a.n) {
+        *reinterpret_cast<f32x4*>(pz) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < a.n) pz[e] = v[e];
+      }
+    }
+    return;
+  }
   float ss = 0.f;
   if (row < a.m) {
     const int64_t idx = row * a.n + col;
@@ -511,8 +538,93 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   if ((T & 7) == 0 && row < a.m && col < a.n) a.partial[row * ((a.n + 31) / 32) + col / 32] = ss;
 }
 
+// The finish of a K split: one workgroup per row. y = (sum of the splits'
+// sums, in split order) + bias + residual, stored rounded, the row's sum of
+// y^2 taken in float32 before rounding (as the tile's epilogue takes it);
+// then, with a norm output, normOut = y * rstd * gamma from the stored y.
 template <int ACT>
-hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
+__global__ __launch_bounds__(256) void w8_split_finish(const float* __restrict__ ypart, int splits,
+                                                       const uint16_t* bias, const uint16_t* residual,
+                                                       const uint16_t* __restrict__ gamma, uint16_t* y,
+                                                       uint16_t* __restrict__ out, int64_t m, int64_t n,
+                                                       float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x, mn = m * n;
+  const int t = threadIdx.x;
+  float ss = 0.f;
+  if ((n & 3) == 0) {
+    // four adjacent columns per thread: 16-byte partial loads, 8-byte
+    // bias / residual / y accesses (rows start 8-byte aligned)
+    for (int64_t c = 4 * t; c < n; c += 1024) {
+      const int64_t idx = row * n + c;
+      f32x4 v = *reinterpret_cast<const f32x4*>(ypart + idx);
+      for (int z = 1; z < splits; ++z) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(ypart + z * mn + idx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += w[e];
+      }
+      const u32x2 bb = bias ? *reinterpret_cast<const u32x2*>(bias + c) : (u32x2){0u, 0u};
+      const u32x2 rr = residual ? *reinterpret_cast<const u32x2*>(residual + idx) : (u32x2){0u, 0u};
+      float yv[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        yv[2 * e] = v[2 * e] + lo_f32<ACT>(bb[e]) + lo_f32<ACT>(rr[e]);
+        yv[2 * e + 1] = v[2 * e + 1] + hi_f32<ACT>(bb[e]) + hi_f32<ACT>(rr[e]);
+      }
+      *reinterpret_cast<u32x2*>(y + idx) = (u32x2){pack2<ACT>(yv[0], yv[1]), pack2<ACT>(yv[2], yv[3])};
+      ss += (yv[0] * yv[0] + yv[1] * yv[1]) + (yv[2] * yv[2] + yv[3] * yv[3]);
+    }
+  } else {
+    for (int64_t c = t; c < n; c += 256) {
+      const int64_t idx = row * n + c;
+      float v = ypart[idx];
+      for (int z = 1; z < splits; ++z) v += ypart[z * mn + idx];
+      const float yv = v + (bias ? to_f32<ACT>(bias[c]) : 0.f) + (residual ? to_f32<ACT>(residual[idx]) : 0.f);
+      y[idx] = from_f32<ACT>(yv);
+      ss += yv * yv;
+    }
+  }
+  if (!out) return;   // the standalone matmul
+  ss = wave_sum(ss);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rstd = 1.0f / sqrtf(ss / (float)n + eps);
+  // every thread reads back only the y values it stored
+  if ((n & 3) == 0) {
+    for (int64_t c = 4 * t; c < n; c += 1024) {
+      const int64_t idx = row * n + c;
+      const u32x2 yy = *reinterpret_cast<const u32x2*>(y + idx);
+      const u32x2 gg = *reinterpret_cast<const u32x2*>(gamma + c);
+      u32x2 o;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        o[e] = pack2<ACT>(lo_f32<ACT>(yy[e]) * rstd * lo_f32<ACT>(gg[e]),
+                          hi_f32<ACT>(yy[e]) * rstd * hi_f32<ACT>(gg[e]));
+      *reinterpret_cast<u32x2*>(out + idx) = o;
+    }
+  } else {
+    for (int64_t c = t; c < n; c += 256) {
+      const int64_t idx = row * n + c;
+      out[idx] = from_f32<ACT>(to_f32<ACT>(y[idx]) * rstd * to_f32<ACT>(gamma[c]));
+    }
+  }
+}
+
+// K splits for an (m, k, n) problem on this tile: the largest of 1, 2, 4
+// whose grid stays within one workgroup per CU (256) while every slice keeps
+// at least two K steps. A small grid over a long K is a chain of load
+// latencies per slice; splitting it shortens the chain.
+int w8_split_count(int64_t m, int64_t k, int64_t n) {
+  const int64_t tiles = ((m + W8_BM - 1) / W8_BM) * ((n + W8_BN - 1) / W8_BN);
+  const int64_t steps = (k + W8_BK - 1) / W8_BK;
+  int s = 1;
+  while (s < 4 && tiles * 2 * s <= 256 && steps >= 2 * W8_KS * 2 * s) s *= 2;
+  return s;
+}
+
+template <int ACT>
+hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s, bool& finished) {
   W8Args a;
   a.x1 = static_cast<const uint16_t*>(p.x1);
   a.x2 = static_cast<const uint8_t*>(p.x2);
@@ -532,13 +644,26 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s) {
   a.s_col = p.s_col;
   const int64_t groups = (p.k + group - 1) / group;
   a.s_bytes = (uint32_t)(((groups - 1) * p.s_row + (p.n - 1) * p.s_col + 1) * 2);
-  const dim3 grid((unsigned)((p.n + W8_BN - 1) / W8_BN), (unsigned)((p.m + W8_BM - 1) / W8_BM));
+  // K split: the splits' sums go to the workspace, whose size covers them
+  // (w8_split_bytes); the split finish then forms y and normOut
+  const int splits = w8_split_count(p.m, p.k, p.n);
+  const bool split = splits > 1 && (size_t)splits * p.m * p.n * sizeof(float) <= p.workspace_size;
+  const int64_t steps = (p.k + W8_BK - 1) / W8_BK;
+  a.ypart = split ? partial : nullptr;
+  a.kz = split ? (steps + splits - 1) / splits * W8_BK : p.k;
+  const dim3 grid((unsigned)((p.n + W8_BN - 1) / W8_BN), (unsigned)((p.m + W8_BM - 1) / W8_BM),
+                  split ? (unsigned)splits : 1u);
   prof_begin(s);
   if (p.w_bits == 4 && p.layout == WQ_LAYOUT_ND && !p.transpose_x2) gemm_w8<ACT, true, true><<<grid, 256 * W8_KS, 0, s>>>(a);
   else if (p.w_bits == 4) gemm_w8<ACT, false, true><<<grid, 256 * W8_KS, 0, s>>>(a);
   else if (p.transpose_x2) gemm_w8<ACT, false, false><<<grid, 256 * W8_KS, 0, s>>>(a);
   else gemm_w8<ACT, true, false><<<grid, 256 * W8_KS, 0, s>>>(a);
   prof_end(s);
+  finished = split;
+  if (!split) return hipGetLastError();
+  w8_split_finish<ACT><<<dim3((unsigned)p.m), 256, 0, s>>>(
+      partial, splits, a.bias, a.residual, static_cast<const uint16_t*>(p.gamma), a.y,
+      static_cast<uint16_t*>(p.norm_out), p.m, p.n, p.eps);
   return hipGetLastError();
 }
 
@@ -563,8 +688,14 @@ bool w8_ok(const WqProblem& p) {
   return p.n % 4 == 0 && p.k * p.n < (int64_t(1) << 31);
 }
 
-hipError_t launch_w8(const WqProblem& p, float* partial, hipStream_t s) {
-  return p.bf16 ? launch_w8_t<ACT_BF16>(p, partial, s) : launch_w8_t<ACT_F16>(p, partial, s);
+hipError_t launch_w8(const WqProblem& p, float* partial, hipStream_t s, bool& finished) {
+  return p.bf16 ? launch_w8_t<ACT_BF16>(p, partial, s, finished)
+                : launch_w8_t<ACT_F16>(p, partial, s, finished);
+}
+
+size_t w8_split_bytes(int64_t m, int64_t k, int64_t n) {
+  const int splits = w8_split_count(m, k, n);
+  return splits > 1 ? (size_t)splits * m * n * sizeof(float) : 0;
 }
 
 }  // namespace wq

@@ -81,7 +81,12 @@ hipError_t launch_decode(const WqProblem& p, float* partial, hipStream_t s);
 // multiple of 4 below 2 GiB, or transposed); partials as gemm_generic's:
 // [row][ceil(n / 32)].
 bool w8_ok(const WqProblem& p);
-hipError_t launch_w8(const WqProblem& p, float* partial, hipStream_t s);
+// `finished`: set when the call also formed y and normOut (a K split with
+// its own finish), so that no norm pass follows.
+hipError_t launch_w8(const WqProblem& p, float* partial, hipStream_t s, bool& finished);
+// Workspace bytes of the INT8 tile's K split for an (m, k, n) row chunk (0:
+// no split).
+size_t w8_split_bytes(int64_t m, int64_t k, int64_t n);
 
 struct MxProblem {
   const uint8_t* x1;     // (k, m) e4m3

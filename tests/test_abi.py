@@ -60,6 +60,13 @@ def test_size_queries():
     assert wq.wq_pack_int4_bytes(-1, 3, wq.WQ_LAYOUT_GFX950_B) == 0
     ws = wq.wq_matmul_add_rmsnorm_workspace_size(4096, 8192, 8192)
     assert ws >= 4096 * (8192 // 32) * 4
+    # small grids over a long K: room for the float32 sums of every K split
+    # (two at 512 x 1024 x 1024, four at 1 x 4096 x 4096 and 36 x 2048 x 250)
+    assert wq.wq_matmul_add_rmsnorm_workspace_size(512, 1024, 1024) >= 2 * 512 * 1024 * 4
+    assert wq.wq_matmul_add_rmsnorm_workspace_size(1, 4096, 4096) >= 4 * 4096 * 4
+    assert wq.wq_matmul_add_rmsnorm_workspace_size(36, 2048, 250) >= 4 * 36 * 250 * 4
+    # a grid of one workgroup per CU or more takes no split
+    assert wq.wq_matmul_add_rmsnorm_workspace_size(1024, 1024, 4096) < 2 * 1024 * 4096 * 4
     assert wq.mx_quant_matmul_inplace_add_workspace_size(4096, 8192, 4096) == 0
     # m % 16 != 0: room for x1 with rows padded to 16 bytes (k x 16 ceil(m/16)), 256-byte rounded
     assert wq.mx_quant_matmul_inplace_add_workspace_size(4100, 8192, 4100) == 8192 * 4112

@@ -102,6 +102,26 @@ def test_weight_quant_matmul_w8():
     _check(out.cpu(), _oracle_mm(c), "w8")
 
 
+@pytest.mark.parametrize("m,k,n", [(40, 4096, 1028), (64, 1536, 1000)])
+def test_weight_quant_matmul_int8_k_split(m, k, n):
+    # small grids over a long K split K across workgroups (four splits, then
+    # two), with the split finish writing y and no norm
+    c = workloads.wq_case(f"wqbmm8s{m}x{k}x{n}", m, k, n, act=torch.float16, w_bits=8,
+                          granularity="group", group_size=128, offset_range=(-0.5, 0.5),
+                          bias_std=0.1, seed=m + k + n)
+    note(f"standalone wq matmul int8 k split {m}x{k}x{n}")
+    ops = _operands(c)
+    out = wq.weight_quant_matmul(**ops)
+    torch.cuda.synchronize()
+    _check(out.cpu(), _oracle_mm(c), c.name)
+    zero = torch.zeros((m, n), dtype=torch.float16, device=DEV)
+    y, _ = wq.matmul_add_rmsnorm(ops["x1"], ops["x2"], k, n, ops["w_dtype"], ops["scale"],
+                                 ops["offset"], 128, ops["bias"], zero,
+                                 torch.ones(n, dtype=torch.float16, device=DEV), 1e-6, layout=ops["layout"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), y.cpu().reshape(m, n))
+
+
 def test_weight_quant_matmul_prefill_full_size_sampled_rows():
     c = workloads.prefill()
     m, k, n = c.mkn

@@ -60,6 +60,8 @@ WQ_CASES = [  # m, k, n, act, granularity, group, layout, transpose, inplace
     (70, 256, 48, torch.float16, "channel", 0, wq.WQ_LAYOUT_ND, True, False),          # INT4 ND transposed
     (70, 336, 132, torch.bfloat16, "group", 32, wq.WQ_LAYOUT_GFX950_B, False, True),   # INT8 tile, INT4 weight
     (70, 512, 132, torch.float16, "group", 64, wq.WQ_LAYOUT_ND, False, True),          # INT8 tile, INT4 ND
+    (36, 2048, 132, torch.bfloat16, "group", 32, wq.WQ_LAYOUT_GFX950_B, False, True),  # INT8 tile, K split 4
+    (36, 2048, 70, torch.float16, "group", 64, wq.WQ_LAYOUT_ND, True, True),           # K split 4, n % 4 != 0
 ]
 
 

@@ -119,6 +119,11 @@ W8 = [  # m, k, n, granularity, group, offset, bias, act: the INT8 64 x 64 tile
     (129, 4096, 260, "group", 192, None, 0.1, torch.float16),
     (48, 16, 8, "channel2d", 0, (-0.5, 0.5), 0.1, torch.float16),     # one 16-deep step
     (200, 640, 300, "group", 160, (-1.0, 1.0), 0.1, torch.bfloat16),
+    # K split across workgroups (small grids over a long K): four splits,
+    # n % 4 != 0 (transposed; the row-major weight takes the generic tile);
+    # two splits with groups across the split and the slice boundaries
+    (36, 2048, 250, "group", 128, (-0.5, 0.5), 0.1, torch.float16),
+    (64, 1536, 1000, "group", 160, (-1.0, 1.0), 0.1, torch.bfloat16),
 ]
 
 
@@ -260,7 +265,7 @@ def test_int8_tile_shapes(shape, transpose):
 @pytest.mark.parametrize("act", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("transpose", [False, True])
 @pytest.mark.parametrize("k,G,m", [(256, 32, 36), (320, 64, 36), (512, 0, 36), (256, 32, 20), (512, 0, 20),
-                                   (384, 64, 20)])
+                                   (384, 64, 20), (2048, 0, 36), (2048, 128, 36)])
 def test_int8_integer_valued_y_is_bit_exact(act, transpose, k, G, m):
     # x1 rows one-hot with sign +-1 (rows 0..3 on K = 0 and 1, where the
     # codes are -128 and 127), INT8 codes over the whole range, scale 1, no
