@@ -538,12 +538,23 @@ __global__ __launch_bounds__(256 * W8_KS) void gemm_w8(W8Args a) {
   if ((T & 7) == 0 && row < a.m && col < a.n) a.partial[row * ((a.n + 31) / 32) + col / 32] = ss;
 }
 
-// The finish of a K split: one workgroup per row. y = (sum of the splits'
-// sums, in split order) + bias + residual, stored rounded, the row's sum of
-// y^2 taken in float32 before rounding (as the tile's epilogue takes it);
-// then, with a norm output, normOut = y * rstd * gamma from the stored y.
-template <int ACT>
-__global__ __launch_bounds__(256) void w8_split_finish(const float* __restrict__ ypart, int splits,
+// The finish of a K split (S splits): one workgroup per row. y = (sum of the
+// splits' sums, in split order) + bias + residual, stored rounded, the row's
+// sum of y^2 taken in float32 before rounding (as the tile's epilogue takes
+// it); then, with a norm output, normOut = y * rstd * gamma from the stored
+// (rounded) y.
+// A split grid has at most 256 tiles over S splits, so a row holds at most
+// 64 * 256 / S columns (W8_SPLIT_MAX_N at S = 2) and S * n <= 16384. With
+// n % 4 == 0 each thread takes four adjacent columns per pass of 1024, at
+// most 16 / S passes: every load of the row (the splits' sums, bias,
+// residual, gamma) is issued before the first store, through buffer
+// resources that read zeros past their ends (y may be the residual's
+// memory, so no load may follow a store), and the stored y stays in
+// registers across the row's reduction.
+constexpr int W8_SPLIT_MAX_N = 8192;
+
+template <int ACT, int S>
+__global__ __launch_bounds__(256) void w8_split_finish(const float* __restrict__ ypart,
                                                        const uint16_t* bias, const uint16_t* residual,
                                                        const uint16_t* __restrict__ gamma, uint16_t* y,
                                                        uint16_t* __restrict__ out, int64_t m, int64_t n,
@@ -552,33 +563,60 @@ __global__ __launch_bounds__(256) void w8_split_finish(const float* __restrict__
   const int64_t row = blockIdx.x, mn = m * n;
   const int t = threadIdx.x;
   float ss = 0.f;
-  if ((n & 3) == 0) {
-    // four adjacent columns per thread: 16-byte partial loads, 8-byte
-    // bias / residual / y accesses (rows start 8-byte aligned)
-    for (int64_t c = 4 * t; c < n; c += 1024) {
-      const int64_t idx = row * n + c;
-      f32x4 v = *reinterpret_cast<const f32x4*>(ypart + idx);
-      for (int z = 1; z < splits; ++z) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(ypart + z * mn + idx);
+  constexpr int J = 16 / S;
+  u32x2 ys[J], gs[J];
+  const bool vec = (n & 3) == 0;
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(ypart + row * n, (uint32_t)((S - 1) * mn * 4 + n * 4));
+    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(bias ? (const void*)bias : ypart, bias ? (uint32_t)(n * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(residual ? (const void*)(residual + row * n) : ypart,
+                                               residual ? (uint32_t)(n * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(out ? (const void*)gamma : ypart, out ? (uint32_t)(n * 2) : 0u);
+    f32x4 pv[S][J];
+    u32x2 bv[J], rv[J];
+    // passes past the row's end are skipped whole (a workgroup-uniform
+    // branch); in the last one, lanes past n read zeros
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += w[e];
-      }
-      const u32x2 bb = bias ? *reinterpret_cast<const u32x2*>(bias + c) : (u32x2){0u, 0u};
-      const u32x2 rr = residual ? *reinterpret_cast<const u32x2*>(residual + idx) : (u32x2){0u, 0u};
+    for (int j = 0; j < J; ++j) {
+      if (1024 * j >= n) break;
+      const int64_t c = 4 * t + 1024 * j;
+      const bool ok = c < n;
+      const uint32_t o2 = ok ? (uint32_t)(c * 2) : BUF_OOB;
+#pragma unroll
+      for (int z = 0; z < S; ++z)
+        pv[z][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rp, ok ? (uint32_t)((z * mn + c) * 4) : BUF_OOB, 0, 0));
+      bv[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rb, o2, 0, 0));
+      rv[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, o2, 0, 0));
+      gs[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, o2, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (1024 * j >= n) break;
+      const int64_t c = 4 * t + 1024 * j;
+      f32x4 v = pv[0][j];
+#pragma unroll
+      for (int z = 1; z < S; ++z)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += pv[z][j][e];
       float yv[4];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        yv[2 * e] = v[2 * e] + lo_f32<ACT>(bb[e]) + lo_f32<ACT>(rr[e]);
-        yv[2 * e + 1] = v[2 * e + 1] + hi_f32<ACT>(bb[e]) + hi_f32<ACT>(rr[e]);
+        yv[2 * e] = v[2 * e] + lo_f32<ACT>(bv[j][e]) + lo_f32<ACT>(rv[j][e]);
+        yv[2 * e + 1] = v[2 * e + 1] + hi_f32<ACT>(bv[j][e]) + hi_f32<ACT>(rv[j][e]);
       }
-      *reinterpret_cast<u32x2*>(y + idx) = (u32x2){pack2<ACT>(yv[0], yv[1]), pack2<ACT>(yv[2], yv[3])};
-      ss += (yv[0] * yv[0] + yv[1] * yv[1]) + (yv[2] * yv[2] + yv[3] * yv[3]);
+      ys[j] = (u32x2){pack2<ACT>(yv[0], yv[1]), pack2<ACT>(yv[2], yv[3])};
+      if (c < n) {
+        *reinterpret_cast<u32x2*>(y + row * n + c) = ys[j];
+        ss += (yv[0] * yv[0] + yv[1] * yv[1]) + (yv[2] * yv[2] + yv[3] * yv[3]);
+      }
     }
   } else {
     for (int64_t c = t; c < n; c += 256) {
       const int64_t idx = row * n + c;
       float v = ypart[idx];
-      for (int z = 1; z < splits; ++z) v += ypart[z * mn + idx];
+#pragma unroll
+      for (int z = 1; z < S; ++z) v += ypart[z * mn + idx];
       const float yv = v + (bias ? to_f32<ACT>(bias[c]) : 0.f) + (residual ? to_f32<ACT>(residual[idx]) : 0.f);
       y[idx] = from_f32<ACT>(yv);
       ss += yv * yv;
@@ -590,20 +628,22 @@ __global__ __launch_bounds__(256) void w8_split_finish(const float* __restrict__
   __syncthreads();
   ss = (red[0] + red[1]) + (red[2] + red[3]);
   const float rstd = 1.0f / sqrtf(ss / (float)n + eps);
-  // every thread reads back only the y values it stored
-  if ((n & 3) == 0) {
-    for (int64_t c = 4 * t; c < n; c += 1024) {
-      const int64_t idx = row * n + c;
-      const u32x2 yy = *reinterpret_cast<const u32x2*>(y + idx);
-      const u32x2 gg = *reinterpret_cast<const u32x2*>(gamma + c);
-      u32x2 o;
+  if (vec) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        o[e] = pack2<ACT>(lo_f32<ACT>(yy[e]) * rstd * lo_f32<ACT>(gg[e]),
-                          hi_f32<ACT>(yy[e]) * rstd * hi_f32<ACT>(gg[e]));
-      *reinterpret_cast<u32x2*>(out + idx) = o;
+    for (int j = 0; j < J; ++j) {
+      if (1024 * j >= n) break;
+      const int64_t c = 4 * t + 1024 * j;
+      if (c < n) {
+        u32x2 o;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          o[e] = pack2<ACT>(lo_f32<ACT>(ys[j][e]) * rstd * lo_f32<ACT>(gs[j][e]),
+                            hi_f32<ACT>(ys[j][e]) * rstd * hi_f32<ACT>(gs[j][e]));
+        *reinterpret_cast<u32x2*>(out + row * n + c) = o;
+      }
     }
   } else {
+    // every thread reads back only the y values it stored
     for (int64_t c = t; c < n; c += 256) {
       const int64_t idx = row * n + c;
       out[idx] = from_f32<ACT>(to_f32<ACT>(y[idx]) * rstd * to_f32<ACT>(gamma[c]));
@@ -620,7 +660,8 @@ int w8_split_count(int64_t m, int64_t k, int64_t n) {
   const int64_t steps = (k + W8_BK - 1) / W8_BK;
   int s = 1;
   while (s < 4 && tiles * 2 * s <= 256 && steps >= 2 * W8_KS * 2 * s) s *= 2;
-  return s;
+  // (the grid bound implies what the finish relies on: s * n <= 16384)
+  return s * n <= 2 * W8_SPLIT_MAX_N ? s : 1;
 }
 
 template <int ACT>
@@ -661,9 +702,14 @@ hipError_t launch_w8_t(const WqProblem& p, float* partial, hipStream_t s, bool& 
   prof_end(s);
   finished = split;
   if (!split) return hipGetLastError();
-  w8_split_finish<ACT><<<dim3((unsigned)p.m), 256, 0, s>>>(
-      partial, splits, a.bias, a.residual, static_cast<const uint16_t*>(p.gamma), a.y,
-      static_cast<uint16_t*>(p.norm_out), p.m, p.n, p.eps);
+  const uint16_t* gamma = static_cast<const uint16_t*>(p.gamma);
+  uint16_t* norm_out = static_cast<uint16_t*>(p.norm_out);
+  if (splits == 2)
+    w8_split_finish<ACT, 2><<<dim3((unsigned)p.m), 256, 0, s>>>(partial, a.bias, a.residual, gamma, a.y,
+                                                                norm_out, p.m, p.n, p.eps);
+  else
+    w8_split_finish<ACT, 4><<<dim3((unsigned)p.m), 256, 0, s>>>(partial, a.bias, a.residual, gamma, a.y,
+                                                                norm_out, p.m, p.n, p.eps);
   return hipGetLastError();
 }
 

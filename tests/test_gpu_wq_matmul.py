@@ -124,6 +124,7 @@ W8 = [  # m, k, n, granularity, group, offset, bias, act: the INT8 64 x 64 tile
     # two splits with groups across the split and the slice boundaries
     (36, 2048, 250, "group", 128, (-0.5, 0.5), 0.1, torch.float16),
     (64, 1536, 1000, "group", 160, (-1.0, 1.0), 0.1, torch.bfloat16),
+    (40, 2048, 8192, "channel", 0, (-0.5, 0.5), 0.1, torch.bfloat16),   # the widest split row
 ]
 
 
