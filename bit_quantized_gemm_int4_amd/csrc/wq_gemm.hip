@@ -9,6 +9,9 @@
 //      32-column tile), row-major; the decode kernel per (workgroup, row);
 //   2. rmsnorm_finish: sums a row's partials in a fixed order, forms
 //      1/RMS and writes normOut = y * rstd * gamma.
+// (When the INT8 tile splits K across workgroups, its launch writes float32
+// sums to the workspace instead, and its own finish, w8_split_finish, forms
+// y and normOut: still two launches.)
 // GEMM kernels:
 //   - gemm_decode (wq_gemm_decode.hip): m <= 32, INT4 GFX950_B, k a
 //     multiple of 128, any group: a weight stream;
