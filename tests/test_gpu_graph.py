@@ -148,6 +148,16 @@ def test_w8_call_replays():
     _check_replays(_WQCall(workloads.w8()))
 
 
+def test_w8_four_way_k_split_replays():
+    # a small grid over a long K: the INT8 tile in four K splits, then the
+    # split finish (float32 sums through the workspace)
+    c = workloads.wq_case("graph w8 split4", 40, 4096, 1028, act=torch.float16, w_bits=8,
+                          granularity="group", group_size=128, offset_range=(-0.5, 0.5),
+                          bias_std=0.1, seed=11)
+    note("graph: wq w8 40x4096x1028 g128 (four K splits)")
+    _check_replays(_WQCall(c))
+
+
 def test_dynamic_quant_and_pack_replay():
     note("graph: dynamic quant (per token int8, MX e4m3 and e2m1) and pack (int4, fp4)")
     rng = np.random.default_rng(3)

@@ -186,6 +186,18 @@ def test_int4_nd_on_the_int8_tile(shape):
     check_wq(c, y, nrm)
 
 
+def test_int8_k_split_deterministic():
+    # the splits' sums are added in split order: two runs agree bit for bit
+    c = workloads.wq_case("w8split-det", 36, 2048, 1000, act=torch.bfloat16, w_bits=8,
+                          granularity="group", group_size=64, offset_range=(-1.0, 1.0),
+                          bias_std=0.1, seed=5)
+    note("wq int8 k split 36x2048x1000 g64 determinism")
+    y0, n0 = wq_on_gpu(c)
+    y1, n1 = wq_on_gpu(c)
+    assert torch.equal(y0, y1) and torch.equal(n0, n1)
+    check_wq(c, y0, n0)
+
+
 def test_int4_on_the_int8_tile_deterministic():
     # the INT8 tile's fixed slice order and fold order: two runs bit for bit
     c = workloads.wq_case("w4tile determinism", 513, 2048, 1000, act=torch.bfloat16, w_bits=4,
